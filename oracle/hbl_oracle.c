@@ -1,0 +1,390 @@
+/*
+ * hbl_oracle.c -- plain CPU oracle for the H-BitLinear forward of BitNet v2.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * reference that the HIP path is checked against.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or constant with the GPU library.
+ *
+ * Source of every formula: the architecture write-up of
+ * "BitNet v2: Native 4-bit Activations with Hadamard Transformation for
+ * 1-bit LLMs" (paper-graph-ui.vercel.app, §3.4 "Detailed, Sentence-Based
+ * Technical Breakdown"), cited below as [BNv2 §3.4 <subsection>, Eq. n].
+ *
+ * Precision policy.
+ *   - The Hadamard transform is evaluated in fp64 (radix-2 butterflies on
+ *     exactly-widened inputs, one final 1/sqrt(n) scale) and rounded once to
+ *     fp32: that fp32 vector is the tensor X_r the quantizer sees.
+ *   - Sums of absolute values (beta, alpha) are accumulated in fp64.
+ *   - The quantizer's decision arithmetic (the scale factor, the product
+ *     x*f, round-half-even, clip) is evaluated in fp32, the precision the
+ *     GPU kernels decide in, so that both sides round the same quantity.
+ *   - The integer matmul is exact (int64 accumulation, checked to fit int32).
+ *   - Compile with -ffp-contract=off: no fused multiply-adds anywhere.
+ *
+ * Readings of points the pages leave open (also listed in the design notes):
+ *   eps = 1e-5f for weights and activations; "round" is round-half-to-even;
+ *   the per-token scale factor f = Qmax/(stat + eps) is formed once per row;
+ *   the dequantisation factor uses the statistic without eps (gamma/127,
+ *   beta/sqrt(7)); H is in natural (Sylvester) order, applied per token row;
+ *   alpha is one scalar per weight matrix; Y[M][N] = Xq[M][K] * Wq[N][K]^T.
+ *
+ * Packed layouts (defined here, bit-exactly; the GPU library must match):
+ *   ternary weights: uint32 [N][K/16]; word w of row n holds k = 16w..16w+15;
+ *       weight j = 4s + b (s,b in 0..3) sits at bits [8b+2s, 8b+2s+2) as the
+ *       unsigned value c = q + 1 in {0,1,2} (3 never occurs).
+ *   INT4 codes: uint32 [M][K/8]; word w of row m holds k = 8w..8w+7;
+ *       code j = 4h + b (h in 0..1, b in 0..3) sits at bits [8b+4h, 8b+4h+4)
+ *       as a two's-complement nibble.
+ *   INT8 codes: int8 [M][K], natural order.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define HBO_EPS 1e-5f /* the pages' epsilon has no printed value; reading */
+
+/* dtype codes understood by this oracle */
+#define HBO_F32 0
+#define HBO_BF16 1
+
+/* ------------------------------------------------------------------ */
+/* scalar helpers                                                      */
+/* ------------------------------------------------------------------ */
+
+/* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even (finite inputs). */
+uint16_t hbo_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+static float load_elem(const void *x, int dtype, int64_t i) {
+  if (dtype == HBO_BF16) return bf16_to_f32(((const uint16_t *)x)[i]);
+  return ((const float *)x)[i];
+}
+
+/* RoundClip(X, a, b) = min(max(round(X), a), b)  [BNv2 §3.4 "Weight
+ * Quantization", Eq. 2]; round = nearest, ties to even (rintf in the default
+ * rounding mode). */
+static float round_clip(float v, float a, float b) {
+  float r = rintf(v);
+  if (r < a) r = a;
+  if (r > b) r = b;
+  return r;
+}
+
+static int is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+
+/* ------------------------------------------------------------------ */
+/* Hadamard transform  [BNv2 §3.4 "The Hadamard Transformation",       */
+/* Eq. 3-6]                                                            */
+/* ------------------------------------------------------------------ */
+
+/* In-place unnormalised Walsh-Hadamard transform of v[0..n), natural
+ * (Sylvester) order: applies H~_m where H~_0 = (1) and
+ * H~_m = [[H~_{m-1}, H~_{m-1}], [H~_{m-1}, -H~_{m-1}]].  One radix-2 stage
+ * per power of two h = 1, 2, 4, ..., n/2: the pair (v[j], v[j+h]) becomes
+ * (v[j] + v[j+h], v[j] - v[j+h]).  Returns the number of additions and
+ * subtractions performed (n * log2 n). */
+int64_t hbo_fwht_f64(double *v, int64_t n) {
+  int64_t ops = 0;
+  for (int64_t h = 1; h < n; h *= 2) {
+    for (int64_t i = 0; i < n; i += 2 * h) {
+      for (int64_t j = i; j < i + h; j++) {
+        double a = v[j];
+        double b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+        ops += 2;
+      }
+    }
+  }
+  return ops;
+}
+
+/* Y = Hadamard(X) row by row, normalised: each row of length K = 2^m is
+ * multiplied by H_m = 2^{-m/2} H~_m  (the 1/sqrt(2) of every recursion level
+ * in Eq. 5 collected into one factor).  y is fp64 [M][K]. */
+int hbo_hadamard(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                 double *y) {
+  if (!is_pow2(K) || ldx < K || M < 0) return 2;
+  const double scale = 1.0 / sqrt((double)K);
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++) {
+    double *row = y + m * K;
+    for (int64_t k = 0; k < K; k++) row[k] = (double)load_elem(x, x_dtype, m * ldx + k);
+    hbo_fwht_f64(row, K);
+    for (int64_t k = 0; k < K; k++) row[k] = row[k] * scale;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-token activation quantizers  [BNv2 §3.4 "INT8 Quantization",     */
+/* Eq. 7; "INT4 Quantization", Eq. 8]                                  */
+/* ------------------------------------------------------------------ */
+
+/* Quantises one fp32 row xr[0..K) (the tensor X_r of Eq. 9).
+ *   INT8: gamma = max|x|; q = RoundClip(127/(gamma+eps) * x, -128, 127);
+ *         dequantisation factor s = gamma/127.
+ *   INT4: beta = mean|x|;  q = RoundClip(sqrt(7)/(beta+eps) * x, -8, 7);
+ *         dequantisation factor s = beta/sqrt(7).
+ * Writes q[0..K) as int8 and returns s; *rowsum = sum of the codes. */
+static float quantize_row(const float *xr, int64_t K, int bits, int8_t *q,
+                          int32_t *rowsum) {
+  float f, s, lo, hi;
+  if (bits == 8) {
+    float gamma = 0.0f;
+    for (int64_t k = 0; k < K; k++) {
+      float a = fabsf(xr[k]);
+      if (a > gamma) gamma = a;
+    }
+    f = 127.0f / (gamma + HBO_EPS);
+    s = gamma / 127.0f;
+    lo = -128.0f;
+    hi = 127.0f;
+  } else {
+    double sum = 0.0;
+    for (int64_t k = 0; k < K; k++) sum += fabs((double)xr[k]);
+    float beta = (float)(sum / (double)K);
+    const float sqrt7 = (float)sqrt(7.0);
+    f = sqrt7 / (beta + HBO_EPS);
+    s = beta / sqrt7;
+    lo = -8.0f;
+    hi = 7.0f;
+  }
+  int64_t total = 0;
+  for (int64_t k = 0; k < K; k++) {
+    float v = round_clip(xr[k] * f, lo, hi);
+    q[k] = (int8_t)v;
+    total += (int64_t)q[k];
+  }
+  *rowsum = (int32_t)total;
+  return s;
+}
+
+/* INT4 packing: code j = 4h + b of each 8-code group at bits [8b+4h, +4). */
+void hbo_pack_int4(const int8_t *q, int64_t M, int64_t K, uint32_t *packed) {
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t w = 0; w < K / 8; w++) {
+      uint32_t word = 0;
+      for (int j = 0; j < 8; j++) {
+        int h = j / 4, b = j % 4;
+        uint32_t nib = (uint32_t)(q[m * K + 8 * w + j]) & 0xfu;
+        word |= nib << (8 * b + 4 * h);
+      }
+      packed[m * (K / 8) + w] = word;
+    }
+}
+
+void hbo_unpack_int4(const uint32_t *packed, int64_t M, int64_t K, int8_t *q) {
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t w = 0; w < K / 8; w++) {
+      uint32_t word = packed[m * (K / 8) + w];
+      for (int j = 0; j < 8; j++) {
+        int h = j / 4, b = j % 4;
+        int nib = (int)((word >> (8 * b + 4 * h)) & 0xfu);
+        q[m * K + 8 * w + j] = (int8_t)(nib >= 8 ? nib - 16 : nib);
+      }
+    }
+}
+
+/* X -> (codes, scales, rowsum).  With hadamard != 0 the row is first rotated
+ * (X_r = Hadamard(X), Eq. 9 without the normalisation layer); with
+ * hadamard == 0 it is quantised as is (plain BitLinear input).
+ * codes: int8 [M][K] for bits = 8, uint32 [M][K/8] (INT4 layout) for bits = 4.
+ * xr_out (nullable): the fp32 values that were quantised, [M][K].
+ * Returns 0, or 2 for a bad shape / mode. */
+int hbo_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                 int hadamard, int bits, void *codes, float *scales,
+                 int32_t *rowsum, float *xr_out) {
+  if (M < 0 || K <= 0 || ldx < K || (bits != 8 && bits != 4)) return 2;
+  if (hadamard && !is_pow2(K)) return 2;
+  if (bits == 4 && K % 8 != 0) return 2;
+  const double scale = 1.0 / sqrt((double)K);
+#pragma omp parallel
+  {
+    double *t = (double *)malloc((size_t)K * sizeof(double));
+    float *xr = (float *)malloc((size_t)K * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)K);
+#pragma omp for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+      if (hadamard) {
+        for (int64_t k = 0; k < K; k++) t[k] = (double)load_elem(x, x_dtype, m * ldx + k);
+        hbo_fwht_f64(t, K);
+        for (int64_t k = 0; k < K; k++) xr[k] = (float)(t[k] * scale);
+      } else {
+        for (int64_t k = 0; k < K; k++) xr[k] = load_elem(x, x_dtype, m * ldx + k);
+      }
+      if (xr_out) memcpy(xr_out + m * K, xr, (size_t)K * sizeof(float));
+      int32_t rs;
+      float s = quantize_row(xr, K, bits, q, &rs);
+      scales[m] = s;
+      if (rowsum) rowsum[m] = rs;
+      if (bits == 8)
+        memcpy((int8_t *)codes + m * K, q, (size_t)K);
+      else
+        hbo_pack_int4(q, 1, K, (uint32_t *)codes + m * (K / 8));
+    }
+    free(t);
+    free(xr);
+    free(q);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Ternary weight quantizer  [BNv2 §3.4 "Weight Quantization",         */
+/* Eq. 1-2]                                                            */
+/* ------------------------------------------------------------------ */
+
+void hbo_pack_ternary(const int8_t *q, int64_t N, int64_t K, uint32_t *packed) {
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t w = 0; w < K / 16; w++) {
+      uint32_t word = 0;
+      for (int j = 0; j < 16; j++) {
+        int s = j / 4, b = j % 4;
+        uint32_t c = (uint32_t)(q[n * K + 16 * w + j] + 1);
+        word |= c << (8 * b + 2 * s);
+      }
+      packed[n * (K / 16) + w] = word;
+    }
+}
+
+/* Returns the number of invalid 2-bit fields (value 3) met; they decode as 0. */
+int64_t hbo_unpack_ternary(const uint32_t *packed, int64_t N, int64_t K, int8_t *q) {
+  int64_t bad = 0;
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t w = 0; w < K / 16; w++) {
+      uint32_t word = packed[n * (K / 16) + w];
+      for (int j = 0; j < 16; j++) {
+        int s = j / 4, b = j % 4;
+        int c = (int)((word >> (8 * b + 2 * s)) & 3u);
+        if (c == 3) {
+          bad++;
+          c = 1;
+        }
+        q[n * K + 16 * w + j] = (int8_t)(c - 1);
+      }
+    }
+  return bad;
+}
+
+/* alpha = mean(|W|) over the whole matrix (fp64 sum, one fp32 result);
+ * q = RoundClip(W / (alpha + eps), -1, 1).  W is fp32 or bf16 [N][K].
+ * Writes the packed codes, alpha, and (nullable) the int8 codes. */
+int hbo_ternarize(const void *w, int w_dtype, int64_t N, int64_t K,
+                  uint32_t *packed, float *alpha, int8_t *q_out) {
+  if (N <= 0 || K <= 0 || K % 16 != 0) return 2;
+  double sum = 0.0;
+  for (int64_t i = 0; i < N * K; i++) sum += fabs((double)load_elem(w, w_dtype, i));
+  float a = (float)(sum / ((double)N * (double)K));
+  float d = a + HBO_EPS;
+  int8_t *q = (int8_t *)malloc((size_t)(N * K));
+  for (int64_t i = 0; i < N * K; i++)
+    q[i] = (int8_t)round_clip(load_elem(w, w_dtype, i) / d, -1.0f, 1.0f);
+  hbo_pack_ternary(q, N, K, packed);
+  if (q_out) memcpy(q_out, q, (size_t)(N * K));
+  free(q);
+  *alpha = a;
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Integer matmul and the full layer  [BNv2 §3.4 "H-BitLinear", Eq. 9] */
+/* ------------------------------------------------------------------ */
+
+static int8_t code_at(const void *codes, int bits, int64_t K, int64_t m, int64_t k) {
+  if (bits == 8) return ((const int8_t *)codes)[m * K + k];
+  uint32_t word = ((const uint32_t *)codes)[m * (K / 8) + k / 8];
+  int j = (int)(k % 8), h = j / 4, b = j % 4;
+  int nib = (int)((word >> (8 * b + 4 * h)) & 0xfu);
+  return (int8_t)(nib >= 8 ? nib - 16 : nib);
+}
+
+static int8_t weight_at(const uint32_t *packed, int64_t K, int64_t n, int64_t k) {
+  uint32_t word = packed[n * (K / 16) + k / 16];
+  int j = (int)(k % 16), s = j / 4, b = j % 4;
+  int c = (int)((word >> (8 * b + 2 * s)) & 3u);
+  return (int8_t)(c - 1);
+}
+
+/* acc[m][n] = sum_k qx[m][k] * qw[n][k]: a plain triple loop.
+ * Returns 0, 2 on a bad shape, 3 if a sum does not fit int32 (cannot happen
+ * for K <= 2^23). */
+int hbo_gemm_i32(const void *codes, int bits, const uint32_t *packed, int64_t M,
+                 int64_t N, int64_t K, int32_t *acc) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || (bits != 8 && bits != 4)) return 2;
+  int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t n = 0; n < N; n++) {
+      int64_t s = 0;
+      for (int64_t k = 0; k < K; k++)
+        s += (int64_t)code_at(codes, bits, K, m, k) * (int64_t)weight_at(packed, K, n, k);
+      if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+      acc[m * N + n] = (int32_t)s;
+    }
+  }
+  return overflow ? 3 : 0;
+}
+
+/* Y = Q_w(W) . Q(X_r), row-major: y[m][n] = (s_m * alpha) * acc[m][n].
+ * y64 (fp64) is the value; y_bf16 (nullable) is the same value rounded to
+ * bf16 through fp32, the output type of the GPU layer. */
+int hbo_dequant_output(const int32_t *acc, const float *scales, float alpha,
+                       int64_t M, int64_t N, double *y64, uint16_t *y_bf16) {
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t n = 0; n < N; n++) {
+      double v = (double)scales[m] * (double)alpha * (double)acc[m * N + n];
+      if (y64) y64[m * N + n] = v;
+      if (y_bf16) y_bf16[m * N + n] = hbo_f32_to_bf16((float)v);
+    }
+  return 0;
+}
+
+/* The whole forward for one layer: quantise X (optionally rotating it),
+ * integer matmul against packed ternary weights, rescale.  Writes y64
+ * [M][N]; the codes/scales/acc scratch is allocated here. */
+int hbo_forward(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                int hadamard, int bits, const uint32_t *packed, float alpha,
+                int64_t N, double *y64) {
+  size_t code_bytes = (bits == 8) ? (size_t)(M * K) : (size_t)(M * (K / 8)) * 4;
+  void *codes = malloc(code_bytes ? code_bytes : 1);
+  float *scales = (float *)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
+  int32_t *acc = (int32_t *)malloc((size_t)(M * N > 0 ? M * N : 1) * sizeof(int32_t));
+  int rc = hbo_quantize(x, x_dtype, M, K, ldx, hadamard, bits, codes, scales, NULL, NULL);
+  if (rc == 0) rc = hbo_gemm_i32(codes, bits, packed, M, N, K, acc);
+  if (rc == 0) rc = hbo_dequant_output(acc, scales, alpha, M, N, y64, NULL);
+  free(codes);
+  free(scales);
+  free(acc);
+  return rc;
+}
+
+/* Number of OpenMP threads the parallel loops above use (1 without OpenMP). */
+int hbo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,348 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Sources of truth used here, per function of the oracle:
+  Hadamard  - the Sylvester recursion of Eq. 5-6 built independently with
+              integer block matrices (exact); scipy.linalg.hadamard (a library
+              routine for the same natural-order matrix); the hand-written H~_2
+              in tests/golden/hadamard_h2.txt; closed forms (H e0, H 1, spikes);
+              invariants (H H = I, norm preservation, linearity); the page's own
+              op count (tests/golden/fwht_opcount.txt).
+  quantizer - hand-worked cases (tests/golden/quant_cases.txt); range and error
+              invariants; code frequencies on Gaussian rows against the normal
+              CDF (closed form).
+  ternarizer- hand-worked case; idempotence on already-ternary matrices;
+              alpha, zero and +-1 fractions on Gaussian weights against closed
+              forms.
+  packing   - hand-worked words (tests/golden/packing_cases.txt); round trips.
+  int GEMM  - numpy int64 matmul; all-(+1) weights give the row sums; identity
+              weights give the codes back.
+  forward   - closed form: for x = H z with integer z the layer returns
+              alpha * T z exactly (INT8) or alpha * T (3c/sqrt7) sign(z) (INT4).
+All formulas: architecture write-up of "BitNet v2: Native 4-bit Activations
+with Hadamard Transformation for 1-bit LLMs", §3.4.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+from scipy.stats import norm
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    rows, kv = [], {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.split()
+            else:
+                rows.append([float(t) for t in line.split()])
+    return rows, kv
+
+
+def sylvester(m):
+    """Unnormalised H~_m from the recursion H~_0 = (1), H~_m = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1), np.int64)
+    for _ in range(m):
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+# ---------------------------------------------------------------- Hadamard
+
+def test_golden_h2_matches_recursion_and_oracle():
+    rows, _ = read_golden("hadamard_h2.txt")
+    h2 = np.array(rows)
+    assert np.array_equal(h2, sylvester(2))
+    # oracle applied to the unit vectors gives the columns of H~_2
+    for j in range(4):
+        e = np.zeros(4)
+        e[j] = 1.0
+        col, _ = oracle.fwht_unnormalized(e)
+        assert np.array_equal(col, h2[:, j])
+
+
+@pytest.mark.parametrize("m", range(0, 7))
+def test_fwht_equals_sylvester_product_exactly(m):
+    n = 1 << m
+    rng = np.random.default_rng(m)
+    x = rng.integers(-1000, 1000, size=(5, n)).astype(np.float64)
+    h = sylvester(m)
+    for row in x:
+        got, ops = oracle.fwht_unnormalized(row)
+        assert np.array_equal(got, h @ row)  # integer inputs: exact in fp64
+        assert ops == n * m
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 256, 1024])
+def test_hadamard_equals_scipy(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((3, n)).astype(np.float32)
+    want = x.astype(np.float64) @ (scipy.linalg.hadamard(n).T / math.sqrt(n))
+    got = oracle.hadamard(x)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_fwht_opcount_matches_page():
+    rows, _ = read_golden("fwht_opcount.txt")
+    n, ops_page, dense = (int(v) for v in rows[0])
+    _, ops = oracle.fwht_unnormalized(np.zeros(n))
+    # the page counts n*log2(n) operations; a radix-2 FWHT does exactly that
+    assert ops == ops_page
+    assert dense == n * n and round(dense / ops) == 341
+
+
+@pytest.mark.parametrize("n", [16, 256, 4096, 16384])
+def test_hadamard_involution_norm_linearity(n):
+    rng = np.random.default_rng(7 + n)
+    x = rng.standard_normal((2, n)).astype(np.float32)
+    y = oracle.hadamard(x)
+    # H is symmetric and orthogonal: H(Hx) = x, |Hx| = |x|
+    yy = oracle.hadamard(y.astype(np.float32))
+    np.testing.assert_allclose(yy, x, atol=1e-6 * np.abs(x).max())
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x.astype(np.float64), axis=1),
+                               rtol=1e-12)
+    # linearity on combinations that are exact in fp32 (bf16-valued inputs)
+    xb = workloads.bf16_to_f32(workloads.random_rows(8 + n, 2, n, "normal"))
+    y = oracle.hadamard(xb)
+    u = (np.float32(2.0) * xb[:1] + xb[1:]).astype(np.float32)
+    assert np.array_equal(u.astype(np.float64), 2.0 * xb[:1].astype(np.float64) + xb[1:])
+    y2 = oracle.hadamard(u)
+    np.testing.assert_allclose(y2[0], 2.0 * y[0] + y[1], atol=1e-9 * np.abs(y).max())
+
+
+@pytest.mark.parametrize("n", [4, 1024, 16384])
+def test_hadamard_special_vectors(n):
+    e0 = np.zeros((1, n), np.float32)
+    e0[0, 0] = 1
+    np.testing.assert_allclose(oracle.hadamard(e0)[0], np.full(n, 1 / math.sqrt(n)), rtol=1e-15)
+    ones = np.ones((1, n), np.float32)
+    want = np.zeros(n)
+    want[0] = math.sqrt(n)
+    np.testing.assert_allclose(oracle.hadamard(ones)[0], want, atol=1e-12)
+    # a spike A e_j is spread evenly: |y_i| = A / sqrt(n) for every i
+    spike = np.zeros((1, n), np.float32)
+    spike[0, n // 3] = 50.0
+    np.testing.assert_allclose(np.abs(oracle.hadamard(spike)[0]), 50.0 / math.sqrt(n), rtol=1e-15)
+
+
+def test_hadamard_bf16_input_is_exact_widening():
+    xb = workloads.random_rows(3, 4, 512)
+    np.testing.assert_array_equal(oracle.hadamard(xb), oracle.hadamard(workloads.bf16_to_f32(xb)))
+
+
+# ---------------------------------------------------------------- quantizers
+
+def test_golden_int8_case():
+    _, kv = read_golden("quant_cases.txt")
+    x = np.array([kv["int8.x"]], np.float32)
+    codes, scales, rowsum = oracle.quantize(x, 8, hadamard=False)
+    assert codes[0].tolist() == [int(v) for v in kv["int8.codes"]]
+    assert scales[0] == np.float32(float(kv["int8.scale"][0]))
+    assert rowsum[0] == int(kv["int8.rowsum"][0])
+
+
+def test_golden_int4_case():
+    _, kv = read_golden("quant_cases.txt")
+    x = np.array([kv["int4.x"]], np.float32)
+    codes, scales, rowsum = oracle.quantize(x, 4, hadamard=False)
+    assert oracle.unpack_int4(codes, 8)[0].tolist() == [int(v) for v in kv["int4.codes"]]
+    assert scales[0] == np.float32(float(kv["int4.scale"][0]))
+    assert rowsum[0] == int(kv["int4.rowsum"][0])
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("had", [True, False])
+def test_quantizer_invariants(bits, had):
+    x = workloads.student_t_rows(11, 0, 64, 1024, 0.01, 20.0, as_bf16=False)
+    codes, s, rowsum, xr = oracle.quantize(x, bits, hadamard=had, want_xr=True)
+    q = oracle.codes_int8(codes, bits, 1024).astype(np.int64)
+    assert np.array_equal(q.sum(1), rowsum)
+    if bits == 8:
+        assert q.min() >= -127 and q.max() <= 127  # absmax never reaches -128
+        assert np.all(np.abs(q).max(1) == 127)
+        np.testing.assert_allclose(s, np.abs(xr).max(1) / 127, rtol=1e-6)
+        # |x - s q| <= 1/(2f) + |q| |1/f - s| with 1/f - s = eps/127
+        err = np.abs(xr - s[:, None] * q)
+        bound = s[:, None] * 0.5 + (np.abs(q) + 1) * 1e-5 / 127 + 1e-6 * np.abs(xr)
+        assert np.all(err <= bound)
+    else:
+        assert q.min() >= -8 and q.max() <= 7
+        np.testing.assert_allclose(s, np.abs(xr).mean(1) / math.sqrt(7), rtol=1e-6)
+        inside = (q > -8) & (q < 7)
+        err = np.abs(xr - s[:, None] * q)
+        bound = s[:, None] * 0.5 + (np.abs(q) + 1) * 1e-5 / math.sqrt(7) + 1e-6 * np.abs(xr)
+        assert np.all(err[inside] <= bound[inside])
+    if had:
+        np.testing.assert_allclose(xr, oracle.hadamard(x).astype(np.float32), rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantizer_scale_invariance(bits):
+    # codes(c x) = codes(x) up to eps: exact power-of-two scaling of the input
+    x = workloads.random_rows(5, 32, 512, "normal", as_bf16=False)
+    c1, s1, _ = oracle.quantize(x, bits)
+    c2, s2, _ = oracle.quantize((x * np.float32(4.0)).astype(np.float32), bits)
+    q1 = oracle.codes_int8(c1, bits, 512)
+    q2 = oracle.codes_int8(c2, bits, 512)
+    assert np.mean(q1 != q2) < 1e-3
+    np.testing.assert_allclose(s2, 4 * s1, rtol=1e-6)
+
+
+def test_int4_code_frequencies_on_gaussian_rows():
+    # For x ~ N(0,1) per row, beta -> sqrt(2/pi) and q = round(x sqrt7/beta):
+    #   P(q = 7) = P(x >= 6.5 beta/sqrt7), P(q = -8) = P(x < -7.5 beta/sqrt7),
+    #   P(q = 0) = P(|x| <= 0.5 beta/sqrt7)  (normal CDF, closed form).
+    x = workloads.random_rows(21, 512, 4096, "normal", as_bf16=False)
+    codes, _, _ = oracle.quantize(x, 4, hadamard=False)
+    q = oracle.unpack_int4(codes, 4096)
+    b = math.sqrt(2 / math.pi) / math.sqrt(7)
+    p7 = 1 - norm.cdf(6.5 * b)
+    pm8 = norm.cdf(-7.5 * b)
+    p0 = norm.cdf(0.5 * b) - norm.cdf(-0.5 * b)
+    n = q.size
+    for got, want in ((np.mean(q == 7), p7), (np.mean(q == -8), pm8), (np.mean(q == 0), p0)):
+        assert abs(got - want) < 6 * math.sqrt(want * (1 - want) / n) + 2e-4
+    assert abs(p7 - 0.025) < 0.001 and abs(pm8 - 0.0118) < 0.001
+
+
+# ---------------------------------------------------------------- ternarizer
+
+def test_golden_ternary_case():
+    _, kv = read_golden("quant_cases.txt")
+    w = np.array([kv["ternary.w"]], np.float32)
+    packed, alpha, q = oracle.ternarize(w)
+    assert q[0].tolist() == [int(v) for v in kv["ternary.codes"]]
+    assert abs(alpha - float(kv["ternary.alpha"][0])) < 1e-7
+
+
+def test_ternarizer_idempotent_on_ternary_matrices():
+    rng = np.random.default_rng(3)
+    t = rng.integers(-1, 2, size=(64, 256)).astype(np.int8)
+    for c in (0.02, 1.0, 37.5):
+        _, alpha, q = oracle.ternarize((t * np.float32(c)).astype(np.float32))
+        assert np.array_equal(q, t)
+        assert abs(alpha - c * np.mean(np.abs(t))) <= 1e-6 * c
+
+
+def test_ternarizer_gaussian_statistics():
+    # W ~ N(0, s^2): alpha -> s sqrt(2/pi); q = 0 iff |w| < alpha/2, so
+    # P(q=0) = 2 Phi(sqrt(2/pi)/2) - 1 = 0.3101, P(q=+-1) = 0.3450 each.
+    w = workloads.gaussian_weights(5, 0, 1024, 4096)
+    _, alpha, q = oracle.ternarize(w)
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+    assert abs(alpha / workloads.W_STD - math.sqrt(2 / math.pi)) < 2e-3
+    p0 = 2 * norm.cdf(math.sqrt(2 / math.pi) / 2) - 1
+    n = q.size
+    assert abs(np.mean(q == 0) - p0) < 6 * math.sqrt(p0 * (1 - p0) / n) + 1e-3
+    assert abs(np.mean(q == 1) - (1 - p0) / 2) < 2e-3
+    assert abs(p0 - 0.3101) < 1e-4
+
+
+# ---------------------------------------------------------------- packing
+
+def test_golden_packing_words():
+    _, kv = read_golden("packing_cases.txt")
+    qt = np.array([[int(v) for v in kv["ternary.codes"]]], np.int8)
+    assert oracle.pack_ternary(qt)[0, 0] == int(kv["ternary.word"][0], 16)
+    q4 = np.array([[int(v) for v in kv["int4.codes"]]], np.int8)
+    assert oracle.pack_int4(q4)[0, 0] == int(kv["int4.word"][0], 16)
+
+
+def test_pack_roundtrips():
+    rng = np.random.default_rng(9)
+    t = rng.integers(-1, 2, size=(17, 512)).astype(np.int8)
+    back, bad = oracle.unpack_ternary(oracle.pack_ternary(t), 512)
+    assert bad == 0 and np.array_equal(back, t)
+    q = rng.integers(-8, 8, size=(9, 256)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(q), 256), q)
+
+
+# ---------------------------------------------------------------- integer GEMM
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_equals_numpy_matmul(bits):
+    rng = np.random.default_rng(bits)
+    M, N, K = 13, 48, 320
+    lo, hi = (-128, 128) if bits == 8 else (-8, 8)
+    q = rng.integers(lo, hi, size=(M, K)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    codes = q if bits == 8 else oracle.pack_int4(q)
+    acc = oracle.gemm_i32(codes, bits, oracle.pack_ternary(t), K)
+    assert np.array_equal(acc, q.astype(np.int64) @ t.astype(np.int64).T)
+
+
+def test_gemm_special_weights():
+    rng = np.random.default_rng(1)
+    K = 64
+    q = rng.integers(-128, 128, size=(5, K)).astype(np.int8)
+    ones = np.ones((16, K), np.int8)
+    acc = oracle.gemm_i32(q, 8, oracle.pack_ternary(ones), K)
+    assert np.all(acc == q.astype(np.int64).sum(1, keepdims=True))
+    eye = np.eye(K, dtype=np.int8)
+    assert np.array_equal(oracle.gemm_i32(q, 8, oracle.pack_ternary(eye), K), q.astype(np.int32))
+
+
+# ---------------------------------------------------------------- forward
+
+def _rotated_integer_inputs(M, K, zmax, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.integers(-zmax, zmax + 1, size=(M, K)).astype(np.float64)
+    z[:, 0] = zmax  # gamma = zmax exactly
+    h = sylvester(int(math.log2(K))).astype(np.float64) / math.sqrt(K)
+    x = (z @ h.T).astype(np.float32)  # x = H z, so Hadamard(x) = z (H H = I)
+    return z, x
+
+
+def test_forward_closed_form_int8():
+    M, K, N = 6, 256, 48
+    z, x = _rotated_integer_inputs(M, K, 127, 4)
+    rng = np.random.default_rng(5)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed, alpha, q = oracle.ternarize((t * np.float32(0.25)).astype(np.float32))
+    assert np.array_equal(q, t)
+    y = oracle.forward(x, packed, alpha, 8, hadamard=True)
+    want = float(alpha) * (z @ t.astype(np.float64).T)
+    assert np.linalg.norm(y - want) <= 1e-6 * np.linalg.norm(want)
+
+
+def test_forward_closed_form_int4():
+    # z in {-c, +c}: beta = c, codes = round(+-sqrt7) = +-3, s = c/sqrt7,
+    # so Q(X_r) = (3c/sqrt7) sign(z) and Y = alpha T Q(X_r).
+    M, K, N, c = 4, 512, 32, 3.0
+    rng = np.random.default_rng(6)
+    z = c * rng.choice([-1.0, 1.0], size=(M, K))
+    h = sylvester(9).astype(np.float64) / math.sqrt(K)
+    x = (z @ h.T).astype(np.float32)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed, alpha, _ = oracle.ternarize(t.astype(np.float32))
+    y = oracle.forward(x, packed, alpha, 4, hadamard=True)
+    want = float(alpha) * (3 * c / math.sqrt(7)) * (np.sign(z) @ t.astype(np.float64).T)
+    assert np.linalg.norm(y - want) <= 1e-5 * np.linalg.norm(want)
+
+
+def test_forward_zero_rows_give_zero():
+    x = np.zeros((3, 64), np.float32)
+    w = workloads.gaussian_weights(1, 0, 16, 64)
+    packed, alpha, _ = oracle.ternarize(w)
+    for bits in (8, 4):
+        assert np.all(oracle.forward(x, packed, alpha, bits) == 0)
+
+
+def test_dequant_output_bf16_rounding():
+    acc = np.array([[1, -3, 1000, 0]], np.int32)
+    s = np.array([0.1], np.float32)
+    y64, yb = oracle.dequant_output(acc, s, np.float32(0.5))
+    np.testing.assert_allclose(y64[0], [0.05, -0.15, 50.0, 0.0], rtol=1e-7)
+    np.testing.assert_array_equal(workloads.bf16_to_f32(yb)[0],
+                                  workloads.bf16_to_f32(workloads.bf16_bits(y64.astype(np.float32)))[0])
