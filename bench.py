@@ -1,0 +1,256 @@
+"""Throughput of the H-BitLinear forward on one MI355X.
+
+Default workload: the attention output projection of a 7B-shaped BitNet v2
+block with the rotation, M=2048 tokens, K=N=4096, INT4 activations (bf16
+Student-t(3) input, 1 % of channels x20; N(0, 0.02^2) weights, ternarised).
+One step = one whole layer (rotation + quantisation, then the ternary
+matmul with its rescale) over the batch, inputs already resident in HBM.
+
+Prints one JSON line.  ``roofline`` is for the dominant kernel (the
+matrix-core matmul), its average duration measured with HIP events over
+back-to-back launches on the stream it runs on; ``cpu_baseline`` is the CPU
+oracle timed on a bounded sample of rows of the same workload.
+
+Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "H-BitLinear tokens/sec & effective TOPS at 7B shapes; % HBM BW / % i8 MFMA peak"
+HBM_PEAK_GBS = 8000.0
+I8_PEAK_TOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wo_7b",
+                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b"])
+    ap.add_argument("--decode-m", type=int, default=1)
+    ap.add_argument("--decode-k", type=int, default=16384)
+    ap.add_argument("--decode-mats", type=int, default=0,
+                    help="distinct weight matrices cycled (0: enough for >= 512 MiB)")
+    ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def dev_x(x_np):
+    import torch
+    if x_np.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x_np).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
+
+
+def time_stream(fn, reps):
+    """Average duration (s) of ``fn`` over ``reps`` back-to-back launches,
+    from HIP events recorded on the current stream (where the library
+    enqueues its kernels)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
+def cpu_baseline(x_np, w_np, bits, had, rows, unit_per_row=1.0):
+    import oracle
+    packed, alpha, _ = oracle.ternarize(w_np)
+    xs = np.ascontiguousarray(x_np[:rows])
+    t0 = time.perf_counter()
+    oracle.forward(xs, packed, alpha, bits, hadamard=had)
+    dt = time.perf_counter() - t0
+    return {"value": rows * unit_per_row / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{rows} of the workload's token rows, whole layer (fp64 rotation, "
+                                        f"quantiser, triple-loop integer matmul), {dt:.1f} s"}
+
+
+def layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, reps):
+    """Per-kernel timing of one layer: rotation+quantisation, then matmul."""
+    q, s, rs = hbl.hadamard_quant(x, bits, hadamard=had)
+    out = hbl.ternary_gemm(q, bits, s, rs, packed, alpha, K)
+    t_q = time_stream(lambda: hbl.hadamard_quant(x, bits, hadamard=had), reps)
+    t_g = time_stream(lambda: hbl.ternary_gemm(q, bits, s, rs, packed, alpha, K, out=out), reps)
+    x_bytes = M * K * x.element_size()
+    code_bytes = M * K // (2 if bits == 4 else 1)
+    q_bytes = x_bytes + code_bytes + 8 * M
+    return t_q, t_g, q_bytes, code_bytes
+
+
+def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
+    M, K = x_np.shape
+    N = w_np.shape[0]
+    x = dev_x(x_np)
+    packed, alpha = hbl.ternarize_weights(torch.from_numpy(w_np).cuda())
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = hbl.forward_workspace(M, K, bits, "cuda")
+
+    def step():
+        hbl.forward(x, packed, alpha, bits, hadamard=had, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+
+    t_q, t_g, q_bytes, code_bytes = layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, args.kernel_reps)
+    ops = 2.0 * M * N * K
+    gemm_tops = ops / t_g / 1e12
+    w_bytes = N * K // 4
+    res = {
+        "metric": METRIC,
+        "value": M / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": label, "M": M, "K": K, "N": N, "bits": bits, "hadamard": had,
+                   "x_dtype": "bf16" if x_np.dtype == np.uint16 else "f32"},
+        "effective_tops": ops / dt / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "k_gemm (ternary matmul)", "achieved": gemm_tops,
+                     "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": gemm_tops / I8_PEAK_TOPS,
+                     "traffic": None, "avg_kernel_us": t_g * 1e6,
+                     "algorithmic_ops_per_launch": ops},
+        "quant_kernel": {"bound": "hbm", "avg_kernel_us": t_q * 1e6,
+                         "algorithmic_bytes_per_launch": q_bytes,
+                         "achieved_gbs": q_bytes / t_q / 1e9,
+                         "frac": q_bytes / t_q / 1e9 / HBM_PEAK_GBS},
+        "gemm_bytes_min": code_bytes + w_bytes + 2 * M * N,
+    }
+    return res
+
+
+def run_decode(args, hbl, torch):
+    import workloads
+    M, K, N = args.decode_m, args.decode_k, 4096
+    w_bytes = N * K // 4
+    n_mats = args.decode_mats or max(10, -(-(512 << 20) // w_bytes))
+    x = dev_x(workloads.decode_inputs(K, M))
+    # distinct matrices: the 10 seeded ones, repeated at distinct addresses
+    base = [hbl.ternarize_weights(torch.from_numpy(workloads.decode_weights(K, N, i)).cuda()) for i in range(10)]
+    mats = [(base[i % 10][0].clone(), base[i % 10][1].clone()) for i in range(n_mats)]
+    del base
+    bits = 8
+    q, s, rs = hbl.hadamard_quant(x, bits)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = hbl.forward_workspace(M, K, bits, "cuda")
+
+    def step(i):
+        p, a = mats[i % n_mats]
+        hbl.forward(x, p, a, bits, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    # matmul kernel alone, cycling the matrices
+    reps = max(args.kernel_reps, 2 * n_mats)
+    ctr = [0]
+
+    def g():
+        p, a = mats[ctr[0] % n_mats]
+        ctr[0] += 1
+        hbl.ternary_gemm(q, bits, s, rs, p, a, K, out=out)
+
+    t_g = time_stream(g, reps)
+    t_q = time_stream(lambda: hbl.hadamard_quant(x, bits), args.kernel_reps)
+    g_bytes = w_bytes + M * K + 8 * M + 2 * M * N
+    bw = g_bytes / t_g / 1e9
+    return {
+        "metric": METRIC, "value": M / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": f"decode M={M} K={K} N={N} INT8, {n_mats} matrices cycled", "M": M, "K": K,
+                   "N": N, "bits": 8, "hadamard": True, "matrices": n_mats},
+        "roofline": {"bound": "hbm", "kernel": "k_gemv (weight streaming)", "achieved": bw,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": bw / HBM_PEAK_GBS, "traffic": None,
+                     "avg_kernel_us": t_g * 1e6, "algorithmic_bytes_per_launch": g_bytes},
+        "quant_kernel": {"avg_kernel_us": t_q * 1e6},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_quantization_amd as hbl
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.workload == "decode":
+        res = run_decode(args, hbl, torch)
+        if not args.no_cpu_baseline:
+            x_np = workloads.decode_inputs(args.decode_k, args.decode_m)
+            w_np = workloads.decode_weights(args.decode_k, 4096, 0)
+            res["cpu_baseline"] = cpu_baseline(x_np, w_np, 8, True, args.decode_m)
+        print(json.dumps(res), flush=True)
+        return
+
+    if args.workload == "block_7b":
+        results = []
+        for bits in ([8, 4] if args.bits == 0 else [args.bits]):
+            tot_t, tot_ops = 0.0, 0.0
+            layers = {}
+            for name, K, N, had in workloads.BLOCK_7B_LAYERS:
+                x_np = workloads.block_input(workloads.BLOCK_7B_INPUT_OF[name])
+                w_np = workloads.block_weights(name)
+                r = run_layer(args, hbl, torch, x_np, w_np, bits, had, name)
+                layers[name] = {"ms": r["ms_per_step"], "gemm_tops": r["roofline"]["achieved"],
+                                "quant_gbs": r["quant_kernel"]["achieved_gbs"]}
+                tot_t += r["ms_per_step"]
+                tot_ops += 2.0 * r["config"]["M"] * N * K
+                del x_np
+            M = workloads.CONFIGS["block_7b"]["M"]
+            results.append({"bits": bits, "tokens_per_s": M / (tot_t / 1e3), "ms": tot_t,
+                            "effective_tops": tot_ops / (tot_t / 1e3) / 1e12, "layers": layers})
+        print(json.dumps({"metric": METRIC, "workload": "block_7b", "results": results}), flush=True)
+        return
+
+    c = {"tiny": workloads.tiny, "wo_7b": workloads.wo_7b, "wdown_7b": workloads.wdown_7b}[args.workload]()
+    label = {"tiny": "tiny: M=8 K=N=256 INT4 H-BitLinear",
+             "wo_7b": "wo_7b: 7B attention output projection, M=2048 K=N=4096 INT4 H-BitLinear",
+             "wdown_7b": "wdown_7b: 7B FFN down projection, M=4096 K=16384 N=4096 INT4 H-BitLinear"}[args.workload]
+    res = run_layer(args, hbl, torch, c["x"], c["w"], c["bits"], True, label)
+    if not args.no_cpu_baseline:
+        rows = {"tiny": 8, "wo_7b": 48, "wdown_7b": 8}[args.workload]
+        res["cpu_baseline"] = cpu_baseline(c["x"], c["w"], c["bits"], True, rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+// C ABI of libhbl: argument validation, workspace carving and dispatch to the
+// HIP kernels.  Every check runs on the host before anything is enqueued.
+#include "../../include/hbl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <climits>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "hbl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HBL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int elem_size(int dtype) { return dtype == HBL_DTYPE_BF16 ? 2 : 4; }
+
+int check_x(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, bool hadamard) {
+  if (x_dtype != HBL_DTYPE_F32 && x_dtype != HBL_DTYPE_BF16)
+    return fail(HBL_ERR_MODE, "x_dtype %d is neither HBL_DTYPE_F32 nor HBL_DTYPE_BF16", x_dtype);
+  if (M < 0 || M > (int64_t)INT_MAX) return fail(HBL_ERR_SHAPE, "M = %lld is out of range", (long long)M);
+  if (hadamard) {
+    if (!is_pow2(K) || K < 16 || K > HBL_MAX_K)
+      return fail(HBL_ERR_SHAPE, "K = %lld must be a power of two in [16, %d] with HBL_HADAMARD",
+                  (long long)K, HBL_MAX_K);
+  } else {
+    if (K < 64 || K % 64 != 0 || K > HBL_MAX_K)
+      return fail(HBL_ERR_SHAPE, "K = %lld must be a multiple of 64 in [64, %d]", (long long)K,
+                  HBL_MAX_K);
+  }
+  if (ldx < K) return fail(HBL_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if ((ldx * elem_size(x_dtype)) % 16 != 0)
+    return fail(HBL_ERR_ALIGN, "ldx * element size = %lld bytes is not a multiple of 16",
+                (long long)(ldx * elem_size(x_dtype)));
+  if (M > 0 && x == nullptr) return fail(HBL_ERR_NULL, "x is NULL");
+  if (!aligned16(x)) return fail(HBL_ERR_ALIGN, "x is not 16-byte aligned");
+  return HBL_OK;
+}
+
+int check_bits(int bits) {
+  if (bits != 8 && bits != 4) return fail(HBL_ERR_MODE, "bits = %d is neither 8 nor 4", bits);
+  return HBL_OK;
+}
+
+int check_flags(int flags) {
+  if (flags & ~HBL_HADAMARD) return fail(HBL_ERR_MODE, "unknown flag bits 0x%x", flags & ~HBL_HADAMARD);
+  return HBL_OK;
+}
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t ldo) {
+  if (M < 0) return fail(HBL_ERR_SHAPE, "M = %lld is negative", (long long)M);
+  if (N < 16 || N % 16 != 0) return fail(HBL_ERR_SHAPE, "N = %lld must be a positive multiple of 16", (long long)N);
+  if (K < 64 || K % 64 != 0) return fail(HBL_ERR_SHAPE, "K = %lld must be a positive multiple of 64", (long long)K);
+  if (ldo < N) return fail(HBL_ERR_SHAPE, "ldo = %lld < N = %lld", (long long)ldo, (long long)N);
+  if (ldo % 4 != 0) return fail(HBL_ERR_ALIGN, "ldo = %lld is not a multiple of 4", (long long)ldo);
+  // token rows are addressed with 64-bit offsets; the grid size is the limit
+  if ((M + 127) / 128 * ((N + 127) / 128) > (int64_t)INT_MAX)
+    return fail(HBL_ERR_SHAPE, "M x N is too large for one launch");
+  return HBL_OK;
+}
+
+int cu_count_cached() {
+  static std::mutex mu;
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (counts[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    counts[dev] = c;
+  }
+  return counts[dev];
+}
+
+size_t codes_bytes(int64_t M, int64_t K, int bits) {
+  return bits == 8 ? (size_t)(M * K) : (size_t)(M * (K / 2));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hbl_version(void) { return 100; }
+
+const char* hbl_status_string(int status) {
+  switch (status) {
+    case HBL_OK: return "success";
+    case HBL_ERR_NULL: return "a required pointer is NULL";
+    case HBL_ERR_SHAPE: return "a size or leading dimension is out of range";
+    case HBL_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+    case HBL_ERR_MODE: return "unknown dtype, bits or flag value";
+    case HBL_ERR_WORKSPACE: return "workspace missing or too small";
+    case HBL_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+const char* hbl_last_error(void) { return g_last_error.c_str(); }
+
+int hbl_device_cu_count(void) {
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return c;
+}
+
+size_t hbl_ternarize_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return round256(sizeof(double) * (size_t)hbl::ternarize_partials(N, K));
+}
+
+int hbl_ternarize_weights(const void* w, int w_dtype, int64_t N, int64_t K, uint32_t* w_packed,
+                          float* alpha, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (w_dtype != HBL_DTYPE_F32 && w_dtype != HBL_DTYPE_BF16)
+    return fail(HBL_ERR_MODE, "w_dtype %d is neither HBL_DTYPE_F32 nor HBL_DTYPE_BF16", w_dtype);
+  if (N < 1 || K < 16 || K % 16 != 0)
+    return fail(HBL_ERR_SHAPE, "need N >= 1 and K a positive multiple of 16 (N = %lld, K = %lld)",
+                (long long)N, (long long)K);
+  if (!w || !w_packed || !alpha) return fail(HBL_ERR_NULL, "w, w_packed and alpha must be non-NULL");
+  if (!aligned16(w) || !aligned16(w_packed) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "w and w_packed must be 16-byte aligned, alpha 4-byte aligned");
+  const size_t need = hbl_ternarize_workspace_size(N, K);
+  if (!ws || ws_bytes < need)
+    return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
+  if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
+  hipError_t e = hbl::launch_ternarize(w, w_dtype == HBL_DTYPE_BF16, N, K, w_packed, alpha,
+                                       static_cast<double*>(ws), hbl::ternarize_partials(N, K),
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ternarize launch");
+  return HBL_OK;
+}
+
+int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, float* y,
+                     void* stream) {
+  g_last_error.clear();
+  int rc = check_x(x, x_dtype, M, K, ldx, true);
+  if (rc) return rc;
+  if (M > 0 && !y) return fail(HBL_ERR_NULL, "y is NULL");
+  if (!aligned16(y)) return fail(HBL_ERR_ALIGN, "y is not 16-byte aligned");
+  hipError_t e = hbl::launch_hadamard_f32(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, y,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hadamard launch");
+  return HBL_OK;
+}
+
+int hbl_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int flags,
+                       int bits, void* codes, float* scales, int32_t* rowsum, void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_bits(bits);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (rc) return rc;
+  if (M > 0 && (!codes || !scales)) return fail(HBL_ERR_NULL, "codes and scales must be non-NULL");
+  if (!aligned16(codes) || !aligned4(scales) || !aligned4(rowsum))
+    return fail(HBL_ERR_ALIGN, "codes must be 16-byte aligned, scales and rowsum 4-byte aligned");
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
+                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  return HBL_OK;
+}
+
+int hbl_ternary_gemm(const void* codes, int bits, const float* scales, const int32_t* rowsum,
+                     const uint32_t* w_packed, const float* alpha, int64_t M, int64_t N, int64_t K,
+                     int out_dtype, void* out, int64_t ldo, void* stream) {
+  g_last_error.clear();
+  int rc = check_bits(bits);
+  if (!rc) rc = check_gemm_shape(M, N, K, ldo);
+  if (rc) return rc;
+  if (out_dtype != HBL_OUT_BF16 && out_dtype != HBL_OUT_F32 && out_dtype != HBL_OUT_I32)
+    return fail(HBL_ERR_MODE, "out_dtype %d is not an HBL_OUT_* value", out_dtype);
+  if (M == 0) return HBL_OK;
+  if (!codes || !scales || !rowsum || !w_packed || !alpha || !out)
+    return fail(HBL_ERR_NULL, "codes, scales, rowsum, w_packed, alpha and out must be non-NULL");
+  if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(out) || !aligned4(scales) ||
+      !aligned4(rowsum) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "codes, w_packed and out must be 16-byte aligned");
+  hipError_t e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K,
+                                          out_dtype, out, ldo, cu_count_cached(),
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return HBL_OK;
+}
+
+size_t hbl_forward_workspace_size(int64_t M, int64_t K, int bits) {
+  if (M < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
+  return round256(codes_bytes(M, K, bits)) + 2 * round256(sizeof(float) * (size_t)M);
+}
+
+int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
+                int bits, const uint32_t* w_packed, const float* alpha, void* y, int64_t ldy, void* ws,
+                size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_bits(bits);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (!rc) rc = check_gemm_shape(M, N, K, ldy);
+  if (rc) return rc;
+  if (M == 0) return HBL_OK;
+  if (!w_packed || !alpha || !y) return fail(HBL_ERR_NULL, "w_packed, alpha and y must be non-NULL");
+  if (!aligned16(w_packed) || !aligned16(y) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "w_packed and y must be 16-byte aligned");
+  const size_t need = hbl_forward_workspace_size(M, K, bits);
+  if (!ws || ws_bytes < need)
+    return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
+  if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  void* codes = base;
+  float* scales = reinterpret_cast<float*>(base + round256(codes_bytes(M, K, bits)));
+  int32_t* rowsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scales) + round256(sizeof(float) * (size_t)M));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
+                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum, s);
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy,
+                               cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return HBL_OK;
+}
+
+}  // extern "C"

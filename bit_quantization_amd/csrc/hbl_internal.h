@@ -1,0 +1,32 @@
+// Internal declarations shared by the HIP kernel files and the C-ABI layer
+// of libhbl.  Nothing here is part of the public interface (include/hbl.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hbl {
+
+// Launchers.  Each validates nothing (the C-ABI layer has done that) and
+// returns the hipError_t of the launch.
+hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K,
+                                 int64_t ldx, bool hadamard, int bits,
+                                 void* codes, float* scales, int32_t* rowsum,
+                                 hipStream_t s);
+hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K,
+                               int64_t ldx, float* y, hipStream_t s);
+hipError_t launch_ternarize(const void* w, bool w_bf16, int64_t N, int64_t K,
+                            uint32_t* packed, float* alpha, double* partials,
+                            int n_partials, hipStream_t s);
+int ternarize_partials(int64_t N, int64_t K);
+
+// out_kind: 0 bf16, 1 f32, 2 i32 (the HBL_OUT_* values)
+hipError_t launch_ternary_gemm(const void* codes, int bits, const float* scales,
+                               const int32_t* rowsum, const uint32_t* wp,
+                               const float* alpha, int64_t M, int64_t N,
+                               int64_t K, int out_kind, void* out, int64_t ldo,
+                               int cu_count, hipStream_t s);
+
+// Token counts up to this take the weight-streaming kernel.
+constexpr int kGemvMaxM = 16;
+
+}  // namespace hbl

@@ -1,0 +1,435 @@
+// Per-token Walsh-Hadamard rotation fused with per-token activation
+// quantisation, for gfx950.
+//
+// What is computed (architecture write-up of "BitNet v2", §3.4):
+//   x_r = H_k x for each token row x of length K = 2^k, H_k the normalised
+//   Sylvester-Hadamard matrix ("The Hadamard Transformation", Eq. 5-6),
+//   evaluated as k radix-2 butterfly stages (a, b) -> (a + b, a - b) in fp32
+//   and one final multiplication by 2^{-k/2};
+//   then INT8 absmax (Eq. 7) or INT4 absmean (Eq. 8) per token:
+//     factor = Qmax / (stat + eps), code = clip(rint(x_r * factor)),
+//     scale = stat / Qmax.
+//
+// Work decomposition (one token row per group of T threads, T = 2^t):
+//   A row of K = 2^k elements is held in registers, E = 2^e per thread,
+//   e = max(3, ceil(k/2)), t = k - e.  Element index bits are split into
+//   lo (bits 0-2, an 8-element chunk = one 16-byte bf16 load), mid (t bits,
+//   the thread index in phase A) and hi (e - 3 bits).
+//   Phase A: each thread loads its chunks (lo, hi vary) and applies the
+//            butterfly stages of the lo and hi bits in registers.
+//   Phase B: the row is exchanged through LDS so that each thread holds the
+//            elements whose mid bits vary, and those t stages run in
+//            registers.  The result goes back to LDS.
+//   Output:  each thread re-reads contiguous 8-element chunks, applies the
+//            1/sqrt(K) scale, the row statistic is reduced across the row,
+//            and the codes are packed and stored contiguously.
+// The butterfly stages commute, so applying them in this order gives the
+// transform exactly in real arithmetic; fp32 rounding differs from a
+// sequential evaluation by a few ulps.
+//
+// LDS addresses are XOR-swizzled so that both the 16-byte chunk accesses of
+// phase A and the 4-byte strided accesses of phase B are free of bank
+// conflicts.
+#include "hbl_internal.h"
+
+namespace hbl {
+namespace {
+
+constexpr float kEps = 1e-5f;
+// (float)sqrt(7): the INT4 clipping constant of Eq. 8.
+constexpr float kSqrt7 = 2.6457513110645907f;
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Loads 8 consecutive elements starting at p (16-byte aligned) as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, float* v) {
+  if constexpr (BF16) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16lo(u.x); v[1] = bf16hi(u.x);
+    v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+    v[4] = bf16lo(u.z); v[5] = bf16hi(u.z);
+    v[6] = bf16lo(u.w); v[7] = bf16hi(u.w);
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// In-register radix-2 stages over register-index bits [B0, B1).
+template <int E, int B0, int B1>
+__device__ __forceinline__ void butterflies(float (&v)[E]) {
+#pragma unroll
+  for (int b = B0; b < B1; ++b) {
+    const int h = 1 << b;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], c = v[i + h];
+        v[i] = a + c;
+        v[i + h] = a - c;
+      }
+    }
+  }
+}
+
+// LDS address swizzle: flips bits 2-4 from bits >= 5 (an involution).
+template <int TL>
+__device__ __forceinline__ int swz(int e) {
+  if constexpr (TL >= 2) {
+    const int hi = (e >> (3 + TL)) & 3;
+    return e ^ (hi << 3) ^ (((e >> 5) & 1) << 2);
+  } else {
+    return e;
+  }
+}
+
+// Reduction of one value over the T threads of a row.  Every thread of the
+// row gets the same bits: the xor-butterfly pairs the same partials on
+// both sides, and the cross-wave step combines the waves in a fixed order.
+template <int T, bool IS_MAX>
+__device__ __forceinline__ float row_reduce(float v, float* red, int row, int tid) {
+  constexpr int W = T < 64 ? T : 64;
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) {
+    const float u = __shfl_xor(v, o);
+    v = IS_MAX ? fmaxf(v, u) : v + u;
+  }
+  if constexpr (T > 64) {
+    constexpr int NW = T / 64;
+    if ((tid & 63) == 0) red[row * NW + (tid >> 6)] = v;
+    __syncthreads();
+    float r = red[row * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      const float u = red[row * NW + i];
+      r = IS_MAX ? fmaxf(r, u) : r + u;
+    }
+    v = r;
+  }
+  return v;
+}
+
+template <int T>
+__device__ __forceinline__ int row_reduce_int(int v, int* red, int row, int tid) {
+  constexpr int W = T < 64 ? T : 64;
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  if constexpr (T > 64) {
+    constexpr int NW = T / 64;
+    if ((tid & 63) == 0) red[row * NW + (tid >> 6)] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r += red[row * NW + i];
+    v = r;
+  }
+  return v;
+}
+
+template <int LOG2K>
+struct Geom {
+  static constexpr int K = 1 << LOG2K;
+  static constexpr int EL = (LOG2K + 1) / 2 > 3 ? (LOG2K + 1) / 2 : 3;  // log2 E
+  static constexpr int TL = LOG2K - EL;                                 // log2 T
+  static constexpr int E = 1 << EL;
+  static constexpr int T = 1 << TL;
+  static constexpr int NC = E / 8;                 // 8-element chunks per thread
+  static constexpr int RPB = T >= 128 ? 1 : 128 / T;  // rows per block
+  static constexpr int THREADS = RPB * T;
+  static constexpr int RED = RPB * (T > 64 ? T / 64 : 1);
+};
+
+// OUT: 0 = codes (BITS 8 or 4), 1 = fp32 rotated values.
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+__global__ void __launch_bounds__(Geom<LOG2K>::THREADS)
+k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
+             void* __restrict__ codes, float* __restrict__ scales,
+             int32_t* __restrict__ rowsum, float* __restrict__ yout) {
+  using G = Geom<LOG2K>;
+  constexpr int K = G::K, E = G::E, T = G::T, TL = G::TL, EL = G::EL, NC = G::NC;
+  constexpr int ESZ = BF16 ? 2 : 4;
+
+  __shared__ __attribute__((aligned(16))) float lds[HAD ? G::RPB * K : 4];
+  __shared__ float redf[G::RED];
+  __shared__ int redi[G::RED];
+
+  const int row = threadIdx.x / T;
+  const int tid = threadIdx.x % T;
+  const int64_t m = (int64_t)blockIdx.x * G::RPB + row;
+  const bool live = m < M;
+  float* L = lds + (HAD ? row * K : 0);
+
+  // Phase A: chunk c of this thread covers elements (c << (3+TL)) | (tid << 3) | 0..7.
+  float v[E];
+  {
+    const char* xr = reinterpret_cast<const char*>(x) + (live ? m : 0) * ldx * ESZ;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = (c << (3 + TL)) | (tid << 3);
+      if (live) {
+        load8<BF16>(xr + (int64_t)e0 * ESZ, v + 8 * c);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * c + j] = 0.0f;
+      }
+    }
+  }
+
+  if constexpr (HAD) {
+    // stages of the lo and hi bits: every register bit
+    butterflies<E, 0, EL>(v);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = (c << (3 + TL)) | (tid << 3);
+      *reinterpret_cast<float4*>(L + swz<TL>(e0)) = make_float4(v[8 * c], v[8 * c + 1], v[8 * c + 2], v[8 * c + 3]);
+      *reinterpret_cast<float4*>(L + swz<TL>(e0 + 4)) = make_float4(v[8 * c + 4], v[8 * c + 5], v[8 * c + 6], v[8 * c + 7]);
+    }
+    __syncthreads();
+    // Phase B: register r holds mid = r & (T-1); the remaining e bits of the
+    // element index are rho = ((r >> TL) << TL) | tid, split into lo and hi.
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int rho = ((r >> TL) << TL) | tid;
+      const int e = ((rho >> 3) << (3 + TL)) | ((r & (T - 1)) << 3) | (rho & 7);
+      v[r] = L[swz<TL>(e)];
+    }
+    butterflies<E, 0, TL>(v);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int rho = ((r >> TL) << TL) | tid;
+      const int e = ((rho >> 3) << (3 + TL)) | ((r & (T - 1)) << 3) | (rho & 7);
+      L[swz<TL>(e)] = v[r];
+    }
+    __syncthreads();
+    // back to the chunk layout of phase A, with the normalisation 2^{-k/2}
+    const float scale = (LOG2K % 2 == 0) ? __uint_as_float((uint32_t)(127 - LOG2K / 2) << 23)
+                                          : (float)(1.0 / __builtin_sqrt((double)K));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = (c << (3 + TL)) | (tid << 3);
+      const float4 a = *reinterpret_cast<const float4*>(L + swz<TL>(e0));
+      const float4 b = *reinterpret_cast<const float4*>(L + swz<TL>(e0 + 4));
+      v[8 * c + 0] = a.x * scale; v[8 * c + 1] = a.y * scale;
+      v[8 * c + 2] = a.z * scale; v[8 * c + 3] = a.w * scale;
+      v[8 * c + 4] = b.x * scale; v[8 * c + 5] = b.y * scale;
+      v[8 * c + 6] = b.z * scale; v[8 * c + 7] = b.w * scale;
+    }
+  }
+
+  if constexpr (OUT == 1) {
+    if (live) {
+      float* yr = yout + m * (int64_t)K;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int e0 = (c << (3 + TL)) | (tid << 3);
+        reinterpret_cast<float4*>(yr + e0)[0] = make_float4(v[8 * c], v[8 * c + 1], v[8 * c + 2], v[8 * c + 3]);
+        reinterpret_cast<float4*>(yr + e0)[1] = make_float4(v[8 * c + 4], v[8 * c + 5], v[8 * c + 6], v[8 * c + 7]);
+      }
+    }
+    return;
+  } else {
+    // row statistic: gamma = max|x_r| (INT8) or sum|x_r| (INT4, divided by K)
+    float st = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) st = (BITS == 8) ? fmaxf(st, fabsf(v[i])) : st + fabsf(v[i]);
+    st = row_reduce<T, BITS == 8>(st, redf, row, tid);
+    float f, s;
+    if constexpr (BITS == 8) {
+      f = 127.0f / (st + kEps);
+      s = st / 127.0f;
+    } else {
+      const float beta = st / (float)K;  // exact: K is a power of two
+      f = kSqrt7 / (beta + kEps);
+      s = beta / kSqrt7;
+    }
+    constexpr float lo = BITS == 8 ? -128.0f : -8.0f;
+    constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
+    int qsum = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      int q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float r = __builtin_rintf(v[8 * c + j] * f);
+        q[j] = (int)fminf(fmaxf(r, lo), hi);
+        qsum += q[j];
+      }
+      const int e0 = (c << (3 + TL)) | (tid << 3);
+      if (live) {
+        if constexpr (BITS == 8) {
+          uint32_t w0 = (q[0] & 0xff) | ((q[1] & 0xff) << 8) | ((q[2] & 0xff) << 16) | ((uint32_t)q[3] << 24);
+          uint32_t w1 = (q[4] & 0xff) | ((q[5] & 0xff) << 8) | ((q[6] & 0xff) << 16) | ((uint32_t)q[7] << 24);
+          *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(codes) + m * (int64_t)K + e0) = make_uint2(w0, w1);
+        } else {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w |= (uint32_t)(q[j] & 0xf) << (8 * (j & 3) + 4 * (j >> 2));
+          reinterpret_cast<uint32_t*>(codes)[m * (int64_t)(K / 8) + (e0 >> 3)] = w;
+        }
+      }
+    }
+    qsum = row_reduce_int<T>(qsum, redi, row, tid);
+    if (live && tid == 0) {
+      scales[m] = s;
+      if (rowsum) rowsum[m] = qsum;
+    }
+  }
+}
+
+// Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
+// per block of 256 threads, each holding up to 8 chunks of 8 elements.
+template <bool BF16, int BITS>
+__global__ void __launch_bounds__(256)
+k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
+              void* __restrict__ codes, float* __restrict__ scales,
+              int32_t* __restrict__ rowsum) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int CH = 8;
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const int nchunk = K / 8;
+  const char* xr = reinterpret_cast<const char*>(x) + m * ldx * ESZ;
+  float v[CH * 8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = tid + 256 * c;
+    if (ch < nchunk) {
+      load8<BF16>(xr + (int64_t)ch * 8 * ESZ, v + 8 * c);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[8 * c + j] = 0.0f;
+    }
+  }
+  float st = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH * 8; ++i) st = (BITS == 8) ? fmaxf(st, fabsf(v[i])) : st + fabsf(v[i]);
+  st = row_reduce<256, BITS == 8>(st, redf, 0, tid);
+  float f, s;
+  if constexpr (BITS == 8) {
+    f = 127.0f / (st + kEps);
+    s = st / 127.0f;
+  } else {
+    // mean as (fp64 of the fp32 sum) / K rounded once, K need not be a power of two
+    const float beta = (float)((double)st / (double)K);
+    f = kSqrt7 / (beta + kEps);
+    s = beta / kSqrt7;
+  }
+  constexpr float lo = BITS == 8 ? -128.0f : -8.0f;
+  constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
+  int qsum = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = tid + 256 * c;
+    if (ch >= nchunk) continue;
+    int q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float r = __builtin_rintf(v[8 * c + j] * f);
+      q[j] = (int)fminf(fmaxf(r, lo), hi);
+      qsum += q[j];
+    }
+    if constexpr (BITS == 8) {
+      uint32_t w0 = (q[0] & 0xff) | ((q[1] & 0xff) << 8) | ((q[2] & 0xff) << 16) | ((uint32_t)q[3] << 24);
+      uint32_t w1 = (q[4] & 0xff) | ((q[5] & 0xff) << 8) | ((q[6] & 0xff) << 16) | ((uint32_t)q[7] << 24);
+      *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(codes) + m * (int64_t)K + 8 * ch) = make_uint2(w0, w1);
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= (uint32_t)(q[j] & 0xf) << (8 * (j & 3) + 4 * (j >> 2));
+      reinterpret_cast<uint32_t*>(codes)[m * (int64_t)(K / 8) + ch] = w;
+    }
+  }
+  qsum = row_reduce_int<256>(qsum, redi, 0, tid);
+  if (tid == 0) {
+    scales[m] = s;
+    if (rowsum) rowsum[m] = qsum;
+  }
+}
+
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+hipError_t launch_fq(const void* x, int64_t M, int64_t ldx, void* codes, float* scales,
+                     int32_t* rowsum, float* y, hipStream_t s) {
+  using G = Geom<LOG2K>;
+  const int64_t blocks = (M + G::RPB - 1) / G::RPB;
+  hipLaunchKernelGGL((k_fwht_quant<LOG2K, BF16, BITS, HAD, OUT>), dim3((unsigned)blocks),
+                     dim3(G::THREADS), 0, s, x, M, ldx, codes, scales, rowsum, y);
+  return hipGetLastError();
+}
+
+template <int LOG2K>
+hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, int bits,
+                          void* codes, float* scales, int32_t* rowsum, hipStream_t s) {
+#define HBL_FQ(B16, BITS, HAD) \
+  return launch_fq<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, s)
+  if (bf16) {
+    if (had) { if (bits == 8) HBL_FQ(true, 8, true); else HBL_FQ(true, 4, true); }
+    else { if (bits == 8) HBL_FQ(true, 8, false); else HBL_FQ(true, 4, false); }
+  } else {
+    if (had) { if (bits == 8) HBL_FQ(false, 8, true); else HBL_FQ(false, 4, true); }
+    else { if (bits == 8) HBL_FQ(false, 8, false); else HBL_FQ(false, 4, false); }
+  }
+#undef HBL_FQ
+}
+
+int ilog2(int K) {
+  int l = 0;
+  while ((1 << l) < K) ++l;
+  return l;
+}
+
+}  // namespace
+
+hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx,
+                                 bool hadamard, int bits, void* codes, float* scales,
+                                 int32_t* rowsum, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const bool pow2 = (K & (K - 1)) == 0;
+  if (!pow2) {
+    // only reachable without the rotation (the ABI layer rejects it otherwise)
+    if (x_bf16) {
+      if (bits == 8) hipLaunchKernelGGL((k_quant_plain<true, 8>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
+      else hipLaunchKernelGGL((k_quant_plain<true, 4>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
+    } else {
+      if (bits == 8) hipLaunchKernelGGL((k_quant_plain<false, 8>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
+      else hipLaunchKernelGGL((k_quant_plain<false, 4>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
+    }
+    return hipGetLastError();
+  }
+  switch (ilog2(K)) {
+    case 4: return dispatch_quant<4>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 5: return dispatch_quant<5>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 6: return dispatch_quant<6>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 7: return dispatch_quant<7>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 8: return dispatch_quant<8>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 9: return dispatch_quant<9>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 10: return dispatch_quant<10>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 11: return dispatch_quant<11>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 12: return dispatch_quant<12>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 13: return dispatch_quant<13>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 14: return dispatch_quant<14>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, float* y,
+                               hipStream_t s) {
+  if (M == 0) return hipSuccess;
+#define HBL_HF(L)                                                                              \
+  case L:                                                                                      \
+    return x_bf16 ? launch_fq<L, true, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s) \
+                  : launch_fq<L, false, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s);
+  switch (ilog2(K)) {
+    HBL_HF(4) HBL_HF(5) HBL_HF(6) HBL_HF(7) HBL_HF(8) HBL_HF(9)
+    HBL_HF(10) HBL_HF(11) HBL_HF(12) HBL_HF(13) HBL_HF(14)
+    default: return hipErrorInvalidValue;
+  }
+#undef HBL_HF
+}
+
+}  // namespace hbl

@@ -1,0 +1,198 @@
+/*
+ * hbl.h -- C ABI of the H-BitLinear forward (BitNet v2) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (architecture write-up of "BitNet v2: Native 4-bit Activations
+ * with Hadamard Transformation for 1-bit LLMs", §3.4):
+ *   - weights are ternarised per tensor with the absmean quantiser
+ *     (§3.4 "Weight Quantization", Eq. 1-2);
+ *   - each token row of the layer input is rotated by the normalised
+ *     Sylvester-Hadamard matrix of its length n = 2^k
+ *     (§3.4 "The Hadamard Transformation", Eq. 3-6);
+ *   - the rotated row is quantised per token, INT8 absmax (Eq. 7) or INT4
+ *     absmean (Eq. 8);
+ *   - the layer output is Y = Q_w(W) . Q(X_r)  (§3.4 "H-BitLinear", Eq. 9),
+ *     evaluated as an integer matmul of the codes followed by one rescale.
+ *
+ * Orientation.  Tokens are rows: X is [M][K] row-major, W is [N][K]
+ * row-major (out-features by in-features), Y = Xq . Wq^T is [M][N].
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a device pointer unless stated otherwise.
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the default stream) and the call returns at once.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call enqueues nothing and returns an HBL_ERR_* code.
+ *     HBL_ERR_HIP reports a failed launch (detail in hbl_last_error()).
+ *     Faults inside a kernel surface at the caller's next synchronisation,
+ *     as with any HIP kernel.
+ *   - Device pointers must be 16-byte aligned.  Inputs are never written.
+ *   - Results are bitwise deterministic (no floating-point atomics).
+ *   - M == 0 is a valid no-op.
+ *
+ * Packed layouts (bit-exact contract):
+ *   ternary weights: uint32 [N][K/16].  Word w of row n holds k = 16w..16w+15;
+ *       weight j = 4s + b (s, b in 0..3) of the word sits in bits
+ *       [8b + 2s, 8b + 2s + 2) as c = q + 1 in {0, 1, 2} (3 is never written).
+ *   INT4 codes: uint32 [M][K/8].  Word w of row m holds k = 8w..8w+7;
+ *       code j = 4h + b (h in 0..1, b in 0..3) sits in bits [8b + 4h, +4) as a
+ *       two's-complement nibble.
+ *   INT8 codes: int8 [M][K], natural order.
+ *   scales: float [M], the per-token dequantisation factor gamma/127 (INT8)
+ *       or beta/sqrt(7) (INT4).
+ *   alpha: one float in device memory, the weight scale mean|W|.
+ */
+#ifndef HBL_H
+#define HBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define HBL_OK 0
+#define HBL_ERR_NULL 1      /* a required pointer is NULL */
+#define HBL_ERR_SHAPE 2     /* a size or leading dimension is out of range */
+#define HBL_ERR_ALIGN 3     /* a pointer or leading dimension is misaligned */
+#define HBL_ERR_MODE 4      /* unknown dtype, bits or flag value */
+#define HBL_ERR_WORKSPACE 5 /* workspace missing or too small */
+#define HBL_ERR_HIP 6       /* a HIP runtime call failed */
+
+/* element types of floating-point inputs */
+#define HBL_DTYPE_F32 0
+#define HBL_DTYPE_BF16 1
+
+/* flags of hbl_hadamard_quant / hbl_forward */
+#define HBL_HADAMARD 1 /* rotate each row before quantising (H-BitLinear);
+                          without it the row is quantised as is (BitLinear) */
+
+/* output types of hbl_ternary_gemm */
+#define HBL_OUT_BF16 0
+#define HBL_OUT_F32 1
+#define HBL_OUT_I32 2
+
+/* The epsilon of Eq. 1, 7 and 8.  The pages give it no value; 1e-5 is this
+ * library's reading, used for weights and activations alike. */
+#define HBL_EPS 1e-5f
+
+/* Largest row length accepted with HBL_HADAMARD (the FF width of the pages'
+ * 7B model, Table 8). */
+#define HBL_MAX_K 16384
+
+/* Library version, major*10000 + minor*100 + patch. */
+int hbl_version(void);
+
+/* Static English text for a status code. */
+const char* hbl_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* hbl_last_error(void);
+
+/* Number of compute units of the current device (0 if unknown). */
+int hbl_device_cu_count(void);
+
+/* ---------------------------------------------------------------------
+ * hbl_ternarize_weights -- absmean ternary weight quantiser
+ * (§3.4 "Weight Quantization", Eq. 1-2).
+ *
+ *   alpha = mean over all N*K entries of |W|   (one scalar per matrix)
+ *   q     = RoundClip(W / (alpha + eps), -1, 1), RoundClip(x, a, b) =
+ *           min(max(round(x), a), b), round = nearest, ties to even.
+ *
+ * w:        [N][K] row-major, element type w_dtype (HBL_DTYPE_F32/BF16).
+ * w_packed: out, uint32 [N][K/16] in the ternary layout above.
+ * alpha:    out, one float (device).
+ * ws:       device workspace of at least hbl_ternarize_workspace_size(N, K)
+ *           bytes (holds fp64 partial sums); contents are scratch.
+ * Shapes:   N >= 1, K >= 16, K % 16 == 0.
+ * The |W| sum is accumulated in fp64 in a fixed order (deterministic).
+ * ------------------------------------------------------------------- */
+size_t hbl_ternarize_workspace_size(int64_t N, int64_t K);
+int hbl_ternarize_weights(const void* w, int w_dtype, int64_t N, int64_t K,
+                          uint32_t* w_packed, float* alpha, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_hadamard_f32 -- the per-token rotation alone
+ * (§3.4 "The Hadamard Transformation", Eq. 3-6): y[m] = H_k x[m], with
+ * H_0 = (1), H_k = 2^{-1/2} [[H_{k-1}, H_{k-1}], [H_{k-1}, -H_{k-1}]]
+ * (natural Sylvester order), evaluated as k radix-2 butterfly stages in
+ * fp32 followed by one multiplication by 2^{-k/2}.
+ *
+ * x: [M][ldx] (first K columns used), x_dtype F32 or BF16.
+ * y: out, float [M][K] row-major.
+ * Shapes: K a power of two, 16 <= K <= HBL_MAX_K; ldx >= K and ldx times the
+ * element size a multiple of 16 bytes.
+ * ------------------------------------------------------------------- */
+int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K,
+                     int64_t ldx, float* y, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_hadamard_quant -- rotation fused with per-token quantisation
+ * (Eq. 3-6 followed by Eq. 7 or Eq. 8).
+ *
+ * With flags & HBL_HADAMARD each row is rotated first (x_r = H x); without
+ * it the row is quantised as is (the input of a plain BitLinear).
+ *   bits == 8: gamma = max_j |x_r|;  q = RoundClip(127/(gamma+eps) x_r,
+ *              -128, 127);  scale = gamma/127.
+ *   bits == 4: beta = mean_j |x_r|;  q = RoundClip(sqrt(7)/(beta+eps) x_r,
+ *              -8, 7);      scale = beta/sqrt(7).
+ * The factor Qmax/(stat+eps) is formed once per row with an IEEE divide and
+ * each code is rint(x_r * factor) clipped, all in fp32.
+ *
+ * codes:  out, int8 [M][K] (bits 8) or uint32 [M][K/8] (bits 4).
+ * scales: out, float [M].
+ * rowsum: out, int32 [M], sum of the row's codes (needed by
+ *         hbl_ternary_gemm); may be NULL.
+ * Shapes: with HBL_HADAMARD K is a power of two, 16 <= K <= HBL_MAX_K;
+ *         without it K % 64 == 0 and K <= HBL_MAX_K.  ldx as above.
+ * ------------------------------------------------------------------- */
+int hbl_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
+                       int64_t ldx, int flags, int bits, void* codes,
+                       float* scales, int32_t* rowsum, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_ternary_gemm -- integer matmul of activation codes with packed
+ * ternary weights and the rescale of Eq. 9:
+ *   acc[m][n] = sum_k q_x[m][k] * q_w[n][k]            (exact, int32)
+ *   out[m][n] = (scales[m] * alpha) * acc[m][n]        (fp32, then rounded
+ *                                                       to nearest-even bf16)
+ * codes/scales/rowsum: as written by hbl_hadamard_quant (rowsum required).
+ * w_packed, alpha:     as written by hbl_ternarize_weights.
+ * out_dtype: HBL_OUT_BF16 or HBL_OUT_F32 write the rescaled value;
+ *            HBL_OUT_I32 writes acc itself (for exact checks).
+ * out: [M][ldo] of out_dtype; ldo >= N, ldo % 4 == 0.
+ * Shapes: N >= 16, N % 16 == 0, K >= 64, K % 64 == 0.
+ * Token counts M <= 16 take a bandwidth-oriented kernel that streams the
+ * weights once; larger M take the matrix-core kernel.
+ * ------------------------------------------------------------------- */
+int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
+                     const int32_t* rowsum, const uint32_t* w_packed,
+                     const float* alpha, int64_t M, int64_t N, int64_t K,
+                     int out_dtype, void* out, int64_t ldo, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_forward -- the whole layer, Eq. 9 without the normalisation layer:
+ *   y = bf16( (scale_m * alpha) * sum_k q_x[m][k] q_w[n][k] ),
+ * q_x the codes of hbl_hadamard_quant(x, flags, bits).
+ * y: out, bf16 [M][ldy]; ldy >= N, ldy % 4 == 0.
+ * ws: device workspace of at least hbl_forward_workspace_size(M, K, bits)
+ *     bytes; it receives the codes, scales and row sums (scratch).
+ * Shapes: the union of the rules of hbl_hadamard_quant and
+ * hbl_ternary_gemm.  Two kernels are enqueued.
+ * ------------------------------------------------------------------- */
+size_t hbl_forward_workspace_size(int64_t M, int64_t K, int bits);
+int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                int64_t N, int flags, int bits, const uint32_t* w_packed,
+                const float* alpha, void* y, int64_t ldy, void* ws,
+                size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HBL_H */

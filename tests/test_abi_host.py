@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/hbl.h declares, and
+reject invalid arguments with the documented status code before anything is
+enqueued.  Pointers passed here are never dereferenced: every call below is
+rejected by validation, or is a documented no-op (M == 0).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hbl.h")
+
+
+@pytest.fixture(scope="module")
+def hbl():
+    import bit_quantization_amd
+    return bit_quantization_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hbl_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["hbl_ternarize_weights", "hbl_hadamard_quant", "hbl_ternary_gemm", "hbl_forward"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(hbl):
+    lib = ctypes.CDLL(hbl.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_version_and_status_strings(hbl):
+    lib = hbl.lib()
+    assert lib.hbl_version() >= 100
+    for s in range(7):
+        assert lib.hbl_status_string(s)
+    assert lib.hbl_status_string(99) == b"unknown status"
+
+
+# fake, 256-byte aligned addresses: validation must fail before any use
+A = 0x100000
+B = 0x200000
+C = 0x300000
+D = 0x400000
+E = 0x500000
+F = 0x600000
+
+
+def last(hbl):
+    return hbl.lib().hbl_last_error().decode()
+
+
+@pytest.mark.parametrize("K,flags,expect", [
+    (100, 1, 2),      # not a power of two with the rotation
+    (8, 1, 2),        # below 16
+    (32768, 1, 2),    # above the maximum
+    (96, 0, 2),       # not a multiple of 64 without the rotation
+    (32768, 0, 2),
+])
+def test_quant_shape_errors(hbl, K, flags, expect):
+    rc = hbl.lib().hbl_hadamard_quant(A, hbl.DTYPE_BF16, 4, K, K, flags, 8, B, C, D, None)
+    assert rc == expect
+    assert "K =" in last(hbl)
+
+
+def test_quant_mode_errors(hbl):
+    lib = hbl.lib()
+    assert lib.hbl_hadamard_quant(A, 7, 4, 256, 256, 1, 8, B, C, D, None) == hbl.ERR_MODE
+    assert lib.hbl_hadamard_quant(A, 1, 4, 256, 256, 1, 5, B, C, D, None) == hbl.ERR_MODE
+    assert lib.hbl_hadamard_quant(A, 1, 4, 256, 256, 4, 8, B, C, D, None) == hbl.ERR_MODE
+
+
+def test_quant_pointer_errors(hbl):
+    lib = hbl.lib()
+    assert lib.hbl_hadamard_quant(None, 1, 4, 256, 256, 1, 8, B, C, D, None) == hbl.ERR_NULL
+    assert lib.hbl_hadamard_quant(A, 1, 4, 256, 256, 1, 8, None, C, D, None) == hbl.ERR_NULL
+    assert lib.hbl_hadamard_quant(A + 8, 1, 4, 256, 256, 1, 8, B, C, D, None) == hbl.ERR_ALIGN
+    assert lib.hbl_hadamard_quant(A, 1, 4, 256, 260, 1, 8, B, C, D, None) == hbl.ERR_ALIGN
+    assert lib.hbl_hadamard_quant(A, 1, 4, 256, 128, 1, 8, B, C, D, None) == hbl.ERR_SHAPE
+    assert lib.hbl_hadamard_quant(A, 1, -1, 256, 256, 1, 8, B, C, D, None) == hbl.ERR_SHAPE
+
+
+def test_quant_zero_rows_is_a_noop(hbl):
+    assert hbl.lib().hbl_hadamard_quant(A, 1, 0, 256, 256, 1, 4, B, C, D, None) == hbl.OK
+
+
+def test_gemm_errors(hbl):
+    lib = hbl.lib()
+    g = lib.hbl_ternary_gemm
+    assert g(A, 8, B, C, D, E, 4, 40, 256, 0, F, 40, None) == hbl.ERR_SHAPE    # N % 16
+    assert g(A, 8, B, C, D, E, 4, 64, 100, 0, F, 64, None) == hbl.ERR_SHAPE    # K % 64
+    assert g(A, 8, B, C, D, E, 4, 64, 256, 0, F, 32, None) == hbl.ERR_SHAPE    # ldo < N
+    assert g(A, 8, B, C, D, E, 4, 64, 256, 0, F, 66, None) == hbl.ERR_ALIGN    # ldo % 4
+    assert g(A, 3, B, C, D, E, 4, 64, 256, 0, F, 64, None) == hbl.ERR_MODE
+    assert g(A, 8, B, C, D, E, 4, 64, 256, 9, F, 64, None) == hbl.ERR_MODE
+    assert g(A, 8, B, None, D, E, 4, 64, 256, 0, F, 64, None) == hbl.ERR_NULL  # rowsum required
+    assert g(A + 4, 8, B, C, D, E, 4, 64, 256, 0, F, 64, None) == hbl.ERR_ALIGN
+    assert g(A, 8, B, C, D, E, 0, 64, 256, 0, F, 64, None) == hbl.OK         # M = 0
+
+
+def test_forward_workspace(hbl):
+    lib = hbl.lib()
+    need = lib.hbl_forward_workspace_size(10, 256, 4)
+    assert need >= 10 * 128 + 2 * 40
+    assert need % 256 == 0
+    rc = lib.hbl_forward(A, 1, 10, 256, 256, 64, 1, 4, B, C, D, 64, E, need - 1, None)
+    assert rc == hbl.ERR_WORKSPACE
+    rc = lib.hbl_forward(A, 1, 10, 256, 256, 64, 1, 4, B, C, D, 64, None, need, None)
+    assert rc == hbl.ERR_WORKSPACE
+    assert lib.hbl_forward(A, 1, 10, 256, 256, 60, 1, 4, B, C, D, 64, E, need, None) == hbl.ERR_SHAPE
+
+
+def test_ternarize_errors(hbl):
+    lib = hbl.lib()
+    need = lib.hbl_ternarize_workspace_size(64, 256)
+    assert need >= 8
+    t = lib.hbl_ternarize_weights
+    assert t(A, 0, 64, 250, B, C, D, need, None) == hbl.ERR_SHAPE
+    assert t(A, 0, 0, 256, B, C, D, need, None) == hbl.ERR_SHAPE
+    assert t(A, 5, 64, 256, B, C, D, need, None) == hbl.ERR_MODE
+    assert t(None, 0, 64, 256, B, C, D, need, None) == hbl.ERR_NULL
+    assert t(A, 0, 64, 256, B, C, D, need - 1, None) == hbl.ERR_WORKSPACE
+    assert t(A + 2, 0, 64, 256, B, C, D, need, None) == hbl.ERR_ALIGN
+
+
+def test_hadamard_f32_errors(hbl):
+    lib = hbl.lib()
+    assert lib.hbl_hadamard_f32(A, 1, 4, 48, 48, B, None) == hbl.ERR_SHAPE
+    assert lib.hbl_hadamard_f32(A, 1, 4, 256, 256, None, None) == hbl.ERR_NULL
+    assert lib.hbl_hadamard_f32(A, 1, 0, 256, 256, B, None) == hbl.OK

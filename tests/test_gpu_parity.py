@@ -1,0 +1,274 @@
+"""GPU parity of every entry point against the CPU oracle, through the C ABI.
+
+Small cases span several tiles and ragged tails; the five workloads run at
+their full sizes in the launch configuration the benchmark times, compared
+on sampled token rows that the oracle recomputes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import (bf16_to_f64, check_codes, check_hadamard, check_output, check_scales,
+                         codes_to_numpy, to_device)
+
+pytestmark = pytest.mark.gpu
+
+ALL_LOG2K = list(range(4, 15))
+
+
+def rows_of(x: np.ndarray, rows) -> np.ndarray:
+    return np.ascontiguousarray(x[rows])
+
+
+def sample_rows(M: int, n: int = 24, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    r = set(rng.choice(M, min(n, M), replace=False).tolist())
+    r.update({0, M - 1})
+    return np.array(sorted(r))
+
+
+# ---------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("log2k", ALL_LOG2K)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hadamard_values(hbl, log2k, dtype):
+    K = 1 << log2k
+    M = 37
+    x = workloads.random_rows(100 + log2k, M, K, "t3", as_bf16=(dtype == "bf16"))
+    y = hbl.hadamard_f32(to_device(x)).cpu().numpy()
+    check_hadamard(y, oracle.hadamard(x), f"K={K} {dtype}")
+
+
+def test_hadamard_strided_rows(hbl):
+    K, M, ld = 1024, 19, 1024 + 64
+    big = workloads.random_rows(7, M, ld, "normal", as_bf16=True)
+    x_dev = to_device(big)[:, :K]
+    y = hbl.hadamard_f32(x_dev).cpu().numpy()
+    check_hadamard(y, oracle.hadamard(np.ascontiguousarray(big[:, :K])), "strided")
+
+
+def test_hadamard_twice_is_identity(hbl):
+    K, M = 4096, 8
+    x = workloads.random_rows(5, M, K, "normal", as_bf16=False)
+    y = hbl.hadamard_f32(to_device(x))
+    z = hbl.hadamard_f32(y).cpu().numpy()
+    assert np.abs(z - x).max() <= 1e-5 * np.abs(x).max()
+
+
+# ------------------------------------------------------------ quantisation
+
+def _quant_case(hbl, x, bits, had, what):
+    q, s, rs = hbl.hadamard_quant(to_device(x), bits, hadamard=had)
+    torch.cuda.synchronize()
+    oq, os_, ors, xr = oracle.quantize(x, bits, hadamard=had, want_xr=True)
+    K = x.shape[1]
+    gq = oracle.codes_int8(codes_to_numpy(q, bits), bits, K)
+    oq8 = oracle.codes_int8(oq, bits, K)
+    nbad = check_codes(gq, oq8, xr, bits, what)
+    check_scales(s.cpu().numpy(), os_, what)
+    grs = rs.cpu().numpy()
+    assert np.array_equal(grs, gq.astype(np.int64).sum(axis=1)), f"{what}: rowsum != sum of codes"
+    assert np.abs(grs.astype(np.int64) - ors).sum() <= nbad
+    return gq, nbad
+
+
+@pytest.mark.parametrize("log2k", ALL_LOG2K)
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quant_with_rotation(hbl, log2k, bits):
+    K = 1 << log2k
+    x = workloads.random_rows(200 + log2k, 37, K, "t3", as_bf16=True)
+    _quant_case(hbl, x, bits, True, f"K={K} INT{bits}")
+
+
+@pytest.mark.parametrize("K", [64, 192, 960, 4096, 16384])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_plain(hbl, K, bits, dtype):
+    x = workloads.random_rows(300 + K % 97, 21, K, "t3", as_bf16=(dtype == "bf16"))
+    _quant_case(hbl, x, bits, False, f"plain K={K} INT{bits} {dtype}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quant_degenerate_rows(hbl, bits):
+    K = 2048
+    rows = [np.zeros(K, np.float32),                      # all zero
+            np.full(K, 3.0, np.float32),                  # constant: rotates to a spike
+            np.eye(1, K, 17, dtype=np.float32)[0] * 50,   # spike: rotates to a flat row
+            np.full(K, 1e-30, np.float32),                # far below eps
+            (np.arange(K) % 7 - 3).astype(np.float32) * 6e4]
+    x = np.stack(rows)
+    gq, _ = _quant_case(hbl, x, bits, True, f"degenerate INT{bits}")
+    assert np.all(gq[0] == 0) and np.all(gq[3] == 0)
+
+
+# -------------------------------------------------------------- ternarise
+
+@pytest.mark.parametrize("N,K", [(256, 256), (64, 4096), (48, 272), (4096, 4096)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ternarize(hbl, N, K, dtype):
+    w = workloads.gaussian_weights(9, N + K, N, K)
+    if dtype == "bf16":
+        w = workloads.bf16_bits(w)
+    packed, alpha = hbl.ternarize_weights(to_device(w))
+    o_packed, o_alpha, _ = oracle.ternarize(w)
+    assert float(alpha.cpu()[0]) == float(o_alpha)
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), o_packed)
+
+
+# ----------------------------------------------------- integer matmul
+
+def _gemm_inputs(M, N, K, bits, seed):
+    x = workloads.random_rows(seed, M, K, "t3", as_bf16=True)
+    had = (K & (K - 1)) == 0
+    codes, scales, rowsum = oracle.quantize(x, bits, hadamard=had)
+    w = workloads.gaussian_weights(seed, 7, N, K)
+    packed, alpha, _ = oracle.ternarize(w)
+    return codes, scales, rowsum, packed, alpha
+
+
+def _dev_codes(codes, bits):
+    return torch.from_numpy(codes).cuda() if bits == 8 else torch.from_numpy(codes.view(np.int32)).cuda()
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 100, 300])
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (256, 256), (272, 1024)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_exact_on_oracle_codes(hbl, M, N, K, bits):
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 1000 + M + N + K)
+    acc = hbl.ternary_gemm(_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(),
+                           torch.from_numpy(rowsum).cuda(), torch.from_numpy(packed.view(np.int32)).cuda(),
+                           torch.tensor([alpha], dtype=torch.float32).cuda(), K, out_dtype=hbl.OUT_I32)
+    ref = oracle.gemm_i32(codes, bits, packed, K)
+    assert np.array_equal(acc.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("M", [5, 130])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_rescaled_outputs(hbl, M, bits):
+    N, K = 96, 512
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 77 + M)
+    args = (_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(), torch.from_numpy(rowsum).cuda(),
+            torch.from_numpy(packed.view(np.int32)).cuda(), torch.tensor([alpha], dtype=torch.float32).cuda(), K)
+    y32 = hbl.ternary_gemm(*args, out_dtype=hbl.OUT_F32).cpu().numpy().astype(np.float64)
+    y16 = bf16_to_f64(hbl.ternary_gemm(*args, out_dtype=hbl.OUT_BF16))
+    acc = oracle.gemm_i32(codes, bits, packed, K)
+    y64, _ = oracle.dequant_output(acc, scales, alpha)
+    # fp32: two roundings (scale*alpha, then the product); bf16: one more
+    assert np.all(np.abs(y32 - y64) <= 2.5e-7 * np.abs(y64))
+    assert np.all(np.abs(y16 - y64) <= (2.0 ** -8) * np.abs(y64))
+
+
+def test_gemm_strided_output(hbl):
+    M, N, K, bits = 40, 64, 256, 8
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 5)
+    out = torch.full((M, N + 32), -7, dtype=torch.int32, device="cuda")
+    hbl.ternary_gemm(_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(),
+                     torch.from_numpy(rowsum).cuda(), torch.from_numpy(packed.view(np.int32)).cuda(),
+                     torch.tensor([alpha], dtype=torch.float32).cuda(), K, out_dtype=hbl.OUT_I32,
+                     out=out[:, :N])
+    o = out.cpu().numpy()
+    assert np.array_equal(o[:, :N], oracle.gemm_i32(codes, bits, packed, K))
+    assert np.all(o[:, N:] == -7), "wrote outside the output view"
+
+
+# ---------------------------------------------------------- whole layer
+
+def test_forward_tiny_workload(hbl):
+    c = workloads.tiny()
+    packed, alpha = hbl.ternarize_weights(to_device(c["w"]))
+    y = hbl.forward(to_device(c["x"]), packed, alpha, c["bits"], hadamard=True)
+    o_packed, o_alpha, _ = oracle.ternarize(c["w"])
+    y64 = oracle.forward(c["x"], o_packed, o_alpha, c["bits"], hadamard=True)
+    check_output(bf16_to_f64(y), y64, "tiny")
+
+
+def test_forward_equals_the_two_steps(hbl):
+    M, K, N, bits = 70, 1024, 128, 4
+    x = to_device(workloads.random_rows(3, M, K, "t3"))
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(3, 3, N, K)))
+    y = hbl.forward(x, packed, alpha, bits)
+    q, s, rs = hbl.hadamard_quant(x, bits)
+    y2 = hbl.ternary_gemm(q, bits, s, rs, packed, alpha, K)
+    assert torch.equal(y, y2)
+
+
+def test_forward_deterministic(hbl):
+    M, K, N, bits = 300, 4096, 512, 8
+    x = to_device(workloads.random_rows(4, M, K, "t3"))
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(4, 4, N, K)))
+    a = hbl.forward(x, packed, alpha, bits)
+    b = hbl.forward(x, packed, alpha, bits)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_tokens(hbl):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(1, 1, 32, 256)))
+    assert hbl.forward(x, packed, alpha, 4).shape == (0, 32)
+
+
+# ------------------------------------------------- full-size workloads
+
+def _full_size_layer(hbl, x_np, w_np, bits, had, what, gemm_rows=8):
+    """GPU at full size; oracle on sampled rows.  Checks codes and scales on
+    the sampled rows, the integer matmul bit-exactly on the oracle's codes of
+    all rows (sampled outputs), and the bf16 layer output."""
+    M, K = x_np.shape
+    x = to_device(x_np)
+    packed, alpha = hbl.ternarize_weights(to_device(w_np))
+    o_packed, o_alpha, _ = oracle.ternarize(w_np)
+    assert float(alpha.cpu()[0]) == float(o_alpha), f"{what}: alpha"
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), o_packed), f"{what}: ternary codes"
+
+    rows = sample_rows(M)
+    xs = rows_of(x_np, rows)
+    q, s, rs = hbl.hadamard_quant(x, bits, hadamard=had)
+    oq, os_, ors, xr = oracle.quantize(xs, bits, hadamard=had, want_xr=True)
+    gq = oracle.codes_int8(codes_to_numpy(q, bits)[rows], bits, K)
+    check_codes(gq, oracle.codes_int8(oq, bits, K), xr, bits, what)
+    check_scales(s.cpu().numpy()[rows], os_, what)
+
+    # integer matmul on the oracle's codes of every row (the bench's launch shape)
+    all_q, all_s, all_rs = oracle.quantize(x_np, bits, hadamard=had)
+    acc = hbl.ternary_gemm(_dev_codes(all_q, bits), bits, torch.from_numpy(all_s).cuda(),
+                           torch.from_numpy(all_rs).cuda(), packed, alpha, K, out_dtype=hbl.OUT_I32)
+    gr = rows[np.linspace(0, len(rows) - 1, min(gemm_rows, len(rows))).astype(int)]
+    ref = oracle.gemm_i32(np.ascontiguousarray(all_q[gr]), bits, o_packed, K)
+    assert np.array_equal(acc.cpu().numpy()[gr], ref), f"{what}: integer matmul"
+    del acc
+
+    y = hbl.forward(x, packed, alpha, bits, hadamard=had)
+    y64 = oracle.forward(rows_of(x_np, gr), o_packed, o_alpha, bits, hadamard=had)
+    check_output(bf16_to_f64(y[torch.from_numpy(gr).cuda()]), y64, what)
+
+
+def test_full_wo_7b(hbl):
+    c = workloads.wo_7b()
+    _full_size_layer(hbl, c["x"], c["w"], c["bits"], True, "wo_7b")
+
+
+def test_full_wdown_7b(hbl):
+    c = workloads.wdown_7b()
+    _full_size_layer(hbl, c["x"], c["w"], c["bits"], True, "wdown_7b")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (16384, 4096)])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_full_decode(hbl, K, N, M):
+    x = workloads.decode_inputs(K, M)
+    w = workloads.decode_weights(K, N, 0)
+    _full_size_layer(hbl, x, w, 8, True, f"decode M={M} K={K}")
+
+
+@pytest.mark.parametrize("layer", ["q", "o", "up", "down"])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_full_block_7b(hbl, layer, bits):
+    names = [n for n, *_ in workloads.BLOCK_7B_LAYERS]
+    _, K, N, had = workloads.BLOCK_7B_LAYERS[names.index(layer)]
+    x = workloads.block_input(workloads.BLOCK_7B_INPUT_OF[layer])
+    w = workloads.block_weights(layer)
+    _full_size_layer(hbl, x, w, bits, had, f"block_7b {layer} INT{bits}")
