@@ -236,10 +236,12 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
       const int64_t kw = (s0 + 4 * b) * 16 + 4 * g;
-      if (s0 + 4 * b >= steps || kw >= KW) continue;
+      // Skip only whole steps (a wave-uniform test): an MFMA always runs on
+      // all 64 lanes, so lanes past the end of K feed zeros instead.
+      if (s0 + 4 * b >= steps) continue;
       // activation codes for k = 16*kw .. 16*kw + 63 of token fr
       uint32_t x[16];
-      if (mlive) {
+      if (mlive && kw < KW) {
         if constexpr (BITS == 8) {
           const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + fr * K + 16 * kw);
 #pragma unroll
