@@ -11,7 +11,9 @@ matrix-core matmul), its average duration measured with HIP events over
 back-to-back launches on the stream it runs on; ``cpu_baseline`` is the CPU
 oracle timed on a bounded sample of rows of the same workload.
 
-Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b.
+Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b, and
+copy (a plain device copy of known size, to calibrate the HBM traffic
+counters).
 """
 from __future__ import annotations
 
@@ -37,7 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wo_7b",
-                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b"])
+                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="copy: bytes moved per launch (calibrates the HBM traffic counters)")
     ap.add_argument("--decode-m", type=int, default=1)
     ap.add_argument("--decode-k", type=int, default=16384)
     ap.add_argument("--decode-mats", type=int, default=0,
@@ -222,6 +226,16 @@ def main():
     import bit_quantization_amd as hbl
     import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.workload == "copy":
+        # a plain device-to-device copy of known size, for counter calibration
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        t = time_stream(lambda: dst.copy_(src), max(3, args.steps))
+        print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n, "avg_kernel_us": t * 1e6,
+                          "achieved_gbs": 2 * n / t / 1e9}), flush=True)
+        return
 
     if args.workload == "decode":
         res = run_decode(args, hbl, torch)

@@ -3,14 +3,14 @@
 //   acc[m][n] = sum_k q_x[m][k] q_w[n][k],  out = (scale_m * alpha) * acc.
 //
 // Two kernels:
-//   k_gemm -- large token counts.  Block tile BM x BN, K staged through LDS
-//     128 bytes at a time, double-buffered, 4 waves in a 2 x 2 grid, each
-//     wave a (BM/2) x (BN/2) tile of 16x16x64 int8 MFMAs with int32
-//     accumulators.  Activation codes are widened to int8 and weights are
-//     decoded from two bits to the unsigned byte c = q + 1 in {0, 1, 2} on
-//     their way from global memory into LDS.  The MFMA therefore sums
-//     q_x * c; the epilogue subtracts sum_k q_x (the token's row sum of
-//     codes) to obtain sum_k q_x * q_w exactly.
+//   k_gemm -- large token counts.  Block tile BM x BN, 4 waves, each wave a
+//     128 x 64 (or 64 x 128) tile of 16x16x64 int8 MFMAs with int32
+//     accumulators; two blocks per CU.  Codes and weights are staged to LDS
+//     as they are stored (packed) and widened by each wave after its LDS
+//     read.  Weights are decoded from two bits to the unsigned byte
+//     c = q + 1 in {0, 1, 2}, so the MFMA sums q_x * c; the epilogue
+//     subtracts sum_k q_x (the token's row sum of codes) to obtain
+//     sum_k q_x * q_w exactly.
 //   k_gemv -- token counts up to 16 (decode).  Bandwidth-bound: each block
 //     owns 16 output features and streams their packed weights once with
 //     16-byte loads; the 4 waves of a block split K and are reduced through
@@ -65,24 +65,49 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, v4i a, int32_t R,
   }
 }
 
-constexpr int BK = 128;           // k per LDS stage
-constexpr int LROW = BK + 16;     // padded LDS row stride in bytes
-
-template <int BITS, int OUT, int BM, int BN>
-__global__ void __launch_bounds__(256, 1)
+// An LDS stage holds S = 2 MFMA k-steps (128 codes: 64 bytes per row for
+// INT4, 128 for INT8).  Lane group g = lane/16 of
+// a fragment covers the S consecutive weight words S*g .. S*g + S-1 of the
+// stage: one LDS read per lane brings the weights of all S steps, and step s
+// uses word S*g + s with the matching 16 codes.  Widening:
+//   weights:  word -> {w & m, w>>2 & m, w>>4 & m, w>>6 & m}, m = 0x03030303,
+//             the bytes c = q_w + 1;
+//   INT4:     word -> {(w << 4) & 0xf0f0f0f0, w & 0xf0f0f0f0}, the bytes
+//             16 q_x (a nibble in the high half of a byte is 16 times its
+//             value as a signed byte), so the sums carry a factor 16;
+//   INT8:     bytes as stored.
+// Epilogue: sum q_x q_w = sum q_x c / (16 for INT4) - rowsum.
+//
+// LDS rows are not padded; 16-byte units are XOR-swizzled by row so that
+// the 16-lane column reads of the fragments and the row-contiguous staging
+// writes both touch distinct banks (64 banks of 4 bytes):
+//   INT8 codes row (128 B):    unit u of row r at u ^ ((r >> 1) & 7)
+//   INT4 codes row (64 B):     unit u of row r at u ^ ((r >> 2) & 3)
+//   weights row (32 B):        unit u of row r at u ^ ((r >> 3) & 1)
+template <int BITS, int OUT, int BM, int BN, int WGM, int WGN, int MINB>
+__global__ void __launch_bounds__(64 * WGM * WGN, MINB)
 k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
        const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
        const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo, int tilesM, int tilesN) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int S = 2;                         // MFMA k-steps per stage
+  constexpr int BKC = 64 * S;                  // codes per row per stage
+  constexpr int AROW = BKC * BITS / 8;         // code bytes per row per stage
+  constexpr int BROW = 16 * S;                 // weight bytes per row per stage
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int PA = BITS == 8 ? BM / 32 : BM / 64;  // 16-byte A loads per thread
-  constexpr int PB = BN / 128;                        // 16-byte B loads per thread
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * LROW];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * LROW];
+  constexpr int BCPR = BROW / 16;              // weight chunks per row
+  constexpr int PA = BM * AROW / 16 / NT;      // 16-byte staging chunks per thread
+  constexpr int PB = BN * BROW / 16 / NT;
+  static_assert(PA * NT * 16 == BM * AROW && PB * NT * 16 == BN * BROW, "staging must divide evenly");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "fragment rows");
+  constexpr int SPR = BITS == 4 ? 2 : 1;       // MFMA steps per 16-byte code read
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AROW];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * BROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
 
   // Tile order: consecutive block ids go to different XCDs, so give each
   // XCD a contiguous range of tiles, then walk M-groups of 8 tiles.
@@ -97,64 +122,65 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
   const int tn = (L % per_group) / gsz;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int64_t KW = K / 16;  // packed weight words per row
-  uint4 ra[PA], rb[PB];
+  const int64_t arow_bytes = BITS == 4 ? K / 2 : K;  // global code row stride
+  const int64_t brow_bytes = K / 4;                  // global weight row stride
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(codes);
+  const uint8_t* B8 = reinterpret_cast<const uint8_t*>(wp);
 
-  auto gload = [&](int kt) {
+  // LDS byte offsets (swizzled) of 16-byte unit u of row r
+  auto aoff = [](int r, int u) {
+    if constexpr (BITS == 8) return r * AROW + 16 * (u ^ ((r >> 1) & 7));
+    else return r * AROW + 16 * (u ^ ((r >> 2) & 3));
+  };
+  auto boff = [](int r, int u) { return r * BROW + 16 * (u ^ ((r >> 3) & 1)); };
+
+  // Staging: chunk p of this thread is row r0 + RPP*p of the tile, 16-byte
+  // unit col.  Every load is issued at a valid address (rows past the end
+  // re-read the last row, k past the end re-reads offset 0) and zeroed when
+  // out of range, so the stage body has no branches.  RPP is a multiple of
+  // 16, so the swizzle of a chunk's row does not depend on p and every LDS
+  // offset is one base plus a constant.
+  constexpr int ACPR = AROW / 16;                    // code chunks per row
+  constexpr int A_RPP = NT / ACPR, B_RPP = NT / BCPR;  // rows per staging pass
+  static_assert(A_RPP % 16 == 0 && B_RPP % 16 == 0, "swizzle period");
+  const int ar0 = tid / ACPR, acol = tid % ACPR;
+  const int br0 = tid / BCPR, bcol = tid % BCPR;
+  const int la0 = aoff(ar0, acol), lb0 = boff(br0, bcol);
+  // The staging loads of a stage are issued in two halves, each written to
+  // LDS halfway through the compute, to halve the registers they hold.
+  static_assert(PA % 2 == 0 && (PB % 2 == 0 || PB == 1), "halves");
+  constexpr int HA = PA / 2, HB = PB >= 2 ? PB / 2 : PB;
+  uint4 ra[HA], rb[HB];
+  auto gload = [&](int kt, int part) {
+    const int64_t ka = (int64_t)kt * AROW + 16 * acol, kb = (int64_t)kt * BROW + 16 * bcol;
+    const bool oka = ka < arow_bytes, okb = kb < brow_bytes;
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      if constexpr (BITS == 8) {
-        const int r = tid / 8 + 32 * p, c = tid % 8;
-        const int64_t k = (int64_t)kt * BK + 16 * c;
-        ra[p] = (m0 + r < M && k < K)
-                    ? *reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (m0 + r) * K + k)
-                    : make_uint4(0, 0, 0, 0);
-      } else {
-        const int r = tid / 4 + 64 * p, c = tid % 4;
-        const int64_t k = (int64_t)kt * BK + 32 * c;
-        ra[p] = (m0 + r < M && k < K)
-                    ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(codes) + (m0 + r) * (K / 2) + k / 2)
-                    : make_uint4(0, 0, 0, 0);
-      }
+    for (int q = 0; q < HA; ++q) {
+      const int64_t row = m0 + ar0 + A_RPP * (part * HA + q);
+      const bool ok = oka && row < M;
+      const uint4 v = *reinterpret_cast<const uint4*>(A8 + (row < M ? row : M - 1) * arow_bytes +
+                                                      (oka ? ka : 16 * acol));
+      ra[q] = ok ? v : make_uint4(0, 0, 0, 0);
     }
+    if (PB >= 2 || part == 0) {
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int r = tid / 2 + 128 * p, c = tid % 2;
-      const int64_t kw = (int64_t)kt * (BK / 16) + 4 * c;
-      rb[p] = (n0 + r < N && kw < KW) ? *reinterpret_cast<const uint4*>(wp + (n0 + r) * KW + kw)
-                                      : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < HB; ++q) {
+        const int64_t row = n0 + br0 + B_RPP * (part * HB + q);
+        const bool ok = okb && row < N;
+        const uint4 v = *reinterpret_cast<const uint4*>(B8 + (row < N ? row : N - 1) * brow_bytes +
+                                                        (okb ? kb : 16 * bcol));
+        rb[q] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int part) {
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      if constexpr (BITS == 8) {
-        const int r = tid / 8 + 32 * p, c = tid % 8;
-        *reinterpret_cast<uint4*>(&As[buf][r * LROW + 16 * c]) = ra[p];
-      } else {
-        const int r = tid / 4 + 64 * p, c = tid % 4;
-        const uint32_t w[4] = {ra[p].x, ra[p].y, ra[p].z, ra[p].w};
-        uint32_t d[8];
+    for (int q = 0; q < HA; ++q)
+      *reinterpret_cast<uint4*>(&As[buf][la0 + A_RPP * AROW * (part * HA + q)]) = ra[q];
+    if (PB >= 2 || part == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          d[2 * i] = sext_nibbles(w[i] & 0x0f0f0f0fu);
-          d[2 * i + 1] = sext_nibbles((w[i] >> 4) & 0x0f0f0f0fu);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&As[buf][r * LROW + 32 * c]);
-        dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-        dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int r = tid / 2 + 128 * p, c = tid % 2;
-      const uint32_t w[4] = {rb[p].x, rb[p].y, rb[p].z, rb[p].w};
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][r * LROW + 64 * c]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[i] = make_uint4(w[i] & 0x03030303u, (w[i] >> 2) & 0x03030303u, (w[i] >> 4) & 0x03030303u,
-                            (w[i] >> 6) & 0x03030303u);
+      for (int q = 0; q < HB; ++q)
+        *reinterpret_cast<uint4*>(&Bs[buf][lb0 + B_RPP * BROW * (part * HB + q)]) = rb[q];
     }
   };
 
@@ -164,29 +190,71 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  const int nk = (int)((K + BK - 1) / BK);
-  gload(0);
-  sstore(0);
+  const int nk = (int)((K + BKC - 1) / BKC);
+  const int fr = lane % 16, g = lane / 16;
+  // Fragment rows are wm*WM + 16*j + fr (codes) and wn*WN + 16*i + fr
+  // (weights): the swizzle depends on fr only, and fragment j (i) sits at a
+  // constant offset from fragment 0.
+  // codes of lane group g: unit g (INT4: both steps) or units 2g, 2g+1
+  // (INT8: one per step); weights: 8 bytes, half (g & 1) of unit g >> 1
+  const int abase0 = BITS == 4 ? aoff(wm * WM + fr, g) : aoff(wm * WM + fr, 2 * g);
+  const int abase1 = BITS == 4 ? abase0 : aoff(wm * WM + fr, 2 * g + 1);
+  const int bbase = boff(wn * WN + fr, g >> 1) + 8 * (g & 1);
+  constexpr int AFRAG = 16 * AROW, BFRAG = 16 * BROW;  // bytes between fragments
+
+  gload(0, 0);
+  sstore(0, 0);
+  gload(0, 1);
+  sstore(0, 1);
   __syncthreads();
-  const int fr = lane % 16, fk = 16 * (lane / 16);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* Ab = As[cur];
+    const uint8_t* Bb = Bs[cur];
+    const int kn = kt + 1 < nk ? kt + 1 : kt;  // the last stage re-reads itself into the spare buffer
+    gload(kn, 0);
+    uint32_t bw[FN][S];
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 64) {
-      v4i bf[FN], af[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        bf[i] = *reinterpret_cast<const v4i*>(&Bs[cur][(wn * WN + 16 * i + fr) * LROW + ks + fk]);
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        af[j] = *reinterpret_cast<const v4i*>(&As[cur][(wm * WM + 16 * j + fr) * LROW + ks + fk]);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = mfma16x16x64(bf[i], af[j], acc[i][j]);
+    for (int i = 0; i < FN; ++i) {
+      const uint2 u = *reinterpret_cast<const uint2*>(Bb + bbase + BFRAG * i);
+      bw[i][0] = u.x;
+      bw[i][1] = u.y;
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+#pragma unroll
+    for (int h = 0; h < S / SPR; ++h) {
+      uint4 ar[FM];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) ar[j] = *reinterpret_cast<const uint4*>(Ab + (h ? abase1 : abase0) + AFRAG * j);
+#pragma unroll
+      for (int t = 0; t < SPR; ++t) {
+        const int s = h * SPR + t;
+        v4i bf[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const uint32_t w = bw[i][s];
+          bf[i] = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                      (int)((w >> 6) & 0x03030303u)};
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          v4i af;
+          if constexpr (BITS == 4) {
+            const uint32_t x0 = t == 0 ? ar[j].x : ar[j].z, x1 = t == 0 ? ar[j].y : ar[j].w;
+            af = v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
+                     (int)(x1 & 0xf0f0f0f0u)};
+          } else {
+            af = v4i{(int)ar[j].x, (int)ar[j].y, (int)ar[j].z, (int)ar[j].w};
+          }
+#pragma unroll
+          for (int i = 0; i < FN; ++i) acc[i][j] = mfma16x16x64(bf[i], af, acc[i][j]);
+        }
+        if (s == S / 2 - 1) {
+          sstore(cur ^ 1, 0);
+          gload(kn, 1);
+        }
+      }
+    }
+    sstore(cur ^ 1, 1);
     __syncthreads();
   }
 
@@ -199,8 +267,11 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
     const float sc = scales[m] * al;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const int64_t n = n0 + wn * WN + 16 * i + 4 * (lane / 16);
-      if (n < N) store4<OUT>(out, m * ldo + n, acc[i][j], R, sc);
+      const int64_t n = n0 + wn * WN + 16 * i + 4 * g;
+      if (n >= N) continue;
+      v4i a = acc[i][j];
+      if constexpr (BITS == 4) a = a >> 4;  // exact: every product carries a factor 16
+      store4<OUT>(out, m * ldo + n, a, R, sc);
     }
   }
 }
@@ -291,21 +362,21 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
 template <int BITS, int OUT>
 hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t* rowsum,
                            const uint32_t* wp, const float* alpha, int64_t M, int64_t N, int64_t K,
-                           void* out, int64_t ldo, int cu_count, hipStream_t s) {
+                           void* out, int64_t ldo, int /*cu_count*/, hipStream_t s) {
   if (M <= kGemvMaxM) {
     hipLaunchKernelGGL((k_gemv<BITS, OUT>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales,
                        rowsum, wp, alpha, (int)M, N, K, out, ldo);
     return hipGetLastError();
   }
-  // Large tiles when they alone fill the chip; otherwise 128 x 128.
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= cu_count) {
-    const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
-    hipLaunchKernelGGL((k_gemm<BITS, OUT, 256, 256>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
+  // 128 x 256 tiles (4 waves of 128 x 64) when M is the smaller side,
+  // 256 x 128 otherwise; two blocks share a CU.
+  if (M <= N) {
+    const int tm = (int)((M + 127) / 128), tn = (int)((N + 255) / 256);
+    hipLaunchKernelGGL((k_gemm<BITS, OUT, 128, 256, 1, 4, 2>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
                        scales, rowsum, wp, alpha, M, N, K, out, ldo, tm, tn);
   } else {
-    const int tm = (int)((M + 127) / 128), tn = (int)((N + 127) / 128);
-    hipLaunchKernelGGL((k_gemm<BITS, OUT, 128, 128>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
+    const int tm = (int)((M + 255) / 256), tn = (int)((N + 127) / 128);
+    hipLaunchKernelGGL((k_gemm<BITS, OUT, 256, 128, 2, 2, 2>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
                        scales, rowsum, wp, alpha, M, N, K, out, ldo, tm, tn);
   }
   return hipGetLastError();
