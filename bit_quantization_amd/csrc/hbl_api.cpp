@@ -163,7 +163,7 @@ int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K, int64_t l
   if (rc) return rc;
   if (M > 0 && !y) return fail(HBL_ERR_NULL, "y is NULL");
   if (!aligned16(y)) return fail(HBL_ERR_ALIGN, "y is not 16-byte aligned");
-  hipError_t e = hbl::launch_hadamard_f32(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, y,
+  hipError_t e = hbl::launch_hadamard_f32(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, y, cu_count_cached(),
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hadamard launch");
   return HBL_OK;
@@ -181,7 +181,7 @@ int hbl_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t
     return fail(HBL_ERR_ALIGN, "codes must be 16-byte aligned, scales and rowsum 4-byte aligned");
   hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
                                             (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum,
-                                            static_cast<hipStream_t>(stream));
+                                            cu_count_cached(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantise launch");
   return HBL_OK;
 }
@@ -236,7 +236,8 @@ int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, i
   int32_t* rowsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scales) + round256(sizeof(float) * (size_t)M));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
-                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum, s);
+                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum,
+                                            cu_count_cached(), s);
   if (e != hipSuccess) return hip_fail(e, "quantise launch");
   e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy,
                                cu_count_cached(), s);

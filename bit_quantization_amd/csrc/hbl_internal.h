@@ -8,12 +8,13 @@ namespace hbl {
 
 // Launchers.  Each validates nothing (the C-ABI layer has done that) and
 // returns the hipError_t of the launch.
+// cu_count: compute units of the device (sizes persistent grids).
 hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K,
                                  int64_t ldx, bool hadamard, int bits,
                                  void* codes, float* scales, int32_t* rowsum,
-                                 hipStream_t s);
+                                 int cu_count, hipStream_t s);
 hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K,
-                               int64_t ldx, float* y, hipStream_t s);
+                               int64_t ldx, float* y, int cu_count, hipStream_t s);
 hipError_t launch_ternarize(const void* w, bool w_bf16, int64_t N, int64_t K,
                             uint32_t* packed, float* alpha, double* partials,
                             int n_partials, hipStream_t s);

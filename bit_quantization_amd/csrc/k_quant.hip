@@ -36,6 +36,8 @@ namespace hbl {
 namespace {
 
 constexpr float kEps = 1e-5f;
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 // (float)sqrt(7): the INT4 clipping constant of Eq. 8.
 constexpr float kSqrt7 = 2.6457513110645907f;
 
@@ -280,6 +282,350 @@ k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of K = 2^k >= 1024 elements: 64 elements per thread, T = K/64 threads
+// per row, 256 threads per block (256/T rows), persistent over row groups.
+//
+// The k butterfly stages are applied in three register passes; between
+// passes the row goes through LDS, always as 16-byte groups of 4 consecutive
+// elements (element bits 0-1 stay in registers as passengers):
+//   pass 1: registers hold element bits 0-5 (64 contiguous elements, loaded
+//           with eight 16-byte loads); 6 stages;
+//   pass 2: registers hold bits 6-9 (and 0-1); thread index = bits 2-5 and
+//           10..k-1; 4 stages;
+//   pass 3: registers hold bits 10..k-1 (a3 = k-10 of them), the low ex =
+//           4-a3 bits of 2-5 and bits 0-1; thread index = the other bits of
+//           2-5 and bits 6-9; a3 stages (absent when k = 10).
+// LDS holds the row in fp32 with 16-byte unit u stored at u ^ ((u >> 4) &
+// 15): the unit-wise writes of pass 1 and the reads and writes of passes 2
+// and 3 then each touch 16 distinct bank groups per 16 lanes.
+// In the last layout each thread quantises groups of 4 consecutive elements
+// (the 1/sqrt(K) scale is folded into the per-row factor), the packed codes
+// go back through LDS in natural order, and each thread stores contiguous
+// 16-byte units.  The next row group's input is loaded while the current
+// one is transformed.
+template <int LOG2K>
+struct G64 {
+  static constexpr int K = 1 << LOG2K;
+  static constexpr int T = K / 64;             // threads per row
+  static constexpr int RPB = 256 / T;          // rows per block
+  static constexpr int A3 = LOG2K - 10;        // active bits of pass 3
+  static constexpr int EX = 4 - A3;            // low bits of 2-5 kept in registers in pass 3
+};
+
+__device__ __forceinline__ int swz16(int e) {  // float index -> swizzled float index
+  const int u = e >> 2;
+  return ((u ^ ((u >> 4) & 15)) << 2) | (e & 3);
+}
+
+// With bf16 input, pass 1 (the 64-point transforms of the contiguous
+// 64-element chunks) runs on the matrix cores instead: per wave, Y = H_64 X
+// for X the 64 x 64 matrix of its 64 chunks, as 16 v_mfma_f32_32x32x16_bf16
+// (2 x 2 output tiles of 32 x 32, 4 k-steps of 16).  The bf16 inputs and the
+// +-1 entries are exact in bf16 and every product is exact; the sums are
+// accumulated in fp32.  The chunks are loaded straight into the operand
+// layout (lane l holds 8 consecutive elements of chunk l % 32 of its column
+// group), and the result is written to LDS as groups of 4 consecutive
+// elements, in the same swizzled layout as the register path.
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+__global__ void __launch_bounds__(256, 2)
+k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
+               void* __restrict__ codes, float* __restrict__ scales,
+               int32_t* __restrict__ rowsum, float* __restrict__ yout) {
+  using G = G64<LOG2K>;
+  constexpr int K = G::K, T = G::T, RPB = G::RPB, A3 = G::A3, EX = G::EX;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int NL = BF16 ? 8 : 16;  // 16-byte loads per thread
+  constexpr bool MFMA1 = BF16 && HAD;
+  __shared__ __attribute__((aligned(16))) float lds[RPB * K];
+  __shared__ float redf[RPB * (T > 64 ? T / 64 : 1)];
+  __shared__ int redi[RPB * (T > 64 ? T / 64 : 1)];
+
+  const int row = threadIdx.x / T;
+  const int t = threadIdx.x % T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* L = lds + row * K;
+  const int64_t ngroups = (M + RPB - 1) / RPB;
+
+  // Chunk (64 contiguous elements) of the block held by this lane in the
+  // matrix-core pass, for column group cg: block chunk 64*wave + 32*cg + lane%32.
+  auto mchunk = [&](int cg) { return 64 * wave + 32 * cg + (lane & 31); };
+
+  // H_64 operands A(rb, s)[i][kk] = H[32*rb + i][16*s + kk], i = lane % 32,
+  // kk = 8*(lane/32) + p, as bf16 +-1.  Since i < 32 and kk < 16,
+  // A(rb, s) = P(s & 1) * (-1)^(rb * (s >> 1)) with
+  // P(0)[i][kk] = (-1)^popcount(i & kk) and P(1) = P(0) * (-1)^(bit 4 of i):
+  // four distinct operands, hP[s & 1][rb * (s >> 1)].
+  v8bf hP[2][2];
+  if constexpr (MFMA1) {
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd)
+#pragma unroll
+      for (int neg = 0; neg < 2; ++neg) {
+        uint32_t w[4];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          uint32_t h2 = 0;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int i = lane & 31, kk = 8 * (lane >> 5) + 2 * pp + half;
+            const int par = (__popc(i & kk) + odd * ((i >> 4) & 1) + neg) & 1;
+            h2 |= (par ? 0xbf80u : 0x3f80u) << (16 * half);
+          }
+          w[pp] = h2;
+        }
+        hP[odd][neg] = __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+  }
+
+  uint4 raw[NL];
+  auto load_rows = [&](int64_t grp) {
+    if constexpr (MFMA1) {
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const int bc = mchunk(cg), r = bc / T, tc = bc % T;
+        const int64_t m = grp * RPB + r;
+        const bool live = grp < ngroups && m < M;
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + (live ? m : 0) * ldx * ESZ +
+                                                          ((int64_t)tc * 64 + 8 * (lane >> 5)) * ESZ);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) raw[4 * cg + st] = live ? src[2 * st] : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int64_t m = grp * RPB + row;
+      const bool live = grp < ngroups && m < M;
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) +
+                                                        (live ? m : 0) * ldx * ESZ + (int64_t)t * 64 * ESZ);
+#pragma unroll
+      for (int q = 0; q < NL; ++q) raw[q] = live ? src[q] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  int64_t grp = blockIdx.x;
+  load_rows(grp);
+  for (; grp < ngroups; grp += gridDim.x) {
+    const int64_t m = grp * RPB + row;
+    const bool live = m < M;
+    float v[64];
+    if constexpr (MFMA1) {
+      // pass 1 on the matrix cores, result to LDS
+      v16f acc[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) acc[rb][cg] = v16f{};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+          const v8bf bx = __builtin_bit_cast(v8bf, raw[4 * cg + st]);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hP[st & 1][rb * (st >> 1)], bx, acc[rb][cg], 0, 0, 0);
+        }
+      load_rows(grp + gridDim.x);  // prefetch the next row group
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const int bc = mchunk(cg), r = bc / T, tc = bc % T;
+        float* Lr = lds + r * K;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            // rows 32*rb + 8*blk + 4*(lane/32) + 0..3 of chunk tc
+            const int e = tc * 64 + 32 * rb + 8 * blk + 4 * (lane >> 5);
+            const v16f& a = acc[rb][cg];
+            *reinterpret_cast<float4*>(Lr + swz16(e)) = make_float4(a[4 * blk], a[4 * blk + 1], a[4 * blk + 2], a[4 * blk + 3]);
+          }
+      }
+      __syncthreads();
+    } else {
+      if constexpr (BF16) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = bf16lo(w[i]);
+            v[8 * q + 2 * i + 1] = bf16hi(w[i]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          v[4 * q] = __uint_as_float(raw[q].x); v[4 * q + 1] = __uint_as_float(raw[q].y);
+          v[4 * q + 2] = __uint_as_float(raw[q].z); v[4 * q + 3] = __uint_as_float(raw[q].w);
+        }
+      }
+      load_rows(grp + gridDim.x);  // prefetch the next row group
+      if constexpr (HAD) {
+        butterflies<64, 0, 6>(v);
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          *reinterpret_cast<float4*>(L + swz16((t << 6) | (4 * q))) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        __syncthreads();
+      }
+    }
+
+    // layout of the last pass: register group g of 4 -> first element
+    auto last_e = [&](int gidx) {
+      if constexpr (A3 == 0) {  // pass 2 layout: j = gidx
+        return ((t >> 4) << 10) | (gidx << 6) | ((t & 15) << 2);
+      } else {
+        const int j3 = gidx >> EX, xx = gidx & ((1 << EX) - 1);
+        const int lo = t & ((1 << A3) - 1), mid = t >> A3;
+        return (j3 << 10) | (mid << 6) | (lo << (2 + EX)) | (xx << 2);
+      }
+    };
+
+    if constexpr (HAD) {
+      // pass 2
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 a = *reinterpret_cast<const float4*>(L + swz16(((t >> 4) << 10) | (j << 6) | ((t & 15) << 2)));
+        v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+      }
+      butterflies<64, 2, 6>(v);
+      if constexpr (A3 > 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          *reinterpret_cast<float4*>(L + swz16(((t >> 4) << 10) | (j << 6) | ((t & 15) << 2))) =
+              make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+        __syncthreads();
+        // pass 3
+#pragma unroll
+        for (int gi = 0; gi < 16; ++gi) {
+          const float4 a = *reinterpret_cast<const float4*>(L + swz16(last_e(gi)));
+          v[4 * gi] = a.x; v[4 * gi + 1] = a.y; v[4 * gi + 2] = a.z; v[4 * gi + 3] = a.w;
+        }
+        butterflies<64, 6 - A3, 6>(v);
+      }
+    }
+
+    // normalisation 2^{-k/2} (or fl(1/sqrt(K)) for odd k)
+    constexpr float scale = (LOG2K % 2 == 0) ? (float)(1.0 / (double)(1 << (LOG2K / 2))) : 0.0f;
+    const float c = HAD ? ((LOG2K % 2 == 0) ? scale : (float)(1.0 / __builtin_sqrt((double)K))) : 1.0f;
+
+    if constexpr (OUT == 1) {
+      // rotated values in natural order through LDS, then contiguous stores
+      __syncthreads();
+#pragma unroll
+      for (int gi = 0; gi < 16; ++gi)
+        *reinterpret_cast<float4*>(L + swz16(last_e(gi))) =
+            make_float4(v[4 * gi] * c, v[4 * gi + 1] * c, v[4 * gi + 2] * c, v[4 * gi + 3] * c);
+      __syncthreads();
+      if (live) {
+        float* yr = yout + m * (int64_t)K;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int u = t + T * q;  // 16-byte unit of the row
+          *reinterpret_cast<float4*>(yr + 4 * u) = *reinterpret_cast<const float4*>(L + swz16(4 * u));
+        }
+      }
+      __syncthreads();
+    } else {
+      float st = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) st = (BITS == 8) ? fmaxf(st, fabsf(v[i])) : st + fabsf(v[i]);
+      st = row_reduce<T, BITS == 8>(st, redf, row, t);
+      float f, s;
+      if constexpr (BITS == 8) {
+        const float gamma = st * c;
+        f = 127.0f / (gamma + kEps);
+        s = gamma / 127.0f;
+      } else {
+        const float beta = (st * c) / (float)K;
+        f = kSqrt7 / (beta + kEps);
+        s = beta / kSqrt7;
+      }
+      // The rotated value is v * c; quantise v * (c * f).  Rounding: the
+      // clipped value plus 1.5 * 2^23 is rounded to an integer by the fp32
+      // add (nearest-even), whose low byte is then the two's-complement code.
+      const float fc = HAD ? c * f : f;
+      constexpr float lo = BITS == 8 ? -128.0f : -8.0f;
+      constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
+      constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: fp32 values in [2^23, 2^24) are integers
+      constexpr int kMagicBits = 0x4b400000;
+      // four codes as the bytes of one word: fma(v, fc, 1.5*2^23) rounds the
+      // exact product v*fc to the nearest integer (ties to even) in the low
+      // mantissa bits; the clip is done on those bits
+      auto quant4 = [&](const float* vv) {
+        int b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int bits = __float_as_int(__builtin_fmaf(vv[j], fc, kMagic));
+          b[j] = min(max(bits, kMagicBits + (int)lo), kMagicBits + (int)hi);
+        }
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)b[1], (uint32_t)b[0], 0x0c0c0400u);
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)b[3], (uint32_t)b[2], 0x04000c0cu);
+        return p01 | p23;
+      };
+      int qsum = 0;
+      if constexpr (!HAD) {
+        // the thread's 64 elements are contiguous: pack and store directly
+#pragma unroll
+        for (int gq = 0; gq < 8; ++gq) {
+          const uint32_t w0 = quant4(v + 8 * gq), w1 = quant4(v + 8 * gq + 4);
+          qsum = __builtin_amdgcn_sdot4((int)w0, 0x01010101, qsum, false);
+          qsum = __builtin_amdgcn_sdot4((int)w1, 0x01010101, qsum, false);
+          const int e0 = (t << 6) | (8 * gq);
+          if (live) {
+            if constexpr (BITS == 8) {
+              *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(codes) + m * (int64_t)K + e0) = make_uint2(w0, w1);
+            } else {
+              reinterpret_cast<uint32_t*>(codes)[m * (int64_t)(K / 8) + (e0 >> 3)] =
+                  (w0 & 0x0f0f0f0fu) | ((w1 & 0x0f0f0f0fu) << 4);
+            }
+          }
+        }
+      } else {
+        // quantise groups of 4 consecutive elements; codes to LDS in natural
+        // order: INT8 one byte per code; INT4 one word per group holding its
+        // nibbles in half h = (e >> 2) & 1 of each byte (the other half zero),
+        // so that two neighbouring groups OR into one packed word
+        uint8_t* C8 = reinterpret_cast<uint8_t*>(L);
+#pragma unroll
+        for (int gi = 0; gi < 16; ++gi) {
+          const uint32_t w = quant4(v + 4 * gi);
+          qsum = __builtin_amdgcn_sdot4((int)w, 0x01010101, qsum, false);
+          const int e = last_e(gi);
+          if constexpr (BITS == 8) {
+            *reinterpret_cast<uint32_t*>(C8 + e) = w;
+          } else {
+            *reinterpret_cast<uint32_t*>(C8 + e) = (w & 0x0f0f0f0fu) << (4 * ((e >> 2) & 1));
+          }
+        }
+        __syncthreads();
+        if (live) {
+          if constexpr (BITS == 8) {
+            int8_t* dst = reinterpret_cast<int8_t*>(codes) + m * (int64_t)K;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int u = t + T * qq;  // 16-byte unit = 16 codes
+              *reinterpret_cast<uint4*>(dst + 16 * u) = *reinterpret_cast<const uint4*>(C8 + 16 * u);
+            }
+          } else {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(codes) + m * (int64_t)(K / 8);
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const int u = t + T * qq;  // 4 output words = 8 groups
+              const uint4 a = *reinterpret_cast<const uint4*>(C8 + 32 * u);
+              const uint4 b = *reinterpret_cast<const uint4*>(C8 + 32 * u + 16);
+              *reinterpret_cast<uint4*>(dst + 4 * u) = make_uint4(a.x | a.y, a.z | a.w, b.x | b.y, b.z | b.w);
+            }
+          }
+        }
+      }
+      qsum = row_reduce_int<T>(qsum, redi, row, t);
+      if (live && t == 0) {
+        scales[m] = s;
+        if (rowsum) rowsum[m] = qsum;
+      }
+      __syncthreads();  // LDS and reduction scratch are reused by the next row group
+    }
+  }
+}
+
 // Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
 // per block of 256 threads, each holding up to 8 chunks of 8 elements.
 template <bool BF16, int BITS>
@@ -353,6 +699,18 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
 }
 
 template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+hipError_t launch_fq64(const void* x, int64_t M, int64_t ldx, void* codes, float* scales, int32_t* rowsum,
+                       float* y, int cu_count, hipStream_t s) {
+  using G = G64<LOG2K>;
+  const int64_t groups = (M + G::RPB - 1) / G::RPB;
+  const int64_t cap = 2 * (int64_t)(cu_count > 0 ? cu_count : 256);  // two blocks fit per CU
+  const int64_t blocks = groups < cap ? groups : cap;
+  hipLaunchKernelGGL((k_fwht_quant64<LOG2K, BF16, BITS, HAD, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, x, M,
+                     ldx, codes, scales, rowsum, y);
+  return hipGetLastError();
+}
+
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
 hipError_t launch_fq(const void* x, int64_t M, int64_t ldx, void* codes, float* scales,
                      int32_t* rowsum, float* y, hipStream_t s) {
   using G = Geom<LOG2K>;
@@ -364,9 +722,12 @@ hipError_t launch_fq(const void* x, int64_t M, int64_t ldx, void* codes, float* 
 
 template <int LOG2K>
 hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, int bits,
-                          void* codes, float* scales, int32_t* rowsum, hipStream_t s) {
-#define HBL_FQ(B16, BITS, HAD) \
-  return launch_fq<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, s)
+                          void* codes, float* scales, int32_t* rowsum, int cu, hipStream_t s) {
+#define HBL_FQ(B16, BITS, HAD)                                                                       \
+  if constexpr (LOG2K >= 10)                                                                         \
+    return launch_fq64<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, cu, s); \
+  else                                                                                               \
+    return launch_fq<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, s)
   if (bf16) {
     if (had) { if (bits == 8) HBL_FQ(true, 8, true); else HBL_FQ(true, 4, true); }
     else { if (bits == 8) HBL_FQ(true, 8, false); else HBL_FQ(true, 4, false); }
@@ -387,7 +748,7 @@ int ilog2(int K) {
 
 hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx,
                                  bool hadamard, int bits, void* codes, float* scales,
-                                 int32_t* rowsum, hipStream_t s) {
+                                 int32_t* rowsum, int cu, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const bool pow2 = (K & (K - 1)) == 0;
   if (!pow2) {
@@ -402,34 +763,39 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
     return hipGetLastError();
   }
   switch (ilog2(K)) {
-    case 4: return dispatch_quant<4>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 5: return dispatch_quant<5>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 6: return dispatch_quant<6>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 7: return dispatch_quant<7>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 8: return dispatch_quant<8>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 9: return dispatch_quant<9>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 10: return dispatch_quant<10>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 11: return dispatch_quant<11>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 12: return dispatch_quant<12>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 13: return dispatch_quant<13>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
-    case 14: return dispatch_quant<14>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, s);
+    case 4: return dispatch_quant<4>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 5: return dispatch_quant<5>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 6: return dispatch_quant<6>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 7: return dispatch_quant<7>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 8: return dispatch_quant<8>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 9: return dispatch_quant<9>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 10: return dispatch_quant<10>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 11: return dispatch_quant<11>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 12: return dispatch_quant<12>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 13: return dispatch_quant<13>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
+    case 14: return dispatch_quant<14>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, float* y,
+hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, float* y, int cu,
                                hipStream_t s) {
   if (M == 0) return hipSuccess;
 #define HBL_HF(L)                                                                              \
   case L:                                                                                      \
     return x_bf16 ? launch_fq<L, true, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s) \
                   : launch_fq<L, false, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s);
+#define HBL_HF64(L)                                                                                      \
+  case L:                                                                                                \
+    return x_bf16 ? launch_fq64<L, true, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, cu, s)     \
+                  : launch_fq64<L, false, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, cu, s);
   switch (ilog2(K)) {
     HBL_HF(4) HBL_HF(5) HBL_HF(6) HBL_HF(7) HBL_HF(8) HBL_HF(9)
-    HBL_HF(10) HBL_HF(11) HBL_HF(12) HBL_HF(13) HBL_HF(14)
+    HBL_HF64(10) HBL_HF64(11) HBL_HF64(12) HBL_HF64(13) HBL_HF64(14)
     default: return hipErrorInvalidValue;
   }
 #undef HBL_HF
+#undef HBL_HF64
 }
 
 }  // namespace hbl
