@@ -60,18 +60,55 @@ def dev_x(x_np):
 
 
 def time_stream(fn, reps):
-    """Average duration (s) of ``fn`` over ``reps`` back-to-back launches,
-    from HIP events recorded on the current stream (where the library
-    enqueues its kernels)."""
+    """Average GPU duration (s) of ``fn`` (one or more library launches).
+
+    The ``reps`` calls are captured once into a HIP graph and the graph is
+    replayed, so that host launch overhead does not leak into the figure;
+    HIP events on the current stream (where the library enqueues) bracket the
+    replays.  Falls back to back-to-back eager launches if capture fails."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
-    a.record()
-    for _ in range(reps):
-        fn()
-    b.record()
-    b.synchronize()
-    return a.elapsed_time(b) / 1e3 / reps
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        n = 5
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3 / (n * reps)
+    except Exception:  # capture unsupported: eager launches
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3 / reps
+
+
+def graph_of(fn):
+    """One call of ``fn`` captured as a HIP graph (None if capture fails)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+    except Exception:
+        torch.cuda.synchronize()
+        return None
 
 
 def cpu_baseline(x_np, w_np, bits, had, min_seconds=10.0, chunk=64):
@@ -117,9 +154,12 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws = hbl.forward_workspace(M, K, bits, "cuda")
 
-    def step():
+    def layer():
         hbl.forward(x, packed, alpha, bits, hadamard=had, out=out, workspace=ws)
 
+    # one step = one graph replay of the layer (both kernels), when capture works
+    g = graph_of(layer)
+    step = g.replay if g is not None else layer
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -158,6 +198,7 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
                          "achieved_gbs": q_bytes / t_q / 1e9,
                          "frac": q_bytes / t_q / 1e9 / HBM_PEAK_GBS},
         "gemm_bytes_min": code_bytes + w_bytes + 2 * M * N,
+        "launch": "hip graph" if g is not None else "eager",
     }
     return res
 
@@ -177,42 +218,110 @@ def run_decode(args, hbl, torch):
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws = hbl.forward_workspace(M, K, bits, "cuda")
 
-    def step(i):
-        p, a = mats[i % n_mats]
-        hbl.forward(x, p, a, bits, out=out, workspace=ws)
+    # one graph holds one decode call per matrix (cycling the matrices);
+    # a step is one call
+    def all_mats():
+        for p, a in mats:
+            hbl.forward(x, p, a, bits, out=out, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
+    g = graph_of(all_mats)
+    run = g.replay if g is not None else all_mats
+    reps = max(1, -(-args.steps // n_mats))
+    for _ in range(max(1, args.warmup // n_mats)):
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(reps):
+        run()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    dt = (time.perf_counter() - t0) / (reps * n_mats)
     # matmul kernel alone, cycling the matrices
-    reps = max(args.kernel_reps, 2 * n_mats)
     ctr = [0]
 
-    def g():
+    def gem():
         p, a = mats[ctr[0] % n_mats]
         ctr[0] += 1
         hbl.ternary_gemm(q, bits, s, rs, p, a, K, out=out)
 
-    t_g = time_stream(g, reps)
+    t_g = time_stream(gem, n_mats)
     t_q = time_stream(lambda: hbl.hadamard_quant(x, bits), args.kernel_reps)
     g_bytes = w_bytes + M * K + 8 * M + 2 * M * N
     bw = g_bytes / t_g / 1e9
     return {
-        "metric": METRIC, "value": M / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": M / dt, "unit": "tokens/s", "n_gpus": 1, "steps": reps * n_mats,
         "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": f"decode M={M} K={K} N={N} INT8, {n_mats} matrices cycled", "M": M, "K": K,
                    "N": N, "bits": 8, "hadamard": True, "matrices": n_mats},
+        "launch": "hip graph" if g is not None else "eager",
         "roofline": {"bound": "hbm", "kernel": "k_gemv (weight streaming)", "achieved": bw,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": bw / HBM_PEAK_GBS, "traffic": None,
                      "avg_kernel_us": t_g * 1e6, "algorithmic_bytes_per_launch": g_bytes},
         "quant_kernel": {"avg_kernel_us": t_q * 1e6},
     }
+
+
+def run_block(args, hbl, torch):
+    """The seven linears of one 7B block at M = 65536 tokens: Q/K/V share one
+    quantisation of their input, up/gate another; Wo and Wdown rotate their
+    inputs.  One step = 4 quantisations + 7 matmuls, per activation mode."""
+    import workloads
+    M = workloads.CONFIGS["block_7b"]["M"]
+    xs = {name: dev_x(workloads.block_input(name)) for name, _ in workloads.BLOCK_7B_INPUTS}
+    ws = {}
+    for name, K, N, had in workloads.BLOCK_7B_LAYERS:
+        ws[name] = hbl.ternarize_weights(torch.from_numpy(workloads.block_weights(name)).cuda())
+    groups = [("attn_in", False, ["q", "k", "v"]), ("o_in", True, ["o"]),
+              ("ffn_in", False, ["up", "gate"]), ("down_in", True, ["down"])]
+    out = {}
+    for name, K, N, had in workloads.BLOCK_7B_LAYERS:
+        out[name] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    results = []
+    for bits in ([8, 4] if args.bits == 0 else [args.bits]):
+        qbuf = {}
+        for inp, had, layers in groups:
+            K = dict(workloads.BLOCK_7B_INPUTS)[inp]
+            shape, dt = hbl.codes_shape(M, K, bits)
+            qbuf[inp] = (torch.empty(shape, dtype=dt, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda"),
+                         torch.empty(M, dtype=torch.int32, device="cuda"))
+
+        def quant(inp, had):
+            q, sc, rs = qbuf[inp]
+            x = xs[inp]
+            hbl._check(hbl.lib().hbl_hadamard_quant(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
+                                                    hbl.HADAMARD if had else 0, bits, q.data_ptr(), sc.data_ptr(),
+                                                    rs.data_ptr(), hbl._stream()), "hbl_hadamard_quant")
+
+        def gemm(inp, layer):
+            q, sc, rs = qbuf[inp]
+            p, a = ws[layer]
+            K = dict(workloads.BLOCK_7B_INPUTS)[inp]
+            hbl.ternary_gemm(q, bits, sc, rs, p, a, K, out=out[layer])
+
+        def step():
+            for inp, had, layers in groups:
+                quant(inp, had)
+                for layer in layers:
+                    gemm(inp, layer)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        per = {}
+        for inp, had, layers in groups:
+            per["quant " + inp] = time_stream(lambda: quant(inp, had), args.kernel_reps) * 1e6
+            for layer in layers:
+                per["gemm " + layer] = time_stream(lambda: gemm(inp, layer), args.kernel_reps) * 1e6
+        ops = sum(2.0 * M * K * N for _, K, N, _ in workloads.BLOCK_7B_LAYERS)
+        gemm_us = sum(v for k, v in per.items() if k.startswith("gemm"))
+        results.append({"bits": bits, "tokens_per_s": M / dt, "ms_per_step": dt * 1e3, "effective_tops": ops / dt / 1e12,
+                        "gemm_only_tops": ops / (gemm_us * 1e-6) / 1e12, "kernel_us": per})
+    return {"metric": METRIC, "workload": "block_7b: the 7 linears of a 7B block, M=65536", "results": results}
 
 
 def main():
@@ -247,23 +356,7 @@ def main():
         return
 
     if args.workload == "block_7b":
-        results = []
-        for bits in ([8, 4] if args.bits == 0 else [args.bits]):
-            tot_t, tot_ops = 0.0, 0.0
-            layers = {}
-            for name, K, N, had in workloads.BLOCK_7B_LAYERS:
-                x_np = workloads.block_input(workloads.BLOCK_7B_INPUT_OF[name])
-                w_np = workloads.block_weights(name)
-                r = run_layer(args, hbl, torch, x_np, w_np, bits, had, name)
-                layers[name] = {"ms": r["ms_per_step"], "gemm_tops": r["roofline"]["achieved"],
-                                "quant_gbs": r["quant_kernel"]["achieved_gbs"]}
-                tot_t += r["ms_per_step"]
-                tot_ops += 2.0 * r["config"]["M"] * N * K
-                del x_np
-            M = workloads.CONFIGS["block_7b"]["M"]
-            results.append({"bits": bits, "tokens_per_s": M / (tot_t / 1e3), "ms": tot_t,
-                            "effective_tops": tot_ops / (tot_t / 1e3) / 1e12, "layers": layers})
-        print(json.dumps({"metric": METRIC, "workload": "block_7b", "results": results}), flush=True)
+        print(json.dumps(run_block(args, hbl, torch)), flush=True)
         return
 
     c = {"tiny": workloads.tiny, "wo_7b": workloads.wo_7b, "wdown_7b": workloads.wdown_7b}[args.workload]()

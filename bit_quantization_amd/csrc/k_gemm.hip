@@ -3,9 +3,9 @@
 //   acc[m][n] = sum_k q_x[m][k] q_w[n][k],  out = (scale_m * alpha) * acc.
 //
 // Two kernels:
-//   k_gemm -- large token counts.  Block tile BM x BN, 4 waves, each wave a
-//     128 x 64 (or 64 x 128) tile of 16x16x64 int8 MFMAs with int32
-//     accumulators; two blocks per CU.  Codes and weights are staged to LDS
+//   k_gemm -- large token counts.  Block tile 256 x 256 (8 waves of
+//     128 x 64) or 128 x 128 (4 waves of 64 x 64), each wave a tile of
+//     16x16x64 int8 MFMAs with int32 accumulators.  Codes and weights are staged to LDS
 //     as they are stored (packed) and widened by each wave after its LDS
 //     read.  Weights are decoded from two bits to the unsigned byte
 //     c = q + 1 in {0, 1, 2}, so the MFMA sums q_x * c; the epilogue
@@ -359,24 +359,194 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode with very few tokens (M <= 4), K % 1024 == 0: dot-product kernel.
+// A block of 512 threads owns NB output features.  Thread t covers the 64
+// codes k = 64*(t % TK) .. +63 (TK = min(256, K/64) threads per feature row)
+// of RPT = NB / (512 / TK) of those features; it loads the tokens' codes for
+// its k-range once (registers) and streams the rows' packed weights with one
+// 16-byte load per row (consecutive threads read consecutive 16 bytes of a
+// row).  Each weight word gives 4 dwords of bytes c = q_w + 1, multiplied
+// into the codes with v_dot4_i32_i8; INT4 codes are widened to 16 q_x (the
+// sums are divided by 16 at the end, exactly).  Partial sums are reduced
+// over the TK threads of a row (xor-butterflies within a wave, then a fixed
+// order over the waves), then rescaled.
+template <int BITS, int OUT, int MT, int TK>
+struct DotGeom {
+  static constexpr int NTH = 512;                          // threads per block
+  static constexpr int RP = NTH / TK;                      // feature rows side by side
+  static constexpr int NB = RP > 8 ? RP : 8;               // features per block
+  static constexpr int RPT = NB / RP;                      // rows per thread
+};
+
+template <int BITS, int OUT, int MT, int TK>
+__global__ void __launch_bounds__(512)
+k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
+           const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
+           const float* __restrict__ alpha, int M, int64_t N, int64_t K,
+           void* __restrict__ out, int64_t ldo) {
+  using DG = DotGeom<BITS, OUT, MT, TK>;
+  constexpr int NB = DG::NB;
+  __shared__ int red[DG::NTH / 64][NB][MT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static_assert(TK >= 16 && TK <= 256, "threads per feature row");
+  constexpr int RP = DG::RP;
+  constexpr int RPT = DG::RPT;
+  const int kt = tid % TK, rg = tid / TK;
+  const int64_t n0 = (int64_t)blockIdx.x * NB;
+  const int64_t KW = K / 16;
+
+  // the weights: rows n0 + rg + RP*i, words 4*kt .. 4*kt+3; issue every load first
+  uint4 w[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) w[i] = load_stream(wp + (n0 + rg + (int64_t)RP * i) * KW + 4 * kt);
+
+  // the tokens' codes for k = 64*kt .. +63, as 16 dwords of signed bytes
+  uint32_t x[MT][16];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < M) {
+      if constexpr (BITS == 8) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (int64_t)m * K + 64 * kt);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 u = p[q];
+          x[m][4 * q] = u.x; x[m][4 * q + 1] = u.y; x[m][4 * q + 2] = u.z; x[m][4 * q + 3] = u.w;
+        }
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(codes) + (int64_t)m * (K / 8) + 8 * kt);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 u = p[q];
+          const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[m][8 * q + 2 * j] = (ww[j] << 4) & 0xf0f0f0f0u;  // codes 0-3 of the word, as 16 q
+            x[m][8 * q + 2 * j + 1] = ww[j] & 0xf0f0f0f0u;     // codes 4-7
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[m][j] = 0;
+    }
+  }
+
+  int acc[RPT][MT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c0 = ws[q] & 0x03030303u, c1 = (ws[q] >> 2) & 0x03030303u;
+      const uint32_t c2 = (ws[q] >> 4) & 0x03030303u, c3 = (ws[q] >> 6) & 0x03030303u;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        int a = acc[i][m];
+        a = __builtin_amdgcn_sdot4((int)c0, (int)x[m][4 * q], a, false);
+        a = __builtin_amdgcn_sdot4((int)c1, (int)x[m][4 * q + 1], a, false);
+        a = __builtin_amdgcn_sdot4((int)c2, (int)x[m][4 * q + 2], a, false);
+        a = __builtin_amdgcn_sdot4((int)c3, (int)x[m][4 * q + 3], a, false);
+        acc[i][m] = a;
+      }
+    }
+  }
+  // reduce over the TK threads of each row: within the wave over the lanes
+  // of the same row group, then over the waves holding that row group
+  constexpr int lanes_per_row = TK < 64 ? TK : 64;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      int v = acc[i][m];
+#pragma unroll
+      for (int o = 1; o < lanes_per_row; o <<= 1) v += __shfl_xor(v, o);
+      acc[i][m] = v;
+    }
+  }
+  // lane 0 of each row group in each wave publishes its partials
+  if ((lane % lanes_per_row) == 0) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RP * i;  // feature within the block
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[i][m];
+    }
+  }
+  __syncthreads();
+  if (tid < NB * MT) {
+    const int row = tid / MT, m = tid % MT;
+    if (m < M) {
+      // the row belongs to row group row % RP, held by TK threads = TK/64 waves
+      // (or part of one wave when TK < 64)
+      int v = 0;
+      if constexpr (TK >= 64) {
+        constexpr int nw = TK / 64;            // waves per row group
+        const int w0 = (row % RP) * nw;        // first wave of the row's group
+#pragma unroll
+        for (int wv = 0; wv < nw; ++wv) v += red[w0 + wv][row][m];
+      } else {
+        v = red[(row % RP) * TK / 64][row][m];
+      }
+      if constexpr (BITS == 4) v >>= 4;  // exact: every product carries a factor 16
+      const int64_t n = n0 + row;
+      const float sc = scales[m] * *alpha;
+      const int t = v - rowsum[m];
+      if constexpr (OUT == 2) {
+        reinterpret_cast<int32_t*>(out)[(int64_t)m * ldo + n] = t;
+      } else if constexpr (OUT == 1) {
+        reinterpret_cast<float*>(out)[(int64_t)m * ldo + n] = sc * (float)t;
+      } else {
+        reinterpret_cast<uint16_t*>(out)[(int64_t)m * ldo + n] = f32_to_bf16_rne(sc * (float)t);
+      }
+    }
+  }
+}
+
 template <int BITS, int OUT>
 hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t* rowsum,
                            const uint32_t* wp, const float* alpha, int64_t M, int64_t N, int64_t K,
-                           void* out, int64_t ldo, int /*cu_count*/, hipStream_t s) {
+                           void* out, int64_t ldo, int cu_count, hipStream_t s) {
+  if (M <= 4 && K % 1024 == 0) {
+    const int64_t tk = K / 64 < 256 ? K / 64 : 256;
+#define HBL_DOT(MT, TK)                                                                                      \
+  if (N % DotGeom<BITS, OUT, MT, TK>::NB == 0) {                                                           \
+    hipLaunchKernelGGL((k_gemv_dot<BITS, OUT, MT, TK>), dim3((unsigned)(N / DotGeom<BITS, OUT, MT, TK>::NB)), \
+                       dim3(512), 0, s, codes, scales, rowsum, wp, alpha, (int)M, N, K, out, ldo);           \
+    return hipGetLastError();                                                                                \
+  }
+#define HBL_DOT_TK(MT)                          \
+  if (tk == 256) { HBL_DOT(MT, 256) }           \
+  else if (tk == 128) { HBL_DOT(MT, 128) }      \
+  else if (tk == 64) { HBL_DOT(MT, 64) }        \
+  else if (tk == 32) { HBL_DOT(MT, 32) }        \
+  else { HBL_DOT(MT, 16) }
+    if (M == 1) { HBL_DOT_TK(1) }
+    else if (M == 2) { HBL_DOT_TK(2) }
+    else { HBL_DOT_TK(4) }
+#undef HBL_DOT_TK
+#undef HBL_DOT
+  }
   if (M <= kGemvMaxM) {
     hipLaunchKernelGGL((k_gemv<BITS, OUT>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales,
                        rowsum, wp, alpha, (int)M, N, K, out, ldo);
     return hipGetLastError();
   }
-  // 128 x 256 tiles (4 waves of 128 x 64) when M is the smaller side,
-  // 256 x 128 otherwise; two blocks share a CU.
-  if (M <= N) {
-    const int tm = (int)((M + 127) / 128), tn = (int)((N + 255) / 256);
-    hipLaunchKernelGGL((k_gemm<BITS, OUT, 128, 256, 1, 4, 2>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
+  // 256 x 256 tiles (8 waves of 128 x 64, one block per CU) when there are
+  // enough of them to fill the chip; otherwise 128 x 128 tiles (4 waves of
+  // 64 x 64, several blocks per CU).
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= cu_count) {
+    const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
+    hipLaunchKernelGGL((k_gemm<BITS, OUT, 256, 256, 2, 4, 1>), dim3((unsigned)(tm * tn)), dim3(512), 0, s, codes,
                        scales, rowsum, wp, alpha, M, N, K, out, ldo, tm, tn);
   } else {
-    const int tm = (int)((M + 255) / 256), tn = (int)((N + 127) / 128);
-    hipLaunchKernelGGL((k_gemm<BITS, OUT, 256, 128, 2, 2, 2>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
+    const int tm = (int)((M + 127) / 128), tn = (int)((N + 127) / 128);
+    hipLaunchKernelGGL((k_gemm<BITS, OUT, 128, 128, 2, 2, 2>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, codes,
                        scales, rowsum, wp, alpha, M, N, K, out, ldo, tm, tn);
   }
   return hipGetLastError();
