@@ -1,6 +1,7 @@
 """Builds libhbl.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
 
-Usage: python -m bit_quantization_amd.build [--force]
+Usage: python bit_quantization_amd/build.py [--force]  (run by path: importing
+the package loads the library, which need not exist or be current yet)
 The library is written next to this file, in-tree, so that it travels with
 the source tree.
 """
@@ -23,7 +24,7 @@ HEADERS = [os.path.join(CSRC, "hbl_internal.h"), os.path.join(ROOT, "include", "
 # -ffp-contract=off: no fused multiply-adds, so every product and sum is
 # rounded as written.  Packed fp32 instructions are disabled.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]

@@ -5,8 +5,9 @@
 // Two kernels:
 //   k_gemm -- large token counts.  Block tile 256 x 256 (8 waves of
 //     128 x 64) or 128 x 128 (4 waves of 64 x 64), each wave a tile of
-//     16x16x64 int8 MFMAs with int32 accumulators.  Codes and weights are staged to LDS
-//     as they are stored (packed) and widened by each wave after its LDS
+//     16x16x64 int8 MFMAs with int32 accumulators.  Codes and weights are
+//     copied to LDS as they are stored (packed), by direct-to-LDS buffer
+//     loads three stages ahead, and widened by each wave after its LDS
 //     read.  Weights are decoded from two bits to the unsigned byte
 //     c = q + 1 in {0, 1, 2}, so the MFMA sums q_x * c; the epilogue
 //     subtracts sum_k q_x (the token's row sum of codes) to obtain
@@ -22,11 +23,16 @@
 // output features of one token: one 8-byte bf16 store.
 #include "hbl_internal.h"
 
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
 namespace hbl {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // Streaming 16-byte load (data used once: do not keep it in the caches).
 __device__ __forceinline__ uint4 load_stream(const uint32_t* p) {
@@ -90,21 +96,25 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
        const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
        const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo, int tilesM, int tilesN) {
-  constexpr int NT = 64 * WGM * WGN;
+  // The body is compiled for the device only: the host pass (which only
+  // needs the launch stub) drops this template's instantiation otherwise.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = WGM * WGN;                // waves
   constexpr int S = 2;                         // MFMA k-steps per stage
+  constexpr int NST = 3;                       // LDS stages in flight
   constexpr int BKC = 64 * S;                  // codes per row per stage
   constexpr int AROW = BKC * BITS / 8;         // code bytes per row per stage
   constexpr int BROW = 16 * S;                 // weight bytes per row per stage
+  constexpr int ACPR = AROW / 16, BCPR = BROW / 16;  // 16-byte units per row
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int BCPR = BROW / 16;              // weight chunks per row
-  constexpr int PA = BM * AROW / 16 / NT;      // 16-byte staging chunks per thread
-  constexpr int PB = BN * BROW / 16 / NT;
-  static_assert(PA * NT * 16 == BM * AROW && PB * NT * 16 == BN * BROW, "staging must divide evenly");
+  constexpr int ADMA = BM * AROW / 1024 / NW;  // 1 KB direct-to-LDS loads per wave per stage
+  constexpr int BDMA = BN * BROW / 1024 / NW;
+  static_assert(ADMA * NW * 1024 == BM * AROW && BDMA * NW * 1024 == BN * BROW, "staging must divide evenly");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "fragment rows");
   constexpr int SPR = BITS == 4 ? 2 : 1;       // MFMA steps per 16-byte code read
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AROW];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * BROW];
+  __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * AROW];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[NST][BN * BROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
@@ -124,8 +134,7 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 
   const int64_t arow_bytes = BITS == 4 ? K / 2 : K;  // global code row stride
   const int64_t brow_bytes = K / 4;                  // global weight row stride
-  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(codes);
-  const uint8_t* B8 = reinterpret_cast<const uint8_t*>(wp);
+  const int arows = (int)min<int64_t>(BM, M - m0), brows = (int)min<int64_t>(BN, N - n0);
 
   // LDS byte offsets (swizzled) of 16-byte unit u of row r
   auto aoff = [](int r, int u) {
@@ -134,55 +143,51 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
   };
   auto boff = [](int r, int u) { return r * BROW + 16 * (u ^ ((r >> 3) & 1)); };
 
-  // Staging: chunk p of this thread is row r0 + RPP*p of the tile, 16-byte
-  // unit col.  Every load is issued at a valid address (rows past the end
-  // re-read the last row, k past the end re-reads offset 0) and zeroed when
-  // out of range, so the stage body has no branches.  RPP is a multiple of
-  // 16, so the swizzle of a chunk's row does not depend on p and every LDS
-  // offset is one base plus a constant.
-  constexpr int ACPR = AROW / 16;                    // code chunks per row
-  constexpr int A_RPP = NT / ACPR, B_RPP = NT / BCPR;  // rows per staging pass
-  static_assert(A_RPP % 16 == 0 && B_RPP % 16 == 0, "swizzle period");
-  const int ar0 = tid / ACPR, acol = tid % ACPR;
-  const int br0 = tid / BCPR, bcol = tid % BCPR;
-  const int la0 = aoff(ar0, acol), lb0 = boff(br0, bcol);
-  // The staging loads of a stage are issued in two halves, each written to
-  // LDS halfway through the compute, to halve the registers they hold.
-  static_assert(PA % 2 == 0 && (PB % 2 == 0 || PB == 1), "halves");
-  constexpr int HA = PA / 2, HB = PB >= 2 ? PB / 2 : PB;
-  uint4 ra[HA], rb[HB];
-  auto gload = [&](int kt, int part) {
-    const int64_t ka = (int64_t)kt * AROW + 16 * acol, kb = (int64_t)kt * BROW + 16 * bcol;
-    const bool oka = ka < arow_bytes, okb = kb < brow_bytes;
+  // Staging by direct-to-LDS buffer loads: each wave instruction fills 1 KB
+  // of a stage (lane l -> 16 bytes at base + 16 l).  Lane l of instruction j
+  // of wave w writes physical unit P = 64 (w + NW j) + l, i.e. row P / CPR,
+  // physical unit P % CPR, which holds logical unit (P % CPR) ^ swizzle(row).
+  // Rows and k past the end get an offset beyond the buffer's range, which
+  // reads as zero.  The buffers start at the block's first row.
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(codes) + m0 * arow_bytes), (short)0,
+      (int)(arows * arow_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wp) + n0 * brow_bytes), (short)0,
+      (int)(brows * brow_bytes), 0x00020000);
+  constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range
+  uint32_t aoffg[ADMA], boffg[BDMA];      // global byte offset of the unit at stage 0 (or kOut)
+  int acolb[ADMA], bcolb[BDMA];           // byte offset of the unit within a stage row
 #pragma unroll
-    for (int q = 0; q < HA; ++q) {
-      const int64_t row = m0 + ar0 + A_RPP * (part * HA + q);
-      const bool ok = oka && row < M;
-      const uint4 v = *reinterpret_cast<const uint4*>(A8 + (row < M ? row : M - 1) * arow_bytes +
-                                                      (oka ? ka : 16 * acol));
-      ra[q] = ok ? v : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < ADMA; ++j) {
+    const int P = 64 * (wave + NW * j) + lane, r = P / ACPR, p = P % ACPR;
+    const int u = BITS == 8 ? (p ^ ((r >> 1) & 7)) : (p ^ ((r >> 2) & 3));
+    acolb[j] = 16 * u;
+    aoffg[j] = r < arows ? (uint32_t)(r * arow_bytes + 16 * u) : kOut;
+  }
+#pragma unroll
+  for (int j = 0; j < BDMA; ++j) {
+    const int P = 64 * (wave + NW * j) + lane, r = P / BCPR, p = P % BCPR;
+    const int u = p ^ ((r >> 3) & 1);
+    bcolb[j] = 16 * u;
+    boffg[j] = r < brows ? (uint32_t)(r * brow_bytes + 16 * u) : kOut;
+  }
+  auto stage_load = [&](int kt, int buf) {
+    const uint32_t ka = (uint32_t)kt * AROW, kb = (uint32_t)kt * BROW;
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) {
+      const bool ok = aoffg[j] != kOut && ka + acolb[j] < arow_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, &As[buf][1024 * (wave + NW * j)], 16, ok ? aoffg[j] + ka : kOut, 0, 0,
+                                               0);
     }
-    if (PB >= 2 || part == 0) {
 #pragma unroll
-      for (int q = 0; q < HB; ++q) {
-        const int64_t row = n0 + br0 + B_RPP * (part * HB + q);
-        const bool ok = okb && row < N;
-        const uint4 v = *reinterpret_cast<const uint4*>(B8 + (row < N ? row : N - 1) * brow_bytes +
-                                                        (okb ? kb : 16 * bcol));
-        rb[q] = ok ? v : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto sstore = [&](int buf, int part) {
-#pragma unroll
-    for (int q = 0; q < HA; ++q)
-      *reinterpret_cast<uint4*>(&As[buf][la0 + A_RPP * AROW * (part * HA + q)]) = ra[q];
-    if (PB >= 2 || part == 0) {
-#pragma unroll
-      for (int q = 0; q < HB; ++q)
-        *reinterpret_cast<uint4*>(&Bs[buf][lb0 + B_RPP * BROW * (part * HB + q)]) = rb[q];
+    for (int j = 0; j < BDMA; ++j) {
+      const bool ok = boffg[j] != kOut && kb + bcolb[j] < brow_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, &Bs[buf][1024 * (wave + NW * j)], 16, ok ? boffg[j] + kb : kOut, 0, 0,
+                                               0);
     }
   };
+  constexpr int DMA_PER_STAGE = ADMA + BDMA;
 
   v4i acc[FN][FM];
 #pragma unroll
@@ -194,25 +199,30 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
   const int fr = lane % 16, g = lane / 16;
   // Fragment rows are wm*WM + 16*j + fr (codes) and wn*WN + 16*i + fr
   // (weights): the swizzle depends on fr only, and fragment j (i) sits at a
-  // constant offset from fragment 0.
-  // codes of lane group g: unit g (INT4: both steps) or units 2g, 2g+1
-  // (INT8: one per step); weights: 8 bytes, half (g & 1) of unit g >> 1
+  // constant offset from fragment 0.  Codes of lane group g: unit g (INT4:
+  // both steps) or units 2g, 2g+1 (INT8: one per step); weights: 8 bytes,
+  // half (g & 1) of unit g >> 1.
   const int abase0 = BITS == 4 ? aoff(wm * WM + fr, g) : aoff(wm * WM + fr, 2 * g);
   const int abase1 = BITS == 4 ? abase0 : aoff(wm * WM + fr, 2 * g + 1);
   const int bbase = boff(wn * WN + fr, g >> 1) + 8 * (g & 1);
   constexpr int AFRAG = 16 * AROW, BFRAG = 16 * BROW;  // bytes between fragments
 
-  gload(0, 0);
-  sstore(0, 0);
-  gload(0, 1);
-  sstore(0, 1);
-  __syncthreads();
+  // prologue: stages 0 and 1 in flight
+  stage_load(0, 0);
+  if (nk > 1) stage_load(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const uint8_t* Ab = As[cur];
-    const uint8_t* Bb = Bs[cur];
-    const int kn = kt + 1 < nk ? kt + 1 : kt;  // the last stage re-reads itself into the spare buffer
-    gload(kn, 0);
+    // stage kt must have landed: at most the loads of stage kt + 1 may be
+    // outstanding; then every wave's share is visible after the barrier
+    if (kt + 1 < nk) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    // the buffer of stage kt + 2 was last read in stage kt - 1: free now
+    if (kt + 2 < nk) stage_load(kt + 2, (kt + 2) % NST);
+    const uint8_t* Ab = As[kt % NST];
+    const uint8_t* Bb = Bs[kt % NST];
     uint32_t bw[FN][S];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -248,14 +258,8 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
           for (int i = 0; i < FN; ++i) acc[i][j] = mfma16x16x64(bf[i], af, acc[i][j]);
         }
-        if (s == S / 2 - 1) {
-          sstore(cur ^ 1, 0);
-          gload(kn, 1);
-        }
       }
     }
-    sstore(cur ^ 1, 1);
-    __syncthreads();
   }
 
   const float al = *alpha;
@@ -274,6 +278,286 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
       store4<OUT>(out, m * ldo + n, a, R, sc);
     }
   }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Persistent matmul for large token counts (K a multiple of 512).
+//
+// One block of 4 waves (2 x 2) per CU, one wave per SIMD.  Block tile
+// BM x BN (256 x 256 when the tiles fill the chip, else 256 x 128), wave
+// tile BM/2 x BN/2 built from 32x32x32 int8 MFMAs whose int32 accumulators
+// live in the accumulation registers.  A stage is BK = 128 codes; four
+// stage buffers, each its own LDS variable, are refilled by direct-to-LDS
+// buffer loads four stages ahead.  Each block walks its tiles in sequence
+// and numbers the stages of all of them consecutively, so the loads and the
+// fragment prefetch of a tile's last stages already bring in the next tile.
+//
+// Fragment layout (32x32x32): lane l covers row / column l % 32 of its
+// fragment and, for MFMA step t of a stage, the 16 codes
+// k = 64 (l / 32) + 16 t .. + 15 of the stage (the same k for both
+// operands, so the MFMA's own k order does not matter).  The accumulator of
+// a fragment holds, in lane l and register r, token l % 32 and feature
+// 8 (r / 4) + 4 (l / 32) + r % 4.
+//
+// Within stage kt the waves meet once, halfway through the MFMAs: past that
+// barrier every wave has read stage kt's buffer (so its refill may start)
+// and stage kt + 1 has landed (so its fragments may be read while the
+// second half of stage kt's MFMAs runs).  The barrier carries no memory
+// fence (a fence would wait for every load in flight, the prefetch
+// included); each wave has waited for its own loads of the stage first.
+//
+// LDS rows are not padded; 16-byte units are XOR-swizzled by row
+// (unit u of row r at u ^ ((r >> s) & (U - 1)), U units per row,
+// s = log2(16 / U)) so that the 16 rows a b128 read touches at once fall
+// into distinct banks.
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+template <int BITS, int OUT, int BM, int BN>
+__global__ void __launch_bounds__(256, 1)
+k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
+          const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
+          const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
+          void* __restrict__ out, int64_t ldo, int tilesM, int tilesN) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int BK = 128, NSTEP = BK / 32, NST = 4;  // NST stage buffers; also the unroll
+  constexpr int AROW = BK * BITS / 8, BROW = BK / 4;  // bytes per row per stage
+  constexpr int AU = AROW / 16, BU = BROW / 16;       // 16-byte units per row
+  constexpr int ASH = ilog2c(16 / AU), BSH = ilog2c(16 / BU);
+  constexpr int NAU = AU / 2, NBU = BU / 2;           // units per lane half per fragment
+  constexpr int ADMA = BM * AROW / 1024 / NW, BDMA = BN * BROW / 1024 / NW;
+  static_assert(ADMA * NW * 1024 == BM * AROW && BDMA * NW * 1024 == BN * BROW, "staging must divide evenly");
+  static_assert(NBU == 1, "one weight unit per lane half");
+  constexpr int DPS = ADMA + BDMA;  // loads per wave per stage
+  constexpr int ASZ = BM * AROW, BSZ = BN * BROW;
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[ASZ], As1[ASZ], As2[ASZ], As3[ASZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
+  auto abuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
+    if constexpr (I == 0) return As0; else if constexpr (I == 1) return As1; else if constexpr (I == 2) return As2; else return As3;
+  };
+  auto bbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
+    if constexpr (I == 0) return Bs0; else if constexpr (I == 1) return Bs1; else if constexpr (I == 2) return Bs2; else return Bs3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % 2, wn = wave / 2;
+  const int64_t arow_bytes = BITS == 4 ? K / 2 : K;  // global code row stride
+  const int64_t brow_bytes = K / 4;                  // global weight row stride
+  const int nk = (int)(K / BK);                      // a multiple of NST
+
+  // Tiles of this block: r P + slot for r = 0, 1, ... (P blocks, a multiple
+  // of 8).  Consecutive block ids go to different XCDs; slot gives each XCD
+  // a contiguous range of each round's tiles, which are then walked in
+  // M-groups of 8 so that an XCD's blocks share codes and weights in its L2.
+  const int G = tilesM * tilesN, P = gridDim.x, b = blockIdx.x;
+  const int slot = (b % 8) * (P / 8) + b / 8;
+  const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
+  auto tile_of = [&](int r, int64_t& m0, int64_t& n0) {
+    const int L = r * P + slot;
+    constexpr int GROUP_M = 8;
+    const int per_group = GROUP_M * tilesN;
+    const int first_m = (L / per_group) * GROUP_M;
+    const int gsz = min(GROUP_M, tilesM - first_m);
+    m0 = (int64_t)(first_m + (L % per_group) % gsz) * BM;
+    n0 = (int64_t)((L % per_group) / gsz) * BN;
+  };
+
+  auto aswz = [](int r, int u) { return u ^ ((r >> ASH) & (AU - 1)); };
+  auto bswz = [](int r, int u) { return u ^ ((r >> BSH) & (BU - 1)); };
+  // Lane l of load j of wave w fills physical unit P = 64 (w + NW j) + l of
+  // a stage: row P / U, physical unit l % U, holding logical unit
+  // (l % U) ^ swizzle(row); the swizzle term is the same for every j, so one
+  // column offset per lane serves all loads.  Rows past the end of the
+  // matrix lie beyond the buffer's range and read as zero.
+  constexpr int AJR = 64 * NW / AU, BJR = 64 * NW / BU;  // rows between loads j and j + 1
+  const int ar0 = (64 * wave + lane) / AU, br0 = (64 * wave + lane) / BU;
+  const uint32_t aoff0 = (uint32_t)ar0 * (uint32_t)arow_bytes + 16u * (uint32_t)aswz(ar0, lane % AU);
+  const uint32_t boff0 = (uint32_t)br0 * (uint32_t)brow_bytes + 16u * (uint32_t)bswz(br0, lane % BU);
+  const uint32_t astep = (uint32_t)AJR * (uint32_t)arow_bytes, bstep = (uint32_t)BJR * (uint32_t)brow_bytes;
+  constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
+
+  // load cursor: tile dr (of this block), stage dk, and that tile's buffers
+  int dr = 0, dk = 0;
+  __amdgpu_buffer_rsrc_t rA, rB;
+  auto set_tile = [&](int r) {
+    int64_t m0 = 0, n0 = 0;
+    if (r < ntiles) tile_of(r, m0, n0);
+    const int arows = r < ntiles ? (int)min<int64_t>(BM, M - m0) : 0;
+    const int brows = r < ntiles ? (int)min<int64_t>(BN, N - n0) : 0;
+    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(codes) + m0 * arow_bytes),
+                                           (short)0, (int)(arows * arow_bytes), 0x00020000);
+    rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wp) + n0 * brow_bytes),
+                                           (short)0, (int)(brows * brow_bytes), 0x00020000);
+  };
+  // loads of stage (dr, dk) into buffer I; advances the cursor
+  auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
+    uint8_t* const Ad = abuf(bi);
+    uint8_t* const Bd = bbuf(bi);
+    const bool live = dr < ntiles;
+    const uint32_t va = live ? aoff0 + (uint32_t)dk * AROW : kOut;
+    const uint32_t vb = live ? boff0 + (uint32_t)dk * BROW : kOut;
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Ad + 1024 * (wave + NW * j), 16, va + j * astep, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+    if (++dk == nk) {
+      dk = 0;
+      set_tile(++dr);
+    }
+  };
+
+  v16i acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
+
+  const int fr = lane % 32, h = lane / 32;
+  const int ar = wm * WM + fr, br = wn * WN + fr;
+  int abase[NAU];
+#pragma unroll
+  for (int v = 0; v < NAU; ++v) abase[v] = ar * AROW + 16 * aswz(ar, NAU * h + v);
+  const int bbase = br * BROW + 16 * bswz(br, h);
+  constexpr int AFRAG = 32 * AROW, BFRAG = 32 * BROW;  // bytes between fragments
+
+  // A stage's fragments: the head (weights, and the code units of the first
+  // half of the MFMA steps) is read across the mid-stage barrier of the
+  // previous stage; the tail (code units of the second half) at the start of
+  // the stage itself, landing while the first half runs.
+  constexpr int HU = NAU / 2;
+  struct Head {
+    uint4 b[FN];
+    uint4 a[FM][HU];
+  };
+  struct Tail {
+    uint4 a[FM][HU];
+  };
+  auto read_head = [&]<int I>(Head& f, std::integral_constant<int, I> bi) {
+    const uint8_t* Ab = abuf(bi);
+    const uint8_t* Bb = bbuf(bi);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) f.b[i] = *reinterpret_cast<const uint4*>(Bb + bbase + BFRAG * i);
+#pragma unroll
+    for (int v = 0; v < HU; ++v)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) f.a[j][v] = *reinterpret_cast<const uint4*>(Ab + abase[v] + AFRAG * j);
+  };
+  auto read_tail = [&]<int I>(Tail& f, std::integral_constant<int, I> bi) {
+    const uint8_t* Ab = abuf(bi);
+#pragma unroll
+    for (int v = 0; v < HU; ++v)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) f.a[j][v] = *reinterpret_cast<const uint4*>(Ab + abase[HU + v] + AFRAG * j);
+  };
+  // MFMA steps t0 .. t1 - 1 (both within one half) of a stage.  Weights
+  // widen from two bits to the bytes c = q + 1
+  // (word -> {w, w >> 2, w >> 4, w >> 6} & 0x03030303); INT4 codes to the
+  // bytes 16 q (low nibbles shifted up, high nibbles in place); INT8 codes
+  // are used as stored.
+  auto compute = [&](const uint4 (&bq)[FN], const uint4 (&aq)[FM][HU], int t0, int t1) {
+#pragma unroll
+    for (int t = t0; t < t1; ++t) {
+      v4i bf[FN];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const uint4 q = bq[i];
+        const uint32_t w = (t == 0) ? q.x : (t == 1) ? q.y : (t == 2) ? q.z : q.w;
+        bf[i] = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                    (int)((w >> 6) & 0x03030303u)};
+      }
+      const int th = t % (NSTEP / 2);  // step within the half
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        v4i af;
+        if constexpr (BITS == 4) {
+          const uint4 q = aq[j][th / 2];
+          const uint32_t x0 = (th % 2 == 0) ? q.x : q.z, x1 = (th % 2 == 0) ? q.y : q.w;
+          af = v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
+                   (int)(x1 & 0xf0f0f0f0u)};
+        } else {
+          const uint4 q = aq[j][th];
+          af = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[i], af, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  auto bar = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Epilogue of compute tile r: sum q_x q_w = sum q_x c (/ 16 for INT4) - rowsum.
+  auto epilogue = [&](int r) {
+    // r made opaque here: nothing of the epilogue is computed early and kept
+    // live through the stage loop
+    asm volatile("" : "+s"(r));
+    int64_t m0, n0;
+    tile_of(r, m0, n0);
+    const float al = *alpha;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = m0 + wm * WM + 32 * j + fr;
+      if (m < M) {
+        const int32_t R = rowsum[m];
+        const float sc = scales[m] * al;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * WN + 32 * i + 8 * q + 4 * h;
+            if (n < N) {
+              v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              if constexpr (BITS == 4) a = a >> 4;  // exact: every product carries a factor 16
+              store4<OUT>(out, m * ldo + n, a, R, sc);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
+  };
+
+  if (ntiles == 0) return;
+  set_tile(0);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (stage_load(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, NST>{});
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * DPS) : "memory");
+  bar();
+  Head h0, h1;
+  Tail tl;
+  read_head(h0, std::integral_constant<int, 0>{});
+  // stage Q of a group of NST: buffer Q, heads h0 / h1 by parity
+  auto body = [&]<int Q>(std::integral_constant<int, Q>) {
+    Head& cur = (Q % 2 == 0) ? h0 : h1;
+    Head& nxt = (Q % 2 == 0) ? h1 : h0;
+    read_tail(tl, std::integral_constant<int, Q>{});
+    compute(cur.b, cur.a, 0, NSTEP / 2);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
+    bar();
+    stage_load(std::integral_constant<int, Q>{});
+    read_head(nxt, std::integral_constant<int, (Q + 1) % NST>{});
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur.b, tl.a, NSTEP / 2, NSTEP);
+  };
+  const int groups_per_tile = nk / NST;
+  for (int r = 0; r < ntiles; ++r) {
+    for (int gq = 0; gq < groups_per_tile; ++gq) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (body(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, NST>{});
+    }
+    epilogue(r);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -536,9 +820,26 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
                        rowsum, wp, alpha, (int)M, N, K, out, ldo);
     return hipGetLastError();
   }
-  // 256 x 256 tiles (8 waves of 128 x 64, one block per CU) when there are
-  // enough of them to fill the chip; otherwise 128 x 128 tiles (4 waves of
-  // 64 x 64, several blocks per CU).
+  if (K % 512 == 0) {
+    // persistent: one block per CU, 256 x 256 tiles when they fill the chip
+    const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int bn = g256 >= cu_count ? 256 : 128;
+    const int tm = (int)((M + 255) / 256), tn = (int)((N + bn - 1) / bn);
+    const int64_t G = (int64_t)tm * tn;
+    const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
+    const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
+    if (bn == 256) {
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
+                         wp, alpha, M, N, K, out, ldo, tm, tn);
+    } else {
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
+                         wp, alpha, M, N, K, out, ldo, tm, tn);
+    }
+    return hipGetLastError();
+  }
+  // Other K: 256 x 256 tiles (8 waves of 128 x 64, one block per CU) when
+  // there are enough of them to fill the chip; otherwise 128 x 128 tiles
+  // (4 waves of 64 x 64, several blocks per CU).
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= cu_count) {
     const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
