@@ -16,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhbl.so")
+PROBE = os.path.join(HERE, "peak_probe")  # stand-alone program: measured device peaks
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["k_quant.hip", "k_ternarize.hip", "k_gemm.hip", "hbl_api.cpp"]
@@ -66,6 +67,13 @@ def build(force: bool = False, verbose: bool = False) -> str:
         tmp = LIB + ".tmp"
         subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
         os.replace(tmp, LIB)
+    probe_src = os.path.join(CSRC, "peak_probe.hip")
+    if force or _stale(PROBE, [probe_src]):
+        cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], probe_src, "-o", PROBE + ".tmp"]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed on peak_probe.hip:\n" + r.stdout.decode(errors="replace"))
+        os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
