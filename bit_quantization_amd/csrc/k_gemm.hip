@@ -333,6 +333,12 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   constexpr int ASZ = BM * AROW, BSZ = BN * BROW;
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASZ], As1[ASZ], As2[ASZ], As3[ASZ];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
+  // bf16 outputs of 256 x 128 tiles are staged through LDS when it has room
+  // besides the stages (INT4); the 256 x 256 tile stores fragments directly
+  // (staging its 128-wide rows costs more registers than it saves)
+  constexpr int OROW = (BN / 2) * 2 + 16;  // bytes per staged output row of a wave
+  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (ASZ + BSZ) + 4 * 32 * OROW <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? 4 * 32 * OROW : 16];
   auto abuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return As0; else if constexpr (I == 1) return As1; else if constexpr (I == 2) return As2; else return As3;
   };
@@ -499,6 +505,51 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     int64_t m0, n0;
     tile_of(r, m0, n0);
     const float al = *alpha;
+    if constexpr (STAGE_OUT) {
+      // bf16 through LDS: for fragment row j the wave writes its 32 tokens x
+      // WN features to its own [32][WN] tile (rows padded by 16 bytes), then
+      // stores whole rows, 16 bytes per lane: far fewer and larger write
+      // requests than the fragments' 16-byte row pieces
+      uint8_t* const Ow = Os + wave * 32 * OROW;
+      constexpr int U = WN * 2 / 16;  // 16-byte units per staged row
+      const bool wide = (ldo & 7) == 0;
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * WM + 32 * j + fr;
+        const int32_t R = m < M ? rowsum[m] : 0;
+        const float sc = m < M ? scales[m] * al : 0.0f;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (BITS == 4) a = a >> 4;  // exact: every product carries a factor 16
+            const uint32_t lo = f32_to_bf16_rne(sc * (float)(a[0] - R)) | ((uint32_t)f32_to_bf16_rne(sc * (float)(a[1] - R)) << 16);
+            const uint32_t hi = f32_to_bf16_rne(sc * (float)(a[2] - R)) | ((uint32_t)f32_to_bf16_rne(sc * (float)(a[3] - R)) << 16);
+            *reinterpret_cast<uint2*>(Ow + fr * OROW + 2 * (32 * i + 8 * q + 4 * h)) = make_uint2(lo, hi);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one fragment's values live at a time
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is the wave's own: no barrier
+#pragma unroll
+        for (int pp = 0; pp < 32 * U / 64; ++pp) {
+          const int row = lane / U + (64 / U) * pp, u = lane % U;
+          const int64_t mm = m0 + wm * WM + 32 * j + row, nn = n0 + wn * WN + 8 * u;
+          const uint4 v = *reinterpret_cast<const uint4*>(Ow + row * OROW + 16 * u);
+          if (mm < M && nn < N) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(out) + mm * ldo + nn;
+            if (wide) {
+              *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+              reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+              reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+            }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next row's writes
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int64_t m = m0 + wm * WM + 32 * j + fr;
@@ -517,6 +568,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
             }
           }
       }
+    }
     }
 #pragma unroll
     for (int i = 0; i < FN; ++i)

@@ -175,6 +175,23 @@ def test_gemm_strided_output(hbl):
     assert np.all(o[:, N:] == -7), "wrote outside the output view"
 
 
+@pytest.mark.parametrize("pad", [4, 8])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_strided_bf16_output(hbl, pad, bits):
+    """bf16 outputs into a row-strided view (stride = N + pad elements), on
+    the persistent matmul path, equal the contiguous result; the padding
+    columns are untouched."""
+    M, N, K = 300, 256, 1024
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 31 + pad)
+    args = (_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(), torch.from_numpy(rowsum).cuda(),
+            torch.from_numpy(packed.view(np.int32)).cuda(), torch.tensor([alpha], dtype=torch.float32).cuda(), K)
+    ref = hbl.ternary_gemm(*args, out_dtype=hbl.OUT_BF16)
+    buf = torch.full((M, N + pad), -7.0, dtype=torch.bfloat16, device="cuda")
+    hbl.ternary_gemm(*args, out_dtype=hbl.OUT_BF16, out=buf[:, :N])
+    assert torch.equal(buf[:, :N].view(torch.int16), ref.view(torch.int16))
+    assert torch.all(buf[:, N:] == -7.0), "wrote outside the output view"
+
+
 # ---------------------------------------------------------- whole layer
 
 def test_forward_tiny_workload(hbl):
