@@ -303,7 +303,8 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 // Within stage kt the waves meet once, halfway through the MFMAs: past that
 // barrier every wave has read stage kt's buffer (so its refill may start)
 // and stage kt + 1 has landed (so its fragments may be read while the
-// second half of stage kt's MFMAs runs).  The barrier carries no memory
+// second half of stage kt's MFMAs runs).  Each MFMA step's operands are
+// widened during the previous step's MFMAs.  The barrier carries no memory
 // fence (a fence would wait for every load in flight, the prefetch
 // included); each wave has waited for its own loads of the stage first.
 //
@@ -458,39 +459,42 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
       for (int j = 0; j < FM; ++j) f.a[j][v] = *reinterpret_cast<const uint4*>(Ab + abase[HU + v] + AFRAG * j);
   };
-  // MFMA steps t0 .. t1 - 1 (both within one half) of a stage.  Weights
-  // widen from two bits to the bytes c = q + 1
-  // (word -> {w, w >> 2, w >> 4, w >> 6} & 0x03030303); INT4 codes to the
-  // bytes 16 q (low nibbles shifted up, high nibbles in place); INT8 codes
-  // are used as stored.
-  auto compute = [&](const uint4 (&bq)[FN], const uint4 (&aq)[FM][HU], int t0, int t1) {
+  // The operands of one MFMA step, widened: weights from two bits to the
+  // bytes c = q + 1 (word -> {w, w >> 2, w >> 4, w >> 6} & 0x03030303); INT4
+  // codes to the bytes 16 q (low nibbles shifted up, high nibbles in place);
+  // INT8 codes as stored.  Step t uses weight word t of the lane's unit and
+  // code unit t / 2 (INT4) or t (INT8) of its half of the stage.
+  struct Dec {
+    v4i bf[FN];
+    v4i af[FM];
+  };
+  auto decode = [&](Dec& d, const uint4 (&bq)[FN], const uint4 (&aq)[FM][HU], int t) {
 #pragma unroll
-    for (int t = t0; t < t1; ++t) {
-      v4i bf[FN];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const uint4 q = bq[i];
-        const uint32_t w = (t == 0) ? q.x : (t == 1) ? q.y : (t == 2) ? q.z : q.w;
-        bf[i] = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+    for (int i = 0; i < FN; ++i) {
+      const uint4 q = bq[i];
+      const uint32_t w = (t == 0) ? q.x : (t == 1) ? q.y : (t == 2) ? q.z : q.w;
+      d.bf[i] = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
                     (int)((w >> 6) & 0x03030303u)};
-      }
-      const int th = t % (NSTEP / 2);  // step within the half
+    }
+    const int th = t % (NSTEP / 2);  // step within the half (head or tail units)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        v4i af;
-        if constexpr (BITS == 4) {
-          const uint4 q = aq[j][th / 2];
-          const uint32_t x0 = (th % 2 == 0) ? q.x : q.z, x1 = (th % 2 == 0) ? q.y : q.w;
-          af = v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
-                   (int)(x1 & 0xf0f0f0f0u)};
-        } else {
-          const uint4 q = aq[j][th];
-          af = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-        }
-#pragma unroll
-        for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[i], af, acc[i][j], 0, 0, 0);
+    for (int j = 0; j < FM; ++j) {
+      if constexpr (BITS == 4) {
+        const uint4 q = aq[j][th / 2];
+        const uint32_t x0 = (th % 2 == 0) ? q.x : q.z, x1 = (th % 2 == 0) ? q.y : q.w;
+        d.af[j] = v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
+                      (int)(x1 & 0xf0f0f0f0u)};
+      } else {
+        const uint4 q = aq[j][th];
+        d.af[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
       }
     }
+  };
+  auto mfmas = [&](const Dec& d) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(d.bf[i], d.af[j], acc[i][j], 0, 0, 0);
   };
   auto bar = [] {
     asm volatile("" ::: "memory");
@@ -586,18 +590,28 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   Head h0, h1;
   Tail tl;
   read_head(h0, std::integral_constant<int, 0>{});
-  // stage Q of a group of NST: buffer Q, heads h0 / h1 by parity
+  // Stage Q of a group of NST: buffer Q, heads h0 / h1 by parity.  The
+  // operands of step t + 1 are widened while step t's MFMAs run (an MFMA
+  // whose operand was just written by the VALU waits for it).
+  static_assert(NSTEP == 4, "four MFMA steps per stage");
   auto body = [&]<int Q>(std::integral_constant<int, Q>) {
     Head& cur = (Q % 2 == 0) ? h0 : h1;
     Head& nxt = (Q % 2 == 0) ? h1 : h0;
     read_tail(tl, std::integral_constant<int, Q>{});
-    compute(cur.b, cur.a, 0, NSTEP / 2);
+    Dec d0, d1;
+    decode(d0, cur.b, cur.a, 0);
+    decode(d1, cur.b, cur.a, 1);
+    mfmas(d0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tail has landed
+    decode(d0, cur.b, tl.a, 2);
+    mfmas(d1);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
     bar();
     stage_load(std::integral_constant<int, Q>{});
     read_head(nxt, std::integral_constant<int, (Q + 1) % NST>{});
-    __builtin_amdgcn_sched_barrier(0);
-    compute(cur.b, tl.a, NSTEP / 2, NSTEP);
+    decode(d1, cur.b, tl.a, 3);
+    mfmas(d0);
+    mfmas(d1);
   };
   const int groups_per_tile = nk / NST;
   for (int r = 0; r < ntiles; ++r) {
