@@ -92,14 +92,63 @@ __device__ __forceinline__ int swz(int e) {
 // Reduction of one value over the T threads of a row.  Every thread of the
 // row gets the same bits: the xor-butterfly pairs the same partials on
 // both sides, and the cross-wave step combines the waves in a fixed order.
+// The value of lane l ^ o, for a butterfly over lane distances o = 1, 2, 4,
+// ... in that order.  Distances 1 and 2 are quad permutations; 4 and 8 are
+// the half-row and row mirrors (lane i <-> 7 - i, 15 - i), which pair each
+// lane with the other half of its group, equivalent to l ^ o once the
+// earlier steps have made every 4- (8-) lane group uniform; 16 and 32 go
+// through the LDS crossbar.  DPP moves cost one VALU slot instead of an
+// LDS round trip.
+template <int O>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (O == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  else if constexpr (O == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (O == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (O == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  else return __shfl_xor(v, O);
+}
+
+// Butterfly over the W lanes of a group: every lane ends with the same bits
+// (each step combines the same two values in either order).
+template <int W, bool IS_MAX>
+__device__ __forceinline__ float lanes_reduce(float v) {
+#define HBL_STEP(O)                                                   \
+  if constexpr (W > O) {                                              \
+    const float u = __int_as_float(lane_xor<O>(__float_as_int(v)));   \
+    v = IS_MAX ? fmaxf(v, u) : v + u;                                 \
+  }
+  HBL_STEP(1) HBL_STEP(2) HBL_STEP(4) HBL_STEP(8) HBL_STEP(16) HBL_STEP(32)
+#undef HBL_STEP
+  return v;
+}
+
+template <int W>
+__device__ __forceinline__ int lanes_reduce_int(int v) {
+#define HBL_STEP(O) \
+  if constexpr (W > O) v += lane_xor<O>(v);
+  HBL_STEP(1) HBL_STEP(2) HBL_STEP(4) HBL_STEP(8) HBL_STEP(16) HBL_STEP(32)
+#undef HBL_STEP
+  return v;
+}
+
+// Sum (or max) of |v[0..N)|, a pairwise tree (log2 N dependent steps).
+template <int N, bool IS_MAX>
+__device__ __forceinline__ float abs_tree(const float* v) {
+  static_assert(N >= 2 && (N & (N - 1)) == 0, "power of two");
+  float t[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) t[i] = IS_MAX ? fmaxf(fabsf(v[i]), fabsf(v[i + N / 2])) : fabsf(v[i]) + fabsf(v[i + N / 2]);
+#pragma unroll
+  for (int w = N / 4; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = IS_MAX ? fmaxf(t[i], t[i + w]) : t[i] + t[i + w];
+  return t[0];
+}
+
 template <int T, bool IS_MAX>
 __device__ __forceinline__ float row_reduce(float v, float* red, int row, int tid) {
   constexpr int W = T < 64 ? T : 64;
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) {
-    const float u = __shfl_xor(v, o);
-    v = IS_MAX ? fmaxf(v, u) : v + u;
-  }
+  v = lanes_reduce<W, IS_MAX>(v);
   if constexpr (T > 64) {
     constexpr int NW = T / 64;
     if ((tid & 63) == 0) red[row * NW + (tid >> 6)] = v;
@@ -118,8 +167,7 @@ __device__ __forceinline__ float row_reduce(float v, float* red, int row, int ti
 template <int T>
 __device__ __forceinline__ int row_reduce_int(int v, int* red, int row, int tid) {
   constexpr int W = T < 64 ? T : 64;
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  v = lanes_reduce_int<W>(v);
   if constexpr (T > 64) {
     constexpr int NW = T / 64;
     if ((tid & 63) == 0) red[row * NW + (tid >> 6)] = v;
@@ -235,9 +283,7 @@ k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
     return;
   } else {
     // row statistic: gamma = max|x_r| (INT8) or sum|x_r| (INT4, divided by K)
-    float st = 0.0f;
-#pragma unroll
-    for (int i = 0; i < E; ++i) st = (BITS == 8) ? fmaxf(st, fabsf(v[i])) : st + fabsf(v[i]);
+    float st = abs_tree<E, BITS == 8>(v);
     st = row_reduce<T, BITS == 8>(st, redf, row, tid);
     float f, s;
     if constexpr (BITS == 8) {
@@ -378,8 +424,10 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
       }
   }
 
-  uint4 raw[NL];
-  auto load_rows = [&](int64_t grp) {
+  // The next row group's input is loaded into the same registers as soon as
+  // the current one's have been consumed.
+  uint4 raw0[NL];
+  auto load_rows = [&](auto& raw, int64_t grp) {
     if constexpr (MFMA1) {
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
@@ -401,9 +449,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
     }
   };
 
-  int64_t grp = blockIdx.x;
-  load_rows(grp);
-  for (; grp < ngroups; grp += gridDim.x) {
+  auto row_group = [&](auto& raw, int64_t grp, int64_t refill) {
     const int64_t m = grp * RPB + row;
     const bool live = m < M;
     float v[64];
@@ -423,7 +469,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           for (int rb = 0; rb < 2; ++rb)
             acc[rb][cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hP[st & 1][rb * (st >> 1)], bx, acc[rb][cg], 0, 0, 0);
         }
-      load_rows(grp + gridDim.x);  // prefetch the next row group
+      load_rows(raw, refill);  // prefetch the next row group
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
         const int bc = mchunk(cg), r = bc / T, tc = bc % T;
@@ -457,7 +503,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           v[4 * q + 2] = __uint_as_float(raw[q].z); v[4 * q + 3] = __uint_as_float(raw[q].w);
         }
       }
-      load_rows(grp + gridDim.x);  // prefetch the next row group
+      load_rows(raw, refill);  // prefetch the next row group
       if constexpr (HAD) {
         butterflies<64, 0, 6>(v);
 #pragma unroll
@@ -524,9 +570,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
       }
       __syncthreads();
     } else {
-      float st = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) st = (BITS == 8) ? fmaxf(st, fabsf(v[i])) : st + fabsf(v[i]);
+      float st = abs_tree<64, BITS == 8>(v);
       st = row_reduce<T, BITS == 8>(st, redf, row, t);
       float f, s;
       if constexpr (BITS == 8) {
@@ -560,14 +604,14 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)b[3], (uint32_t)b[2], 0x04000c0cu);
         return p01 | p23;
       };
-      int qsum = 0;
+      int qs[4] = {0, 0, 0, 0};  // four independent row-sum chains
       if constexpr (!HAD) {
         // the thread's 64 elements are contiguous: pack and store directly
 #pragma unroll
         for (int gq = 0; gq < 8; ++gq) {
           const uint32_t w0 = quant4(v + 8 * gq), w1 = quant4(v + 8 * gq + 4);
-          qsum = __builtin_amdgcn_sdot4((int)w0, 0x01010101, qsum, false);
-          qsum = __builtin_amdgcn_sdot4((int)w1, 0x01010101, qsum, false);
+          qs[(2 * gq) % 4] = __builtin_amdgcn_sdot4((int)w0, 0x01010101, qs[(2 * gq) % 4], false);
+          qs[(2 * gq + 1) % 4] = __builtin_amdgcn_sdot4((int)w1, 0x01010101, qs[(2 * gq + 1) % 4], false);
           const int e0 = (t << 6) | (8 * gq);
           if (live) {
             if constexpr (BITS == 8) {
@@ -587,7 +631,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 #pragma unroll
         for (int gi = 0; gi < 16; ++gi) {
           const uint32_t w = quant4(v + 4 * gi);
-          qsum = __builtin_amdgcn_sdot4((int)w, 0x01010101, qsum, false);
+          qs[gi % 4] = __builtin_amdgcn_sdot4((int)w, 0x01010101, qs[gi % 4], false);
           const int e = last_e(gi);
           if constexpr (BITS == 8) {
             *reinterpret_cast<uint32_t*>(C8 + e) = w;
@@ -616,14 +660,23 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           }
         }
       }
-      qsum = row_reduce_int<T>(qsum, redi, row, t);
+      const int qsum = row_reduce_int<T>((qs[0] + qs[1]) + (qs[2] + qs[3]), redi, row, t);
       if (live && t == 0) {
-        scales[m] = s;
-        if (rowsum) rowsum[m] = qsum;
+        // the row index made opaque here, so that the store addresses are
+        // formed now from the base pointers rather than kept (and spilled)
+        // across the loop: a reload would wait for the prefetched rows
+        int64_t mi = m;
+        asm volatile("" : "+v"(mi));
+        scales[mi] = s;
+        if (rowsum) rowsum[mi] = qsum;
       }
       __syncthreads();  // LDS and reduction scratch are reused by the next row group
     }
-  }
+  };
+  const int64_t S = gridDim.x;
+  int64_t grp = blockIdx.x;
+  load_rows(raw0, grp);
+  for (; grp < ngroups; grp += S) row_group(raw0, grp, grp + S);
 }
 
 // Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
