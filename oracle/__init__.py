@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         _lib.hbo_fwht_f64.restype = I64
         _lib.hbo_hadamard.argtypes = [P, I, I64, I64, I64, P]
         _lib.hbo_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P]
+        _lib.hbo_norm_quantize.argtypes = [P, I, I64, I64, I64, P, I, I, P, P, P, P]
+        _lib.hbo_hadamard_backward.argtypes = [P, I, I64, I64, I64, P]
+        _lib.hbo_ternarize_rotated.argtypes = [P, I, I64, I64, P, P, P, P]
         _lib.hbo_ternarize.argtypes = [P, I, I64, I64, P, P, P]
         _lib.hbo_gemm_i32.argtypes = [P, I, P, I64, I64, I64, P]
         _lib.hbo_dequant_output.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
@@ -130,6 +133,51 @@ def quantize(x: np.ndarray, bits: int, hadamard: bool = True, want_xr: bool = Fa
                               _p(codes), _p(scales), _p(rowsum),
                               _p(xr) if want_xr else None), "quantize")
     return (codes, scales, rowsum, xr) if want_xr else (codes, scales, rowsum)
+
+
+def norm_quantize(x: np.ndarray, bits: int, gain: np.ndarray | None = None,
+                  hadamard: bool = True, want_xr: bool = False):
+    """RMSNorm (per-channel gain, None = ones), then the optional rotation, then
+    per-token quantisation: Eq. 9 with its normalisation layer.  Same returns
+    as quantize()."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float32)
+    if g is not None and g.shape != (K,):
+        raise ValueError("gain must have shape (K,)")
+    codes = np.empty((M, K), np.int8) if bits == 8 else np.empty((M, K // 8), np.uint32)
+    scales = np.empty(M, np.float32)
+    rowsum = np.empty(M, np.int32)
+    xr = np.empty((M, K), np.float32) if want_xr else None
+    _check(lib().hbo_norm_quantize(_p(x), _dtype_code(x), M, K, K, _p(g) if g is not None else None,
+                                   int(hadamard), bits, _p(codes), _p(scales), _p(rowsum),
+                                   _p(xr) if want_xr else None), "norm_quantize")
+    return (codes, scales, rowsum, xr) if want_xr else (codes, scales, rowsum)
+
+
+def hadamard_backward(dy: np.ndarray) -> np.ndarray:
+    """dX = H^T dY per row by the explicit transposed product (O(K^2) per
+    row), fp64 [M][K]."""
+    dy = np.ascontiguousarray(dy)
+    M, K = dy.shape
+    dx = np.empty((M, K), np.float64)
+    _check(lib().hbo_hadamard_backward(_p(dy), _dtype_code(dy), M, K, K, _p(dx)), "hadamard_backward")
+    return dx
+
+
+def ternarize_rotated(w: np.ndarray, want_wr: bool = False):
+    """Q_w(W H^T): rows of W rotated, then ternarised.  Returns (packed, alpha,
+    codes[, the rotated fp32 matrix])."""
+    w = np.ascontiguousarray(w)
+    N, K = w.shape
+    packed = np.empty((N, K // 16), np.uint32)
+    alpha = np.zeros(1, np.float32)
+    q = np.empty((N, K), np.int8)
+    wr = np.empty((N, K), np.float32) if want_wr else None
+    _check(lib().hbo_ternarize_rotated(_p(w), _dtype_code(w), N, K, _p(packed), _p(alpha), _p(q),
+                                       _p(wr) if want_wr else None), "ternarize_rotated")
+    out = (packed, np.float32(alpha[0]), q)
+    return out + (wr,) if want_wr else out
 
 
 def ternarize(w: np.ndarray):

@@ -207,15 +207,38 @@ void hbo_unpack_int4(const uint32_t *packed, int64_t M, int64_t K, int8_t *q) {
     }
 }
 
-/* X -> (codes, scales, rowsum).  With hadamard != 0 the row is first rotated
- * (X_r = Hadamard(X), Eq. 9 without the normalisation layer); with
- * hadamard == 0 it is quantised as is (plain BitLinear input).
+/* ------------------------------------------------------------------ */
+/* Normalisation layer of H-BitLinear  [BNv2 §3.4 "H-BitLinear: The    */
+/* Composite Layer", Eq. 9: X_r = Hadamard(LN(X)), LN = RMSNorm]       */
+/* ------------------------------------------------------------------ */
+
+/* RMSNorm of one row, in fp64: t[k] = x[k] * r * g[k] with
+ * r = 1 / sqrt(mean_j x[j]^2 + eps) and g the per-channel gain (NULL: a
+ * gain of one).  The pages name RMSNorm without printing it; this is the
+ * usual root-mean-square normalisation, with the library's eps. */
+static void rmsnorm_row_f64(const void *x, int x_dtype, int64_t off, int64_t K,
+                            const float *gain, double *t) {
+  double ss = 0.0;
+  for (int64_t k = 0; k < K; k++) {
+    double v = (double)load_elem(x, x_dtype, off + k);
+    t[k] = v;
+    ss += v * v;
+  }
+  const double r = 1.0 / sqrt(ss / (double)K + (double)HBO_EPS);
+  for (int64_t k = 0; k < K; k++) t[k] = t[k] * r * (gain ? (double)gain[k] : 1.0);
+}
+
+/* X -> (codes, scales, rowsum), optionally through the normalisation layer
+ * (norm != 0, gain nullable) and the rotation (hadamard != 0):
+ *   t   = norm ? RMSNorm(x) : x            (fp64, exact widening of x)
+ *   X_r = hadamard ? H t : t, rounded once to fp32
+ * then the quantiser of Eq. 7 or Eq. 8 on X_r.
  * codes: int8 [M][K] for bits = 8, uint32 [M][K/8] (INT4 layout) for bits = 4.
  * xr_out (nullable): the fp32 values that were quantised, [M][K].
  * Returns 0, or 2 for a bad shape / mode. */
-int hbo_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                 int hadamard, int bits, void *codes, float *scales,
-                 int32_t *rowsum, float *xr_out) {
+static int quantize_rows(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         int norm, const float *gain, int hadamard, int bits, void *codes,
+                         float *scales, int32_t *rowsum, float *xr_out) {
   if (M < 0 || K <= 0 || ldx < K || (bits != 8 && bits != 4)) return 2;
   if (hadamard && !is_pow2(K)) return 2;
   if (bits == 4 && K % 8 != 0) return 2;
@@ -227,12 +250,16 @@ int hbo_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
     int8_t *q = (int8_t *)malloc((size_t)K);
 #pragma omp for schedule(static)
     for (int64_t m = 0; m < M; m++) {
-      if (hadamard) {
+      if (norm) {
+        rmsnorm_row_f64(x, x_dtype, m * ldx, K, gain, t);
+      } else {
         for (int64_t k = 0; k < K; k++) t[k] = (double)load_elem(x, x_dtype, m * ldx + k);
+      }
+      if (hadamard) {
         hbo_fwht_f64(t, K);
         for (int64_t k = 0; k < K; k++) xr[k] = (float)(t[k] * scale);
       } else {
-        for (int64_t k = 0; k < K; k++) xr[k] = load_elem(x, x_dtype, m * ldx + k);
+        for (int64_t k = 0; k < K; k++) xr[k] = (float)t[k];
       }
       if (xr_out) memcpy(xr_out + m * K, xr, (size_t)K * sizeof(float));
       int32_t rs;
@@ -247,6 +274,60 @@ int hbo_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
     free(t);
     free(xr);
     free(q);
+  }
+  return 0;
+}
+
+/* Eq. 9 without the normalisation layer: with hadamard != 0 the row is
+ * rotated first (X_r = Hadamard(X)); with hadamard == 0 it is quantised as
+ * is (plain BitLinear input). */
+int hbo_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                 int hadamard, int bits, void *codes, float *scales,
+                 int32_t *rowsum, float *xr_out) {
+  return quantize_rows(x, x_dtype, M, K, ldx, 0, NULL, hadamard, bits, codes, scales, rowsum,
+                       xr_out);
+}
+
+/* Eq. 9 with its normalisation layer: X_r = Hadamard(RMSNorm(X)) (or
+ * RMSNorm(X) alone with hadamard == 0), then quantised. */
+int hbo_norm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                      const float *gain, int hadamard, int bits, void *codes, float *scales,
+                      int32_t *rowsum, float *xr_out) {
+  return quantize_rows(x, x_dtype, M, K, ldx, 1, gain, hadamard, bits, codes, scales, rowsum,
+                       xr_out);
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward of the rotation  [BNv2 §3.4 "Gradient Handling Through the */
+/* Hadamard Transformation", Eq. 10]                                   */
+/* ------------------------------------------------------------------ */
+
+/* dX = H^T dY row by row, written out as the transposed matrix product
+ * dx[k] = sum_j H[j][k] dy[j], with the entries of the normalised
+ * Sylvester matrix in closed form: H[j][k] = (-1)^popcount(j & k) / sqrt(K).
+ * O(K^2) per row on purpose: it does not use the fast transform, so it is
+ * an independent check of the claim that the backward is the forward
+ * transform again.  dx is fp64 [M][K]. */
+int hbo_hadamard_backward(const void *dy, int dy_dtype, int64_t M, int64_t K, int64_t lddy,
+                          double *dx) {
+  if (!is_pow2(K) || lddy < K || M < 0) return 2;
+  const double scale = 1.0 / sqrt((double)K);
+#pragma omp parallel
+  {
+    double *g = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+      for (int64_t j = 0; j < K; j++) g[j] = (double)load_elem(dy, dy_dtype, m * lddy + j);
+      for (int64_t k = 0; k < K; k++) {
+        double s = 0.0;
+        for (int64_t j = 0; j < K; j++) {
+          const double h = (__builtin_popcountll((unsigned long long)(j & k)) & 1) ? -1.0 : 1.0;
+          s += h * g[j];
+        }
+        dx[m * K + k] = s * scale;
+      }
+    }
+    free(g);
   }
   return 0;
 }
@@ -306,6 +387,28 @@ int hbo_ternarize(const void *w, int w_dtype, int64_t N, int64_t K,
   free(q);
   *alpha = a;
   return 0;
+}
+
+/* Weight and activation rotation  [BNv2 §3.4 "Ablation Study: Why
+ * Activation-Only Hadamard Transformation", Table 5]: the ternarised matrix
+ * is Q_w(W H^T).  Row n of W H^T is H applied to row n of W (H is
+ * symmetric); each row is rotated in fp64 (the transform of Eq. 3-6),
+ * rounded once to fp32, and the fp32 matrix is ternarised as by
+ * hbo_ternarize.  wr_out (nullable) receives that fp32 matrix [N][K]. */
+int hbo_ternarize_rotated(const void *w, int w_dtype, int64_t N, int64_t K, uint32_t *packed,
+                          float *alpha, int8_t *q_out, float *wr_out) {
+  if (N <= 0 || K < 16 || !is_pow2(K)) return 2;
+  double *y = (double *)malloc((size_t)(N * K) * sizeof(double));
+  float *wr = (float *)malloc((size_t)(N * K) * sizeof(float));
+  int rc = hbo_hadamard(w, w_dtype, N, K, K, y);
+  if (rc == 0) {
+    for (int64_t i = 0; i < N * K; i++) wr[i] = (float)y[i];
+    rc = hbo_ternarize(wr, HBO_F32, N, K, packed, alpha, q_out);
+    if (rc == 0 && wr_out) memcpy(wr_out, wr, (size_t)(N * K) * sizeof(float));
+  }
+  free(y);
+  free(wr);
+  return rc;
 }
 
 /* ------------------------------------------------------------------ */

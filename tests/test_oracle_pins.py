@@ -346,3 +346,149 @@ def test_dequant_output_bf16_rounding():
     np.testing.assert_allclose(y64[0], [0.05, -0.15, 50.0, 0.0], rtol=1e-7)
     np.testing.assert_array_equal(workloads.bf16_to_f32(yb)[0],
                                   workloads.bf16_to_f32(workloads.bf16_bits(y64.astype(np.float32)))[0])
+
+
+# ------------------------------------------- normalisation layer (Eq. 9 LN)
+# Reading: RMSNorm y_k = x_k / sqrt(mean_j x_j^2 + eps) * g_k (the pages name
+# RMSNorm without a formula).  Pins: hand-worked cases; the closed form of the
+# output's mean square; scale invariance; the gain is elementwise; the codes
+# of a normalised row equal those of the raw row (the quantisers are scale
+# invariant up to eps), with the scale divided by the row's RMS.
+
+def test_golden_rmsnorm_cases():
+    _, kv = read_golden("rmsnorm_cases.txt")
+    f = lambda key: np.array([float(v) for v in kv[key]])
+    x1 = f("c1.x").astype(np.float32)[None]
+    _, _, _, y1 = oracle.norm_quantize(x1, 8, hadamard=False, want_xr=True)
+    np.testing.assert_allclose(y1[0], f("c1.y"), rtol=1e-7, atol=0)
+    x2 = f("c2.x").astype(np.float32)[None]
+    g2 = f("c2.g").astype(np.float32)
+    _, _, _, y2 = oracle.norm_quantize(x2, 8, gain=g2, hadamard=False, want_xr=True)
+    np.testing.assert_allclose(y2[0], f("c2.y"), rtol=1e-7, atol=0)
+    codes, scales, rowsum = oracle.norm_quantize(x1, 8, hadamard=True)
+    assert codes[0].tolist() == [int(v) for v in kv["c3.codes"]]
+    assert abs(float(scales[0]) - float(kv["c3.scale"][0])) <= 1e-9
+    assert int(rowsum[0]) == int(kv["c3.rowsum"][0])
+
+
+@pytest.mark.parametrize("n", [64, 1024, 16384])
+def test_rmsnorm_mean_square_closed_form(n):
+    rng = np.random.default_rng(100 + n)
+    # rows of very different magnitudes; the mean square of the output is
+    # ms / (ms + eps) exactly (before the fp32 rounding)
+    x = (rng.standard_normal((4, n)) * np.array([[1e-3], [0.1], [1.0], [30.0]])).astype(np.float32)
+    _, _, _, y = oracle.norm_quantize(x, 8, hadamard=False, want_xr=True)
+    ms = (x.astype(np.float64) ** 2).mean(axis=1)
+    want = ms / (ms + float(oracle.EPS))
+    got = (y.astype(np.float64) ** 2).mean(axis=1)
+    np.testing.assert_allclose(got, want, rtol=1e-6)
+    # with the rotation the row's L2 norm is unchanged (H orthogonal)
+    _, _, _, yr = oracle.norm_quantize(x, 8, hadamard=True, want_xr=True)
+    np.testing.assert_allclose((yr.astype(np.float64) ** 2).mean(axis=1), want, rtol=1e-6)
+
+
+def test_rmsnorm_scale_invariance_and_elementwise_gain():
+    n = 4096
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((3, n)) * 5).astype(np.float32)
+    g = rng.uniform(-2, 2, n).astype(np.float32)
+    _, _, _, y = oracle.norm_quantize(x, 8, hadamard=False, want_xr=True)
+    _, _, _, y4 = oracle.norm_quantize(np.float32(4.0) * x, 8, hadamard=False, want_xr=True)
+    # ms >> eps: scaling the row by 4 changes the output by < 1e-6 relative
+    np.testing.assert_allclose(y4, y, rtol=2e-6, atol=0)
+    _, _, _, yg = oracle.norm_quantize(x, 8, gain=g, hadamard=False, want_xr=True)
+    np.testing.assert_allclose(yg, y.astype(np.float64) * g, rtol=2e-7, atol=0)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_rmsnorm_codes_match_raw_codes(bits):
+    # RMSNorm without gain multiplies each row by one positive factor; the
+    # quantisers divide by the row statistic, so the codes are those of the
+    # raw row except where eps moves a value across a rounding boundary, and
+    # the scale is divided by the row's RMS
+    n = 4096
+    rng = np.random.default_rng(11 + bits)
+    x = (rng.standard_t(3, (16, n)) * 3).astype(np.float32)
+    c0, s0, r0 = oracle.quantize(x, bits, hadamard=True)
+    c1, s1, r1 = oracle.norm_quantize(x, bits, hadamard=True)
+    q0 = oracle.codes_int8(c0, bits, n).astype(int)
+    q1 = oracle.codes_int8(c1, bits, n).astype(int)
+    diff = q0 != q1
+    assert np.abs(q0 - q1).max() <= 1
+    assert diff.mean() <= 1e-3
+    rms = np.sqrt((x.astype(np.float64) ** 2).mean(axis=1) + float(oracle.EPS))
+    np.testing.assert_allclose(s1.astype(np.float64) * rms, s0, rtol=1e-5)
+
+
+# ------------------------------------------- Hadamard backward (Eq. 10)
+
+@pytest.mark.parametrize("m", [1, 3, 6])
+def test_hadamard_backward_equals_autograd(m):
+    # dL/dX of L = <G, H X> by torch autograd through an explicit matrix
+    # built from the Sylvester recursion (an independent route)
+    import torch
+    n = 1 << m
+    h = torch.tensor(sylvester(m) / math.sqrt(n), dtype=torch.float64)
+    rng = np.random.default_rng(m)
+    x = torch.tensor(rng.standard_normal((4, n)), dtype=torch.float64, requires_grad=True)
+    g = rng.standard_normal((4, n)).astype(np.float32)
+    loss = ((x @ h.T) * torch.tensor(g, dtype=torch.float64)).sum()
+    loss.backward()
+    got = oracle.hadamard_backward(g)
+    np.testing.assert_allclose(got, x.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [256, 2048])
+def test_hadamard_backward_is_adjoint_and_equals_forward(n):
+    rng = np.random.default_rng(n + 3)
+    x = rng.standard_normal((3, n)).astype(np.float32)
+    g = rng.standard_normal((3, n)).astype(np.float32)
+    dx = oracle.hadamard_backward(g)
+    # <H x, g> = <x, H^T g> row by row
+    lhs = (oracle.hadamard(x) * g.astype(np.float64)).sum(axis=1)
+    rhs = (x.astype(np.float64) * dx).sum(axis=1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-10)
+    # H^T = H: the backward is the forward transform (the claim of Eq. 10)
+    np.testing.assert_allclose(dx, oracle.hadamard(g), rtol=0, atol=1e-10)
+    want = g.astype(np.float64) @ (scipy.linalg.hadamard(n) / math.sqrt(n))
+    np.testing.assert_allclose(dx, want, rtol=0, atol=1e-10)
+
+
+# ------------------------------------------- weight + activation rotation
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_rotated_weights_equal_w_times_h_transpose(m):
+    n = 1 << m
+    rng = np.random.default_rng(20 + m)
+    w = (rng.standard_normal((8, n)) * 0.02).astype(np.float32)
+    packed, alpha, q, wr = oracle.ternarize_rotated(w, want_wr=True)
+    want = w.astype(np.float64) @ (sylvester(m).T / math.sqrt(n))
+    np.testing.assert_allclose(wr, want, rtol=1e-6, atol=1e-9)
+    p2, a2, q2 = oracle.ternarize(wr)
+    assert np.array_equal(q, q2) and np.array_equal(packed, p2) and alpha == a2
+
+
+def test_rotation_cancels_between_weights_and_activations():
+    # (W H^T)(H x) = W x: the variant computes the same unquantised product
+    n = 1024
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal((16, n)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((4, n)).astype(np.float32)
+    _, _, _, wr = oracle.ternarize_rotated(w, want_wr=True)
+    got = oracle.hadamard(x) @ wr.astype(np.float64).T
+    want = x.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-6 * np.abs(want).max())
+    # rotating the rotated rows again gives W back (H H = I)
+    back = oracle.hadamard(wr)
+    np.testing.assert_allclose(back, w, rtol=0, atol=1e-7)
+
+
+def test_rotated_gaussian_weights_statistics():
+    # rows of iid N(0, s^2) stay iid N(0, s^2) under an orthogonal rotation:
+    # alpha = s sqrt(2/pi), zero fraction P(|z| < 0.5 sqrt(2/pi))
+    n, s = 4096, workloads.W_STD
+    w = workloads.gaussian_weights(41, 0, 256, n)
+    _, alpha, q = oracle.ternarize_rotated(w)
+    assert abs(alpha / (s * math.sqrt(2 / math.pi)) - 1) < 3e-3
+    p0 = 2 * norm.cdf(0.5 * math.sqrt(2 / math.pi)) - 1
+    assert abs((q == 0).mean() - p0) < 3e-3
