@@ -53,6 +53,11 @@ _SIGS = {
     "hbl_ternary_gemm": ([_P, _I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
     "hbl_forward_workspace_size": ([_I64, _I64, _I], _SZ),
     "hbl_forward": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
+    "hbl_hadamard_backward_f32": ([_P, _I, _I64, _I64, _I64, _P, _P], _I),
+    "hbl_norm_hadamard_quant": ([_P, _I, _I64, _I64, _I64, _P, _I, _I, _P, _P, _P, _P], _I),
+    "hbl_norm_forward": ([_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
+    "hbl_ternarize_rotated_workspace_size": ([_I64, _I64], _SZ),
+    "hbl_ternarize_weights_rotated": ([_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -125,6 +130,37 @@ def ternarize_weights(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     return packed, alpha
 
 
+def ternarize_weights_rotated(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Q_w(W H^T), the weight side of the weight-and-activation rotation
+    variant (Table 5): rows of W rotated, then ternarised.  Returns (packed,
+    alpha) as ternarize_weights."""
+    w = w.contiguous()
+    N, K = w.shape
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=w.device)
+    alpha = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = torch.empty(max(1, _lib.hbl_ternarize_rotated_workspace_size(N, K)), dtype=torch.uint8, device=w.device)
+    _check(_lib.hbl_ternarize_weights_rotated(_ptr(w), _x_dtype(w), N, K, _ptr(packed), _ptr(alpha), _ptr(ws),
+                                              ws.numel(), _stream()), "hbl_ternarize_weights_rotated")
+    return packed, alpha
+
+
+def hadamard_backward_f32(dy: torch.Tensor) -> torch.Tensor:
+    """dL/dx = H^T dL/d(Hx) per row (Eq. 10), fp32 [M][K]."""
+    M, K, ld = _rows(dy)
+    dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    _check(_lib.hbl_hadamard_backward_f32(_ptr(dy), _x_dtype(dy), M, K, ld, _ptr(dx), _stream()),
+           "hbl_hadamard_backward_f32")
+    return dx
+
+
+def _gain(gain: torch.Tensor | None, K: int) -> int | None:
+    if gain is None:
+        return None
+    if gain.dtype != torch.float32 or gain.shape != (K,) or not gain.is_contiguous():
+        raise ValueError("gain must be a contiguous float32 tensor of shape (K,)")
+    return _ptr(gain)
+
+
 def hadamard_f32(x: torch.Tensor) -> torch.Tensor:
     """Row-wise normalised Hadamard rotation (Eq. 3-6), fp32 [M][K]."""
     M, K, ldx = _rows(x)
@@ -150,6 +186,20 @@ def hadamard_quant(x: torch.Tensor, bits: int, hadamard: bool = True):
     _check(_lib.hbl_hadamard_quant(_ptr(x), _x_dtype(x), M, K, ldx, HADAMARD if hadamard else 0, bits,
                                    _ptr(codes), _ptr(scales), _ptr(rowsum), _stream()),
            "hbl_hadamard_quant")
+    return codes, scales, rowsum
+
+
+def norm_hadamard_quant(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, hadamard: bool = True):
+    """hadamard_quant after the RMSNorm layer of Eq. 9 (per-channel gain,
+    None for one).  Same returns as hadamard_quant."""
+    M, K, ldx = _rows(x)
+    shape, dt = codes_shape(M, K, bits)
+    codes = torch.empty(shape, dtype=dt, device=x.device)
+    scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    _check(_lib.hbl_norm_hadamard_quant(_ptr(x), _x_dtype(x), M, K, ldx, _gain(gain, K),
+                                        HADAMARD if hadamard else 0, bits, _ptr(codes), _ptr(scales),
+                                        _ptr(rowsum), _stream()), "hbl_norm_hadamard_quant")
     return codes, scales, rowsum
 
 
@@ -188,4 +238,20 @@ def forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: in
     _check(_lib.hbl_forward(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, bits,
                             _ptr(packed), _ptr(alpha), _ptr(out), out.stride(0), _ptr(workspace),
                             workspace.numel(), _stream()), "hbl_forward")
+    return out
+
+
+def norm_forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: int,
+                 gain: torch.Tensor | None = None, hadamard: bool = True, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """forward with the RMSNorm layer of Eq. 9 in front: bf16 [M][N]."""
+    M, K, ldx = _rows(x)
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = forward_workspace(M, K, bits, x.device)
+    _check(_lib.hbl_norm_forward(_ptr(x), _x_dtype(x), M, K, ldx, _gain(gain, K), N,
+                                 HADAMARD if hadamard else 0, bits, _ptr(packed), _ptr(alpha), _ptr(out),
+                                 out.stride(0), _ptr(workspace), workspace.numel(), _stream()), "hbl_norm_forward")
     return out

@@ -101,6 +101,67 @@ size_t codes_bytes(int64_t M, int64_t K, int bits) {
   return bits == 8 ? (size_t)(M * K) : (size_t)(M * (K / 2));
 }
 
+// codes, then scales, then row sums, each on a 256-byte boundary
+size_t codes_region(int64_t M, int64_t K, int bits) {
+  return round256(codes_bytes(M, K, bits)) + 2 * round256(sizeof(float) * (size_t)M);
+}
+
+int check_gain(const float* gain) {
+  if (!aligned16(gain)) return fail(HBL_ERR_ALIGN, "gain is not 16-byte aligned");
+  return HBL_OK;
+}
+
+int quant_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, bool norm, const float* gain,
+               int flags, int bits, void* codes, float* scales, int32_t* rowsum, void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_bits(bits);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (!rc && norm) rc = check_gain(gain);
+  if (rc) return rc;
+  if (M > 0 && (!codes || !scales)) return fail(HBL_ERR_NULL, "codes and scales must be non-NULL");
+  if (!aligned16(codes) || !aligned4(scales) || !aligned4(rowsum))
+    return fail(HBL_ERR_ALIGN, "codes must be 16-byte aligned, scales and rowsum 4-byte aligned");
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
+                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum, norm,
+                                            gain, cu_count_cached(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  return HBL_OK;
+}
+
+int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, bool norm, const float* gain,
+                 int64_t N, int flags, int bits, const uint32_t* w_packed, const float* alpha, void* y,
+                 int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_bits(bits);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (!rc) rc = check_gemm_shape(M, N, K, ldy);
+  if (!rc && norm) rc = check_gain(gain);
+  if (rc) return rc;
+  if (M == 0) return HBL_OK;
+  if (!w_packed || !alpha || !y) return fail(HBL_ERR_NULL, "w_packed, alpha and y must be non-NULL");
+  if (!aligned16(w_packed) || !aligned16(y) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "w_packed and y must be 16-byte aligned");
+  const size_t need = codes_region(M, K, bits);
+  if (!ws || ws_bytes < need)
+    return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
+  if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  void* codes = base;
+  float* scales = reinterpret_cast<float*>(base + round256(codes_bytes(M, K, bits)));
+  int32_t* rowsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scales) + round256(sizeof(float) * (size_t)M));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
+                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum, norm, gain,
+                                            cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy,
+                               cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return HBL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,19 +232,19 @@ int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K, int64_t l
 
 int hbl_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int flags,
                        int bits, void* codes, float* scales, int32_t* rowsum, void* stream) {
-  g_last_error.clear();
-  int rc = check_flags(flags);
-  if (!rc) rc = check_bits(bits);
-  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
-  if (rc) return rc;
-  if (M > 0 && (!codes || !scales)) return fail(HBL_ERR_NULL, "codes and scales must be non-NULL");
-  if (!aligned16(codes) || !aligned4(scales) || !aligned4(rowsum))
-    return fail(HBL_ERR_ALIGN, "codes must be 16-byte aligned, scales and rowsum 4-byte aligned");
-  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
-                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum,
-                                            cu_count_cached(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "quantise launch");
-  return HBL_OK;
+  return quant_impl(x, x_dtype, M, K, ldx, false, nullptr, flags, bits, codes, scales, rowsum, stream);
+}
+
+int hbl_norm_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                            const float* gain, int flags, int bits, void* codes, float* scales,
+                            int32_t* rowsum, void* stream) {
+  return quant_impl(x, x_dtype, M, K, ldx, true, gain, flags, bits, codes, scales, rowsum, stream);
+}
+
+int hbl_hadamard_backward_f32(const void* dy, int dy_dtype, int64_t M, int64_t K, int64_t lddy, float* dx,
+                              void* stream) {
+  // H is symmetric and orthogonal: the backward is the forward transform
+  return hbl_hadamard_f32(dy, dy_dtype, M, K, lddy, dx, stream);
 }
 
 int hbl_ternary_gemm(const void* codes, int bits, const float* scales, const int32_t* rowsum,
@@ -210,38 +271,51 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales, const int
 
 size_t hbl_forward_workspace_size(int64_t M, int64_t K, int bits) {
   if (M < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
-  return round256(codes_bytes(M, K, bits)) + 2 * round256(sizeof(float) * (size_t)M);
+  return codes_region(M, K, bits);
 }
 
 int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
                 int bits, const uint32_t* w_packed, const float* alpha, void* y, int64_t ldy, void* ws,
                 size_t ws_bytes, void* stream) {
+  return forward_impl(x, x_dtype, M, K, ldx, false, nullptr, N, flags, bits, w_packed, alpha, y, ldy, ws,
+                      ws_bytes, stream);
+}
+
+int hbl_norm_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const float* gain,
+                     int64_t N, int flags, int bits, const uint32_t* w_packed, const float* alpha, void* y,
+                     int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(x, x_dtype, M, K, ldx, true, gain, N, flags, bits, w_packed, alpha, y, ldy, ws, ws_bytes,
+                      stream);
+}
+
+size_t hbl_ternarize_rotated_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return round256(sizeof(float) * (size_t)N * (size_t)K) + hbl_ternarize_workspace_size(N, K);
+}
+
+int hbl_ternarize_weights_rotated(const void* w, int w_dtype, int64_t N, int64_t K, uint32_t* w_packed,
+                                  float* alpha, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  int rc = check_flags(flags);
-  if (!rc) rc = check_bits(bits);
-  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
-  if (!rc) rc = check_gemm_shape(M, N, K, ldy);
-  if (rc) return rc;
-  if (M == 0) return HBL_OK;
-  if (!w_packed || !alpha || !y) return fail(HBL_ERR_NULL, "w_packed, alpha and y must be non-NULL");
-  if (!aligned16(w_packed) || !aligned16(y) || !aligned4(alpha))
-    return fail(HBL_ERR_ALIGN, "w_packed and y must be 16-byte aligned");
-  const size_t need = hbl_forward_workspace_size(M, K, bits);
+  if (w_dtype != HBL_DTYPE_F32 && w_dtype != HBL_DTYPE_BF16)
+    return fail(HBL_ERR_MODE, "w_dtype %d is neither HBL_DTYPE_F32 nor HBL_DTYPE_BF16", w_dtype);
+  if (N < 1 || N > (int64_t)INT_MAX || !is_pow2(K) || K < 16 || K > HBL_MAX_K)
+    return fail(HBL_ERR_SHAPE, "need N >= 1 and K a power of two in [16, %d] (N = %lld, K = %lld)", HBL_MAX_K,
+                (long long)N, (long long)K);
+  if (!w || !w_packed || !alpha) return fail(HBL_ERR_NULL, "w, w_packed and alpha must be non-NULL");
+  if (!aligned16(w) || !aligned16(w_packed) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "w and w_packed must be 16-byte aligned, alpha 4-byte aligned");
+  const size_t need = hbl_ternarize_rotated_workspace_size(N, K);
   if (!ws || ws_bytes < need)
     return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
   if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
-  char* base = static_cast<char*>(ws);
-  void* codes = base;
-  float* scales = reinterpret_cast<float*>(base + round256(codes_bytes(M, K, bits)));
-  int32_t* rowsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scales) + round256(sizeof(float) * (size_t)M));
+  float* wr = static_cast<float*>(ws);
+  double* partials = reinterpret_cast<double*>(static_cast<char*>(ws) + round256(sizeof(float) * (size_t)N * (size_t)K));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx,
-                                            (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum,
-                                            cu_count_cached(), s);
-  if (e != hipSuccess) return hip_fail(e, "quantise launch");
-  e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy,
-                               cu_count_cached(), s);
-  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  // rows of W H^T are the rows of W rotated (H is symmetric)
+  hipError_t e = hbl::launch_hadamard_f32(w, w_dtype == HBL_DTYPE_BF16, N, (int)K, K, wr, cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "hadamard launch");
+  e = hbl::launch_ternarize(wr, false, N, K, w_packed, alpha, partials, hbl::ternarize_partials(N, K), s);
+  if (e != hipSuccess) return hip_fail(e, "ternarize launch");
   return HBL_OK;
 }
 

@@ -9,9 +9,11 @@ namespace hbl {
 // Launchers.  Each validates nothing (the C-ABI layer has done that) and
 // returns the hipError_t of the launch.
 // cu_count: compute units of the device (sizes persistent grids).
+// norm: RMSNorm of each row (per-channel gain, nullable) before the rotation.
 hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K,
                                  int64_t ldx, bool hadamard, int bits,
                                  void* codes, float* scales, int32_t* rowsum,
+                                 bool norm, const float* gain,
                                  int cu_count, hipStream_t s);
 hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K,
                                int64_t ldx, float* y, int cu_count, hipStream_t s);

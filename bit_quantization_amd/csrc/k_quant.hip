@@ -145,6 +145,20 @@ __device__ __forceinline__ float abs_tree(const float* v) {
   return t[0];
 }
 
+// Sum of squares of v[0..N) as a pairwise tree (products rounded, then
+// added; no fused multiply-add).
+template <int N>
+__device__ __forceinline__ float sq_tree(const float* v) {
+  float a[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) a[i] = v[i] * v[i] + v[i + N / 2] * v[i + N / 2];
+#pragma unroll
+  for (int w = N / 4; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) a[i] = a[i] + a[i + w];
+  return a[0];
+}
+
 template <int T, bool IS_MAX>
 __device__ __forceinline__ float row_reduce(float v, float* red, int row, int tid) {
   constexpr int W = T < 64 ? T : 64;
@@ -180,6 +194,30 @@ __device__ __forceinline__ int row_reduce_int(int v, int* red, int row, int tid)
   return v;
 }
 
+// Normalisation layer of H-BitLinear (RMSNorm, Eq. 9): the row's values
+// become v * r * g with r = 1 / sqrt(mean of the squares + eps) and g the
+// per-channel gain (NULL: one).  ss is this thread's partial sum of squares;
+// the row total is reduced through red (a buffer of its own, so that the
+// statistic's reduction later in the row needs no extra barrier).  ge(i) is
+// the element index of v[i].
+template <int T, int N, typename GE>
+__device__ __forceinline__ void rmsnorm_apply(float* v, float ss, float kf, const float* __restrict__ gain,
+                                              float* red, int row, int tid, GE ge) {
+  ss = row_reduce<T, false>(ss, red, row, tid);
+  const float r = 1.0f / __builtin_sqrtf(ss / kf + kEps);
+  if (gain) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 g = *reinterpret_cast<const float4*>(gain + ge(i));
+      v[i] = (v[i] * r) * g.x; v[i + 1] = (v[i + 1] * r) * g.y;
+      v[i + 2] = (v[i + 2] * r) * g.z; v[i + 3] = (v[i + 3] * r) * g.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = v[i] * r;
+  }
+}
+
 template <int LOG2K>
 struct Geom {
   static constexpr int K = 1 << LOG2K;
@@ -193,12 +231,14 @@ struct Geom {
   static constexpr int RED = RPB * (T > 64 ? T / 64 : 1);
 };
 
-// OUT: 0 = codes (BITS 8 or 4), 1 = fp32 rotated values.
-template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+// OUT: 0 = codes (BITS 8 or 4), 1 = fp32 rotated values.  NORM: the row
+// goes through the RMSNorm layer (gain nullable) before the rotation.
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 __global__ void __launch_bounds__(Geom<LOG2K>::THREADS)
 k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
              void* __restrict__ codes, float* __restrict__ scales,
-             int32_t* __restrict__ rowsum, float* __restrict__ yout) {
+             int32_t* __restrict__ rowsum, float* __restrict__ yout,
+             const float* __restrict__ gain) {
   using G = Geom<LOG2K>;
   constexpr int K = G::K, E = G::E, T = G::T, TL = G::TL, EL = G::EL, NC = G::NC;
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -206,6 +246,7 @@ k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
   __shared__ __attribute__((aligned(16))) float lds[HAD ? G::RPB * K : 4];
   __shared__ float redf[G::RED];
   __shared__ int redi[G::RED];
+  __shared__ float redn[NORM ? G::RED : 1];
 
   const int row = threadIdx.x / T;
   const int tid = threadIdx.x % T;
@@ -228,6 +269,9 @@ k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
       }
     }
   }
+  if constexpr (NORM)
+    rmsnorm_apply<T, E>(v, sq_tree<E>(v), (float)K, gain, redn, row, tid,
+                        [&](int i) { return ((i >> 3) << (3 + TL)) | (tid << 3) | (i & 7); });
 
   if constexpr (HAD) {
     // stages of the lo and hi bits: every register bit
@@ -373,19 +417,23 @@ __device__ __forceinline__ int swz16(int e) {  // float index -> swizzled float 
 // layout (lane l holds 8 consecutive elements of chunk l % 32 of its column
 // group), and the result is written to LDS as groups of 4 consecutive
 // elements, in the same swizzled layout as the register path.
-template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 __global__ void __launch_bounds__(256, 2)
 k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
                void* __restrict__ codes, float* __restrict__ scales,
-               int32_t* __restrict__ rowsum, float* __restrict__ yout) {
+               int32_t* __restrict__ rowsum, float* __restrict__ yout,
+               const float* __restrict__ gain) {
   using G = G64<LOG2K>;
   constexpr int K = G::K, T = G::T, RPB = G::RPB, A3 = G::A3, EX = G::EX;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int NL = BF16 ? 8 : 16;  // 16-byte loads per thread
-  constexpr bool MFMA1 = BF16 && HAD;
+  // the matrix-core first pass needs the bf16 inputs themselves as operands;
+  // normalised rows take the register path
+  constexpr bool MFMA1 = BF16 && HAD && !NORM;
   __shared__ __attribute__((aligned(16))) float lds[RPB * K];
   __shared__ float redf[RPB * (T > 64 ? T / 64 : 1)];
   __shared__ int redi[RPB * (T > 64 ? T / 64 : 1)];
+  __shared__ float redn[NORM ? RPB * (T > 64 ? T / 64 : 1) : 1];
 
   const int row = threadIdx.x / T;
   const int t = threadIdx.x % T;
@@ -503,6 +551,11 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           v[4 * q + 2] = __uint_as_float(raw[q].z); v[4 * q + 3] = __uint_as_float(raw[q].w);
         }
       }
+      // with the normalisation the prefetch is issued after it: the gain
+      // and the prefetched rows would not both fit in registers
+      if constexpr (NORM)
+        rmsnorm_apply<T, 64>(v, sq_tree<64>(v), (float)K, gain, redn, row, t,
+                             [&](int i) { return (t << 6) | i; });
       load_rows(raw, refill);  // prefetch the next row group
       if constexpr (HAD) {
         butterflies<64, 0, 6>(v);
@@ -681,15 +734,16 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 
 // Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
 // per block of 256 threads, each holding up to 8 chunks of 8 elements.
-template <bool BF16, int BITS>
+template <bool BF16, int BITS, bool NORM>
 __global__ void __launch_bounds__(256)
 k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
               void* __restrict__ codes, float* __restrict__ scales,
-              int32_t* __restrict__ rowsum) {
+              int32_t* __restrict__ rowsum, const float* __restrict__ gain) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int CH = 8;
   __shared__ float redf[4];
   __shared__ int redi[4];
+  __shared__ float redn[4];
   const int tid = threadIdx.x;
   const int64_t m = blockIdx.x;
   const int nchunk = K / 8;
@@ -704,6 +758,12 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[8 * c + j] = 0.0f;
     }
+  }
+  if constexpr (NORM) {
+    // chunks past the row end are zero and hold a zero gain index: clamp it
+    rmsnorm_apply<256, CH * 8>(v, sq_tree<CH * 8>(v), (float)K, gain, redn, 0, tid,
+                               [&](int i) { const int ch = tid + 256 * (i >> 3);
+                                            return (ch < nchunk ? 8 * ch : 0) + (i & 7); });
   }
   float st = 0.0f;
 #pragma unroll
@@ -751,36 +811,38 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
   }
 }
 
-template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 hipError_t launch_fq64(const void* x, int64_t M, int64_t ldx, void* codes, float* scales, int32_t* rowsum,
-                       float* y, int cu_count, hipStream_t s) {
+                       float* y, const float* gain, int cu_count, hipStream_t s) {
   using G = G64<LOG2K>;
   const int64_t groups = (M + G::RPB - 1) / G::RPB;
   const int64_t cap = 2 * (int64_t)(cu_count > 0 ? cu_count : 256);  // two blocks fit per CU
   const int64_t blocks = groups < cap ? groups : cap;
-  hipLaunchKernelGGL((k_fwht_quant64<LOG2K, BF16, BITS, HAD, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, x, M,
-                     ldx, codes, scales, rowsum, y);
+  hipLaunchKernelGGL((k_fwht_quant64<LOG2K, BF16, BITS, HAD, OUT, NORM>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     x, M, ldx, codes, scales, rowsum, y, gain);
   return hipGetLastError();
 }
 
-template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT>
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 hipError_t launch_fq(const void* x, int64_t M, int64_t ldx, void* codes, float* scales,
-                     int32_t* rowsum, float* y, hipStream_t s) {
+                     int32_t* rowsum, float* y, const float* gain, hipStream_t s) {
   using G = Geom<LOG2K>;
   const int64_t blocks = (M + G::RPB - 1) / G::RPB;
-  hipLaunchKernelGGL((k_fwht_quant<LOG2K, BF16, BITS, HAD, OUT>), dim3((unsigned)blocks),
-                     dim3(G::THREADS), 0, s, x, M, ldx, codes, scales, rowsum, y);
+  hipLaunchKernelGGL((k_fwht_quant<LOG2K, BF16, BITS, HAD, OUT, NORM>), dim3((unsigned)blocks),
+                     dim3(G::THREADS), 0, s, x, M, ldx, codes, scales, rowsum, y, gain);
   return hipGetLastError();
 }
 
-template <int LOG2K>
+template <int LOG2K, bool NORM>
 hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, int bits,
-                          void* codes, float* scales, int32_t* rowsum, int cu, hipStream_t s) {
-#define HBL_FQ(B16, BITS, HAD)                                                                       \
-  if constexpr (LOG2K >= 10)                                                                         \
-    return launch_fq64<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, cu, s); \
-  else                                                                                               \
-    return launch_fq<LOG2K, B16, BITS, HAD, 0>(x, M, ldx, codes, scales, rowsum, nullptr, s)
+                          void* codes, float* scales, int32_t* rowsum, const float* gain, int cu,
+                          hipStream_t s) {
+#define HBL_FQ(B16, BITS, HAD)                                                                              \
+  if constexpr (LOG2K >= 10)                                                                                \
+    return launch_fq64<LOG2K, B16, BITS, HAD, 0, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, cu, \
+                                                       s);                                                  \
+  else                                                                                                      \
+    return launch_fq<LOG2K, B16, BITS, HAD, 0, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, s)
   if (bf16) {
     if (had) { if (bits == 8) HBL_FQ(true, 8, true); else HBL_FQ(true, 4, true); }
     else { if (bits == 8) HBL_FQ(true, 8, false); else HBL_FQ(true, 4, false); }
@@ -789,6 +851,44 @@ hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool
     else { if (bits == 8) HBL_FQ(false, 8, false); else HBL_FQ(false, 4, false); }
   }
 #undef HBL_FQ
+}
+
+template <bool NORM>
+hipError_t launch_plain(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, int bits, void* codes,
+                        float* scales, int32_t* rowsum, const float* gain, hipStream_t s) {
+  if (x_bf16) {
+    if (bits == 8)
+      hipLaunchKernelGGL((k_quant_plain<true, 8, NORM>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes,
+                         scales, rowsum, gain);
+    else
+      hipLaunchKernelGGL((k_quant_plain<true, 4, NORM>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes,
+                         scales, rowsum, gain);
+  } else {
+    if (bits == 8)
+      hipLaunchKernelGGL((k_quant_plain<false, 8, NORM>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes,
+                         scales, rowsum, gain);
+    else
+      hipLaunchKernelGGL((k_quant_plain<false, 4, NORM>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes,
+                         scales, rowsum, gain);
+  }
+  return hipGetLastError();
+}
+
+int ilog2(int K);
+
+template <bool NORM>
+hipError_t quant_by_k(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, bool hadamard, int bits,
+                      void* codes, float* scales, int32_t* rowsum, const float* gain, int cu, hipStream_t s) {
+  if ((K & (K - 1)) != 0)  // only reachable without the rotation (the ABI layer rejects it otherwise)
+    return launch_plain<NORM>(x, x_bf16, M, K, ldx, bits, codes, scales, rowsum, gain, s);
+#define HBL_QK(L) \
+  case L: return dispatch_quant<L, NORM>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, gain, cu, s);
+  switch (ilog2(K)) {
+    HBL_QK(4) HBL_QK(5) HBL_QK(6) HBL_QK(7) HBL_QK(8) HBL_QK(9)
+    HBL_QK(10) HBL_QK(11) HBL_QK(12) HBL_QK(13) HBL_QK(14)
+    default: return hipErrorInvalidValue;
+  }
+#undef HBL_QK
 }
 
 int ilog2(int K) {
@@ -801,34 +901,10 @@ int ilog2(int K) {
 
 hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx,
                                  bool hadamard, int bits, void* codes, float* scales,
-                                 int32_t* rowsum, int cu, hipStream_t s) {
+                                 int32_t* rowsum, bool norm, const float* gain, int cu, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const bool pow2 = (K & (K - 1)) == 0;
-  if (!pow2) {
-    // only reachable without the rotation (the ABI layer rejects it otherwise)
-    if (x_bf16) {
-      if (bits == 8) hipLaunchKernelGGL((k_quant_plain<true, 8>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
-      else hipLaunchKernelGGL((k_quant_plain<true, 4>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
-    } else {
-      if (bits == 8) hipLaunchKernelGGL((k_quant_plain<false, 8>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
-      else hipLaunchKernelGGL((k_quant_plain<false, 4>), dim3((unsigned)M), dim3(256), 0, s, x, M, K, ldx, codes, scales, rowsum);
-    }
-    return hipGetLastError();
-  }
-  switch (ilog2(K)) {
-    case 4: return dispatch_quant<4>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 5: return dispatch_quant<5>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 6: return dispatch_quant<6>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 7: return dispatch_quant<7>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 8: return dispatch_quant<8>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 9: return dispatch_quant<9>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 10: return dispatch_quant<10>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 11: return dispatch_quant<11>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 12: return dispatch_quant<12>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 13: return dispatch_quant<13>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    case 14: return dispatch_quant<14>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, cu, s);
-    default: return hipErrorInvalidValue;
-  }
+  return norm ? quant_by_k<true>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, gain, cu, s)
+              : quant_by_k<false>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, nullptr, cu, s);
 }
 
 hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, float* y, int cu,
@@ -836,12 +912,12 @@ hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int
   if (M == 0) return hipSuccess;
 #define HBL_HF(L)                                                                              \
   case L:                                                                                      \
-    return x_bf16 ? launch_fq<L, true, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s) \
-                  : launch_fq<L, false, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, s);
+    return x_bf16 ? launch_fq<L, true, 8, true, 1, false>(x, M, ldx, nullptr, nullptr, nullptr, y, nullptr, s) \
+                  : launch_fq<L, false, 8, true, 1, false>(x, M, ldx, nullptr, nullptr, nullptr, y, nullptr, s);
 #define HBL_HF64(L)                                                                                      \
   case L:                                                                                                \
-    return x_bf16 ? launch_fq64<L, true, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, cu, s)     \
-                  : launch_fq64<L, false, 8, true, 1>(x, M, ldx, nullptr, nullptr, nullptr, y, cu, s);
+    return x_bf16 ? launch_fq64<L, true, 8, true, 1, false>(x, M, ldx, nullptr, nullptr, nullptr, y, nullptr, cu, s)     \
+                  : launch_fq64<L, false, 8, true, 1, false>(x, M, ldx, nullptr, nullptr, nullptr, y, nullptr, cu, s);
   switch (ilog2(K)) {
     HBL_HF(4) HBL_HF(5) HBL_HF(6) HBL_HF(7) HBL_HF(8) HBL_HF(9)
     HBL_HF64(10) HBL_HF64(11) HBL_HF64(12) HBL_HF64(13) HBL_HF64(14)

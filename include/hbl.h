@@ -66,7 +66,7 @@ extern "C" {
 #define HBL_DTYPE_F32 0
 #define HBL_DTYPE_BF16 1
 
-/* flags of hbl_hadamard_quant / hbl_forward */
+/* flags of hbl_hadamard_quant / hbl_forward (and their _norm_ forms) */
 #define HBL_HADAMARD 1 /* rotate each row before quantising (H-BitLinear);
                           without it the row is quantised as is (BitLinear) */
 
@@ -132,6 +132,17 @@ int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K,
                      int64_t ldx, float* y, void* stream);
 
 /* ---------------------------------------------------------------------
+ * hbl_hadamard_backward_f32 -- backward of the rotation
+ * (§3.4 "Gradient Handling Through the Hadamard Transformation", Eq. 10):
+ * given dy = dL/d(H x) per token row, writes dx = dL/dx = H^T dy.  H is
+ * symmetric and orthogonal, so this is the forward transform applied to dy:
+ * the same kernel, the same arithmetic and the same arguments as
+ * hbl_hadamard_f32 (dy in place of x, dx in place of y).
+ * ------------------------------------------------------------------- */
+int hbl_hadamard_backward_f32(const void* dy, int dy_dtype, int64_t M, int64_t K,
+                              int64_t lddy, float* dx, void* stream);
+
+/* ---------------------------------------------------------------------
  * hbl_hadamard_quant -- rotation fused with per-token quantisation
  * (Eq. 3-6 followed by Eq. 7 or Eq. 8).
  *
@@ -154,6 +165,23 @@ int hbl_hadamard_f32(const void* x, int x_dtype, int64_t M, int64_t K,
 int hbl_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
                        int64_t ldx, int flags, int bits, void* codes,
                        float* scales, int32_t* rowsum, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_norm_hadamard_quant -- hbl_hadamard_quant preceded by the layer's
+ * normalisation (§3.4 "H-BitLinear: The Composite Layer", Eq. 9:
+ * X_r = Hadamard(LN(X)), LN being RMSNorm).  The pages name RMSNorm without
+ * a formula; this library reads it as the usual one:
+ *   RMSNorm(x)_k = x_k * r * gain_k,  r = 1/sqrt(mean_j x_j^2 + eps),
+ * in fp32 (the mean of squares as a tree sum, r with an IEEE square root
+ * and divide), applied before the rotation.
+ * gain: device float [K], 16-byte aligned, or NULL for a gain of one.
+ * Other arguments, shapes and outputs as hbl_hadamard_quant; the scales
+ * are those of the normalised rows.
+ * ------------------------------------------------------------------- */
+int hbl_norm_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
+                            int64_t ldx, const float* gain, int flags, int bits,
+                            void* codes, float* scales, int32_t* rowsum,
+                            void* stream);
 
 /* ---------------------------------------------------------------------
  * hbl_ternary_gemm -- integer matmul of activation codes with packed
@@ -190,6 +218,37 @@ int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                 int64_t N, int flags, int bits, const uint32_t* w_packed,
                 const float* alpha, void* y, int64_t ldy, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_norm_forward -- the whole layer of Eq. 9 with its normalisation:
+ * hbl_norm_hadamard_quant(x, gain, flags, bits) then hbl_ternary_gemm.
+ * Arguments as hbl_forward plus gain (as hbl_norm_hadamard_quant); the
+ * workspace is hbl_forward_workspace_size(M, K, bits) bytes.
+ * ------------------------------------------------------------------- */
+int hbl_norm_forward(const void* x, int x_dtype, int64_t M, int64_t K,
+                     int64_t ldx, const float* gain, int64_t N, int flags,
+                     int bits, const uint32_t* w_packed, const float* alpha,
+                     void* y, int64_t ldy, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------
+ * hbl_ternarize_weights_rotated -- the weight side of the "weight and
+ * activation rotation" variant (§3.4 "Ablation Study: Why Activation-Only
+ * Hadamard Transformation", Table 5): the matrix quantised is W H^T instead
+ * of W, so that Q_w(W H^T) . Q(H x) approximates W x.  Row n of W H^T is
+ * the rotation of row n of W (H is symmetric): each row goes through the
+ * transform of hbl_hadamard_f32 (fp32) and the fp32 result through the
+ * quantiser of hbl_ternarize_weights.  Pair it with HBL_HADAMARD on the
+ * activations.
+ * w, w_packed, alpha: as hbl_ternarize_weights.
+ * ws: device workspace of at least hbl_ternarize_rotated_workspace_size(N,
+ *     K) bytes (the rotated fp32 matrix, then the partial sums); scratch.
+ * Shapes: N >= 1; K a power of two, 16 <= K <= HBL_MAX_K.
+ * ------------------------------------------------------------------- */
+size_t hbl_ternarize_rotated_workspace_size(int64_t N, int64_t K);
+int hbl_ternarize_weights_rotated(const void* w, int w_dtype, int64_t N, int64_t K,
+                                  uint32_t* w_packed, float* alpha, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -138,3 +138,48 @@ def test_hadamard_f32_errors(hbl):
     assert lib.hbl_hadamard_f32(A, 1, 4, 48, 48, B, None) == hbl.ERR_SHAPE
     assert lib.hbl_hadamard_f32(A, 1, 4, 256, 256, None, None) == hbl.ERR_NULL
     assert lib.hbl_hadamard_f32(A, 1, 0, 256, 256, B, None) == hbl.OK
+
+
+def test_norm_quant_errors(hbl):
+    lib = hbl.lib()
+    q = lib.hbl_norm_hadamard_quant
+    assert q(A, 1, 4, 256, 256, E + 4, 1, 8, B, C, D, None) == hbl.ERR_ALIGN           # gain alignment
+    assert "gain" in last(hbl)
+    assert q(A, 1, 4, 100, 100, E, 1, 8, B, C, D, None) == hbl.ERR_SHAPE
+    assert q(A, 1, 4, 256, 256, E, 4, 8, B, C, D, None) == hbl.ERR_MODE
+    assert q(A, 1, 4, 256, 256, None, 1, 3, B, C, D, None) == hbl.ERR_MODE
+    assert q(A, 1, 4, 256, 256, None, 1, 8, None, C, D, None) == hbl.ERR_NULL
+    assert q(A, 1, 0, 256, 256, None, 1, 4, B, C, D, None) == hbl.OK                   # M = 0
+
+
+def test_norm_forward_errors(hbl):
+    lib = hbl.lib()
+    need = lib.hbl_forward_workspace_size(10, 256, 4)
+    f = lib.hbl_norm_forward
+    assert f(A, 1, 10, 256, 256, F + 8, 64, 1, 4, B, C, D, 64, E, need, None) == hbl.ERR_ALIGN
+    assert f(A, 1, 10, 256, 256, None, 64, 1, 4, B, C, D, 64, E, need - 1, None) == hbl.ERR_WORKSPACE
+    assert f(A, 1, 10, 256, 256, None, 60, 1, 4, B, C, D, 64, E, need, None) == hbl.ERR_SHAPE
+    assert f(A, 1, 0, 256, 256, None, 64, 1, 4, B, C, D, 64, E, need, None) == hbl.OK
+
+
+def test_hadamard_backward_errors(hbl):
+    lib = hbl.lib()
+    b = lib.hbl_hadamard_backward_f32
+    assert b(A, 1, 4, 48, 48, B, None) == hbl.ERR_SHAPE
+    assert b(A, 1, 4, 256, 256, None, None) == hbl.ERR_NULL
+    assert b(A, 2, 4, 256, 256, B, None) == hbl.ERR_MODE
+    assert b(A, 1, 0, 256, 256, B, None) == hbl.OK
+
+
+def test_ternarize_rotated_errors(hbl):
+    lib = hbl.lib()
+    need = lib.hbl_ternarize_rotated_workspace_size(64, 256)
+    assert need >= 64 * 256 * 4 + lib.hbl_ternarize_workspace_size(64, 256)
+    t = lib.hbl_ternarize_weights_rotated
+    assert t(A, 0, 64, 192, B, C, D, need, None) == hbl.ERR_SHAPE      # not a power of two
+    assert t(A, 0, 64, 32768, B, C, D, need, None) == hbl.ERR_SHAPE    # above the maximum
+    assert t(A, 0, 0, 256, B, C, D, need, None) == hbl.ERR_SHAPE
+    assert t(A, 5, 64, 256, B, C, D, need, None) == hbl.ERR_MODE
+    assert t(None, 0, 64, 256, B, C, D, need, None) == hbl.ERR_NULL
+    assert t(A, 0, 64, 256, B, C, D, need - 1, None) == hbl.ERR_WORKSPACE
+    assert t(A + 2, 0, 64, 256, B, C, D, need, None) == hbl.ERR_ALIGN
