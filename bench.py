@@ -11,9 +11,11 @@ matrix-core matmul), its average duration measured with HIP events over
 back-to-back launches on the stream it runs on; ``cpu_baseline`` is the CPU
 oracle timed on a bounded sample of rows of the same workload.
 
-Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b, and
-copy (a plain device copy of known size, to calibrate the HBM traffic
-counters).
+Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b,
+msweep (layer time over token counts 1-256 for BitLinear INT8 against
+H-BitLinear INT8/INT4, and the break-even batch where the rotated INT4 layer
+catches up), and copy (a plain device copy of known size, to calibrate the
+HBM traffic counters).
 """
 from __future__ import annotations
 
@@ -70,7 +72,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wo_7b",
-                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "copy"])
+                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "msweep", "copy"])
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="copy: bytes moved per launch (calibrates the HBM traffic counters)")
     ap.add_argument("--decode-m", type=int, default=1)
@@ -318,6 +320,64 @@ def run_decode(args, hbl, torch):
     }
 
 
+def run_msweep(args, hbl, torch):
+    """Layer time against the token count M = 1 ... 256 at the two 7B input
+    widths (K = 4096 and 16384, N = 4096), for four layer kinds:
+      bitlinear_a8   plain BitLinear, INT8 codes, no rotation (the b1.58 layer)
+      hbitlinear_a8  H-BitLinear, INT8 codes
+      hbitlinear_a4  H-BitLinear, INT4 codes
+      norm_hbitlinear_a4  H-BitLinear INT4 with the RMSNorm layer in front
+    Each time is one whole layer call (quantisation kernel + matmul kernel),
+    averaged over HIP-graph replays that cycle enough distinct weight
+    matrices (>= 512 MiB) that the weights stream from HBM.  The break-even
+    batch is the smallest M at which the rotated INT4 layer is no slower than
+    the plain INT8 one."""
+    import workloads
+    Ms = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+    kinds = [("bitlinear_a8", 8, False, False), ("hbitlinear_a8", 8, True, False),
+             ("hbitlinear_a4", 4, True, False), ("norm_hbitlinear_a4", 4, True, True)]
+    table, breakeven = [], {}
+    for K in (4096, 16384):
+        N = 4096
+        n_mats = max(10, -(-(512 << 20) // (N * K // 4)))
+        base = [hbl.ternarize_weights(torch.from_numpy(workloads.decode_weights(K, N, i)).cuda()) for i in range(10)]
+        mats = [(base[i % 10][0].clone(), base[i % 10][1].clone()) for i in range(n_mats)]
+        del base
+        gain = torch.from_numpy(np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32)).cuda()
+        breakeven[K] = None
+        for M in Ms:
+            x = dev_x(workloads.decode_inputs(K, M))
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            row = {"K": K, "N": N, "M": M}
+            for name, bits, had, norm in kinds:
+                ws = hbl.forward_workspace(M, K, bits, "cuda")
+
+                def all_mats():
+                    for p, a in mats:
+                        if norm:
+                            hbl.norm_forward(x, p, a, bits, gain=gain, hadamard=had, out=out, workspace=ws)
+                        else:
+                            hbl.forward(x, p, a, bits, hadamard=had, out=out, workspace=ws)
+
+                t = time_stream(all_mats, 2) / n_mats
+                row[f"{name}_us"] = t * 1e6
+            row["rotation_overhead_a8"] = row["hbitlinear_a8_us"] / row["bitlinear_a8_us"] - 1.0
+            row["a4_vs_bitlinear_a8"] = row["hbitlinear_a4_us"] / row["bitlinear_a8_us"]
+            if breakeven[K] is None and row["hbitlinear_a4_us"] <= row["bitlinear_a8_us"]:
+                breakeven[K] = M
+            table.append(row)
+            print(json.dumps({"progress": row}), file=sys.stderr, flush=True)
+        del mats
+        torch.cuda.empty_cache()
+    return {
+        "metric": "H-BitLinear vs BitLinear layer time over the token count (break-even batch)",
+        "value": breakeven[4096], "unit": "tokens (smallest M where H-BitLinear INT4 <= BitLinear INT8, K=4096)",
+        "n_gpus": 1, "higher_is_better": False, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "msweep: M = 1..256, K in {4096, 16384}, N = 4096, weights cycled from HBM"},
+        "breakeven_m": {str(k): v for k, v in breakeven.items()}, "sweep": table,
+    }
+
+
 def run_block(args, hbl, torch):
     """The seven linears of one 7B block at M = 65536 tokens: Q/K/V share one
     quantisation of their input, up/gate another; Wo and Wdown rotate their
@@ -414,6 +474,10 @@ def main():
 
     if args.workload == "block_7b":
         print(json.dumps(run_block(args, hbl, torch)), flush=True)
+        return
+
+    if args.workload == "msweep":
+        print(json.dumps(run_msweep(args, hbl, torch)), flush=True)
         return
 
     c = {"tiny": workloads.tiny, "wo_7b": workloads.wo_7b, "wdown_7b": workloads.wdown_7b}[args.workload]()
