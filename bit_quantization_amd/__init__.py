@@ -58,6 +58,11 @@ _SIGS = {
     "hbl_norm_forward": ([_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
     "hbl_ternarize_rotated_workspace_size": ([_I64, _I64], _SZ),
     "hbl_ternarize_weights_rotated": ([_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P], _I),
+    "hbl_prepare_weights_mx": ([_P, _I64, _I64, _P, _P], _I),
+    "hbl_hadamard_quant_mx": ([_P, _I, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "hbl_ternary_gemm_mx": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
+    "hbl_forward_mx_workspace_size": ([_I64, _I64], _SZ),
+    "hbl_forward_mx": ([_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -254,4 +259,58 @@ def norm_forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bit
     _check(_lib.hbl_norm_forward(_ptr(x), _x_dtype(x), M, K, ldx, _gain(gain, K), N,
                                  HADAMARD if hadamard else 0, bits, _ptr(packed), _ptr(alpha), _ptr(out),
                                  out.stride(0), _ptr(workspace), workspace.numel(), _stream()), "hbl_norm_forward")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# INT4 on the FP6 x FP4 matrix cores (MX6 codes, MX4 weights; include/hbl.h)
+
+def prepare_weights_mx(packed: torch.Tensor, K: int) -> torch.Tensor:
+    """Ternary layout -> MX4 layout (int32 [N][K/16] holding the words)."""
+    N = packed.shape[0]
+    wq = torch.empty((N, K // 16), dtype=torch.int32, device=packed.device)
+    _check(_lib.hbl_prepare_weights_mx(_ptr(packed), N, K, _ptr(wq), _stream()), "hbl_prepare_weights_mx")
+    return wq
+
+
+def hadamard_quant_mx(x: torch.Tensor, hadamard: bool = True):
+    """INT4 quantisation (Eq. 8) with MX6 codes: (codes uint8 [M][3K/4],
+    scales float32 [M])."""
+    M, K, ldx = _rows(x)
+    codes = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(_lib.hbl_hadamard_quant_mx(_ptr(x), _x_dtype(x), M, K, ldx, HADAMARD if hadamard else 0, _ptr(codes),
+                                      _ptr(scales), _stream()), "hbl_hadamard_quant_mx")
+    return codes, scales
+
+
+def ternary_gemm_mx(codes: torch.Tensor, scales: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, K: int,
+                    out_dtype: int = OUT_BF16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The FP6 x FP4 matmul with the rescale of Eq. 9."""
+    M = codes.shape[0]
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=codes.device)
+    _check(_lib.hbl_ternary_gemm_mx(_ptr(codes), _ptr(scales), _ptr(wq), _ptr(alpha), M, N, K, out_dtype, _ptr(out),
+                                    out.stride(0), _stream()), "hbl_ternary_gemm_mx")
+    return out
+
+
+def forward_mx_workspace(M: int, K: int, device) -> torch.Tensor:
+    return torch.empty(max(1, _lib.hbl_forward_mx_workspace_size(M, K)), dtype=torch.uint8, device=device)
+
+
+def forward_mx(x: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, hadamard: bool = True,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The INT4 layer of Eq. 9 on the FP6 x FP4 matrix cores: bf16 [M][N],
+    the same values as forward(x, packed, alpha, 4, hadamard)."""
+    M, K, ldx = _rows(x)
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = forward_mx_workspace(M, K, x.device)
+    _check(_lib.hbl_forward_mx(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, _ptr(wq), _ptr(alpha),
+                               _ptr(out), out.stride(0), _ptr(workspace), workspace.numel(), _stream()),
+           "hbl_forward_mx")
     return out

@@ -106,6 +106,15 @@ size_t codes_region(int64_t M, int64_t K, int bits) {
   return round256(codes_bytes(M, K, bits)) + 2 * round256(sizeof(float) * (size_t)M);
 }
 
+// the FP6 x FP4 path: MX6 codes come from the rotation/quantisation kernel
+// for rows of 1024 .. HBL_MAX_K elements, a power of two
+int check_mx_k(int64_t K) {
+  if (!is_pow2(K) || K < 1024 || K > HBL_MAX_K)
+    return fail(HBL_ERR_SHAPE, "K = %lld must be a power of two in [1024, %d] on the FP6 x FP4 path", (long long)K,
+                HBL_MAX_K);
+  return HBL_OK;
+}
+
 int check_gain(const float* gain) {
   if (!aligned16(gain)) return fail(HBL_ERR_ALIGN, "gain is not 16-byte aligned");
   return HBL_OK;
@@ -286,6 +295,89 @@ int hbl_norm_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t l
                      int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(x, x_dtype, M, K, ldx, true, gain, N, flags, bits, w_packed, alpha, y, ldy, ws, ws_bytes,
                       stream);
+}
+
+int hbl_prepare_weights_mx(const uint32_t* w_packed, int64_t N, int64_t K, uint32_t* w_mx, void* stream) {
+  g_last_error.clear();
+  if (N < 1 || K < 16 || K % 16 != 0)
+    return fail(HBL_ERR_SHAPE, "need N >= 1 and K a positive multiple of 16 (N = %lld, K = %lld)", (long long)N,
+                (long long)K);
+  if (!w_packed || !w_mx) return fail(HBL_ERR_NULL, "w_packed and w_mx must be non-NULL");
+  if (!aligned16(w_packed) || !aligned16(w_mx)) return fail(HBL_ERR_ALIGN, "w_packed and w_mx must be 16-byte aligned");
+  hipError_t e = hbl::launch_prepare_mx4(w_packed, N, K, w_mx, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  return HBL_OK;
+}
+
+int hbl_hadamard_quant_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int flags, void* codes_mx,
+                          float* scales, void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (!rc) rc = check_mx_k(K);
+  if (rc) return rc;
+  if (M > 0 && (!codes_mx || !scales)) return fail(HBL_ERR_NULL, "codes_mx and scales must be non-NULL");
+  if (!aligned16(codes_mx) || !aligned4(scales))
+    return fail(HBL_ERR_ALIGN, "codes_mx must be 16-byte aligned, scales 4-byte aligned");
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, (flags & HBL_HADAMARD) != 0,
+                                            6, codes_mx, scales, nullptr, false, nullptr, cu_count_cached(),
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  return HBL_OK;
+}
+
+int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales, const uint32_t* w_mx, const float* alpha,
+                        int64_t M, int64_t N, int64_t K, int out_dtype, void* out, int64_t ldo, void* stream) {
+  g_last_error.clear();
+  int rc = check_gemm_shape(M, N, K, ldo);
+  if (rc) return rc;
+  if (K % 512 != 0) return fail(HBL_ERR_SHAPE, "K = %lld must be a multiple of 512 on the FP6 x FP4 path", (long long)K);
+  if (out_dtype != HBL_OUT_BF16 && out_dtype != HBL_OUT_F32 && out_dtype != HBL_OUT_I32)
+    return fail(HBL_ERR_MODE, "out_dtype %d is not an HBL_OUT_* value", out_dtype);
+  if (M == 0) return HBL_OK;
+  if (!codes_mx || !scales || !w_mx || !alpha || !out)
+    return fail(HBL_ERR_NULL, "codes_mx, scales, w_mx, alpha and out must be non-NULL");
+  if (!aligned16(codes_mx) || !aligned16(w_mx) || !aligned16(out) || !aligned4(scales) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "codes_mx, w_mx and out must be 16-byte aligned");
+  if ((K / 4 * 3) * 256 > (int64_t)INT_MAX)  // a 256-row tile is addressed with 32-bit offsets
+    return fail(HBL_ERR_SHAPE, "K = %lld is too large for the FP6 x FP4 path", (long long)K);
+  hipError_t e = hbl::launch_gemm_mx(codes_mx, scales, w_mx, alpha, M, N, K, out_dtype, out, ldo, cu_count_cached(),
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return HBL_OK;
+}
+
+size_t hbl_forward_mx_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0) return 0;
+  return round256((size_t)M * (size_t)(K / 4 * 3)) + round256(sizeof(float) * (size_t)M);
+}
+
+int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
+                   const uint32_t* w_mx, const float* alpha, void* y, int64_t ldy, void* ws, size_t ws_bytes,
+                   void* stream) {
+  g_last_error.clear();
+  int rc = check_flags(flags);
+  if (!rc) rc = check_x(x, x_dtype, M, K, ldx, (flags & HBL_HADAMARD) != 0);
+  if (!rc) rc = check_mx_k(K);
+  if (!rc) rc = check_gemm_shape(M, N, K, ldy);
+  if (rc) return rc;
+  if (M == 0) return HBL_OK;
+  if (!w_mx || !alpha || !y) return fail(HBL_ERR_NULL, "w_mx, alpha and y must be non-NULL");
+  if (!aligned16(w_mx) || !aligned16(y) || !aligned4(alpha))
+    return fail(HBL_ERR_ALIGN, "w_mx and y must be 16-byte aligned");
+  const size_t need = hbl_forward_mx_workspace_size(M, K);
+  if (!ws || ws_bytes < need)
+    return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
+  if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
+  void* codes = ws;
+  float* scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)M * (size_t)(K / 4 * 3)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, (flags & HBL_HADAMARD) != 0,
+                                            6, codes, scales, nullptr, false, nullptr, cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "quantise launch");
+  e = hbl::launch_gemm_mx(codes, scales, w_mx, alpha, M, N, K, HBL_OUT_BF16, y, ldy, cu_count_cached(), s);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return HBL_OK;
 }
 
 size_t hbl_ternarize_rotated_workspace_size(int64_t N, int64_t K) {

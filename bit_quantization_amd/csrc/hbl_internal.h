@@ -10,6 +10,8 @@ namespace hbl {
 // returns the hipError_t of the launch.
 // cu_count: compute units of the device (sizes persistent grids).
 // norm: RMSNorm of each row (per-channel gain, nullable) before the rotation.
+// bits: 8 or 4 (codes in the public layouts), or 6: INT4 codes written as
+// MX6 operands of the FP6 x FP4 matmul (K a power of two >= 1024).
 hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K,
                                  int64_t ldx, bool hadamard, int bits,
                                  void* codes, float* scales, int32_t* rowsum,
@@ -28,6 +30,15 @@ hipError_t launch_ternary_gemm(const void* codes, int bits, const float* scales,
                                const float* alpha, int64_t M, int64_t N,
                                int64_t K, int out_kind, void* out, int64_t ldo,
                                int cu_count, hipStream_t s);
+
+// FP6 x FP4 matmul of MX6 codes and MX4 weights (k_gemm_mx.hip); K % 512 == 0.
+hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t* wq,
+                          const float* alpha, int64_t M, int64_t N, int64_t K,
+                          int out_kind, void* out, int64_t ldo, int cu_count,
+                          hipStream_t s);
+// ternary layout -> MX4 layout (same size)
+hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t* wq,
+                              hipStream_t s);
 
 // Token counts up to this take the weight-streaming kernel.
 constexpr int kGemvMaxM = 16;

@@ -1,0 +1,417 @@
+// INT4 H-BitLinear matmul on the FP6 x FP4 matrix cores of gfx950 (the
+// rescale of Eq. 9, architecture write-up of "BitNet v2", §3.4
+// "H-BitLinear"):
+//   acc[m][n] = sum_k q_x[m][k] q_w[n][k],  out = (scale_m * alpha) * acc.
+//
+// The INT4 activation codes q_x in [-8, 7] are exact in the 6-bit float
+// E3M2 (OCP "BF6": 1 sign, 3 exponent (bias 3), 2 mantissa bits) and the
+// ternary weights in the 4-bit float E2M1 (1 sign, 2 exponent (bias 1), 1
+// mantissa bit), every product is an integer of magnitude <= 8, and the
+// fp32 accumulator holds every partial sum exactly (|sum| <= 8 K < 2^24 for
+// K <= 2^21).  So v_mfma_f32_32x32x64_f8f6f4 computes the integer matmul
+// exactly, at twice the rate per clock of the int8 matrix cores.
+//
+// Operand layouts (both produced by this library; see include/hbl.h):
+//   codes, "MX6": per token row K * 3/4 bytes, in blocks of 128 codes
+//     (96 bytes).  Group g = 0..3 of a block holds codes 32 g .. 32 g + 31 as
+//     a 192-bit field, code e at bits 6 e .. 6 e + 5 (little endian); its
+//     first 16 bytes sit at byte 16 g of the block, its last 8 bytes at
+//     byte 64 + 8 g.  The split keeps every LDS read 16-byte aligned.
+//   weights, "MX4": uint32 [N][K/16], word w holds k = 16 w .. 16 w + 15
+//     with two bits per weight: for n = 0..7, bit 4n+1 = (q_{16w+n} != 0),
+//     bit 4n+3 = (q_{16w+n} < 0), bit 4n = (q_{16w+8+n} != 0),
+//     bit 4n+2 = (q_{16w+8+n} < 0).  Then word & 0xAAAAAAAA holds the E2M1
+//     codes of k = 16w .. 16w+7 (nibble n, sign at bit 3, exponent bit at
+//     bit 1) and (word << 1) & 0xAAAAAAAA those of k = 16w+8 .. 16w+15.
+//
+// Kernel structure (k_gemm_mx): persistent, one block of 4 waves (2 x 2) per
+// CU, one wave per SIMD, block tile 256 tokens x BN features (BN = 256 when
+// the tiles fill the chip, else 128), wave tile 128 x BN/2 of 32x32x64
+// MFMAs with fp32 accumulators.  A stage is 128 codes (two MFMA steps);
+// four stage buffers, each its own LDS variable, are refilled four stages
+// ahead by direct-to-LDS buffer loads; the stage sequence runs through the
+// block's tiles, so the last stages of a tile already load the next one.
+// The waves meet once per stage, between its two MFMA steps: past that
+// barrier the stage's buffer may be refilled and the next stage's fragments
+// are read while the second step runs.  The barrier carries no memory fence
+// (a fence would also wait for the prefetch in flight); each wave has waited
+// for its own loads of the next stage first.
+//
+// Fragment layout (32x32x64, measured on the device): lane l of an operand
+// holds row l % 32 and the 32 k's 32 (l / 32) .. + 31 of the MFMA step,
+// as consecutive 6-bit (codes) or 4-bit (weights) fields; in the
+// accumulator, lane l and register r hold token l % 32 and feature
+// 8 (r / 4) + 4 (l / 32) + r % 4.  Step t of a stage gives lane half h the
+// stage's k = 64 h + 32 t .. + 31, i.e. code group 2 h + t: the lane's
+// weight unit (16 bytes, k = 64 h .. 64 h + 63) serves both steps, its code
+// main parts are units 2 h and 2 h + 1, and one tail unit (h) holds the
+// last 8 bytes of both groups.
+//
+// LDS rows are not padded; 16-byte units are XOR-swizzled by row (unit u of
+// row r at u ^ ((r >> s) & (U - 1)), U units per row, s = log2(16 / U)) so
+// that the 16 rows one b128 read touches at once fall into distinct banks.
+#include "hbl_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+namespace hbl {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// fp32 -> bf16, round to nearest even (the same rounding as the int8 path)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// four consecutive features of one token: acc holds exact integers
+template <int OUT>
+__device__ __forceinline__ void store4f(void* out, int64_t idx, float a0, float a1, float a2, float a3, float sc) {
+  if constexpr (OUT == 2) {
+    *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(out) + idx) = make_int4((int)a0, (int)a1, (int)a2, (int)a3);
+  } else if constexpr (OUT == 1) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = make_float4(sc * a0, sc * a1, sc * a2, sc * a3);
+  } else {
+    const uint32_t lo = bf16_rne(sc * a0) | (bf16_rne(sc * a1) << 16);
+    const uint32_t hi = bf16_rne(sc * a2) | (bf16_rne(sc * a3) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = make_uint2(lo, hi);
+  }
+}
+
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+template <int OUT, int BM, int BN>
+__global__ void __launch_bounds__(256, 1)
+k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, const uint32_t* __restrict__ wq,
+          const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
+          int tilesM, int tilesN) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
+  constexpr int MROW = 64, TROW = 32, BROW = 32;    // bytes per row per stage: code mains, code tails, weights
+  constexpr int MU = MROW / 16, TU = TROW / 16, BU = BROW / 16;
+  constexpr int MSH = ilog2c(16 / MU), TSH = ilog2c(16 / TU), BSH = ilog2c(16 / BU);
+  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = BM * TROW / 1024 / NW, BDMA = BN * BROW / 1024 / NW;
+  static_assert(MDMA * NW * 1024 == BM * MROW && TDMA * NW * 1024 == BM * TROW && BDMA * NW * 1024 == BN * BROW,
+                "staging must divide evenly");
+  constexpr int DPS = MDMA + TDMA + BDMA;  // loads per wave per stage
+  constexpr int MSZ = BM * MROW, TSZ = BM * TROW, BSZ = BN * BROW;
+  __shared__ __attribute__((aligned(1024))) uint8_t Am0[MSZ], Am1[MSZ], Am2[MSZ], Am3[MSZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t At0[TSZ], At1[TSZ], At2[TSZ], At3[TSZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
+  // bf16 outputs of 256 x 128 tiles are staged through LDS (whole-row stores)
+  constexpr int OROW = (BN / 2) * 2 + 16;
+  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (MSZ + TSZ + BSZ) + 4 * 32 * OROW <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? 4 * 32 * OROW : 16];
+  auto mbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
+    if constexpr (I == 0) return Am0; else if constexpr (I == 1) return Am1; else if constexpr (I == 2) return Am2; else return Am3;
+  };
+  auto tbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
+    if constexpr (I == 0) return At0; else if constexpr (I == 1) return At1; else if constexpr (I == 2) return At2; else return At3;
+  };
+  auto bbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
+    if constexpr (I == 0) return Bs0; else if constexpr (I == 1) return Bs1; else if constexpr (I == 2) return Bs2; else return Bs3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % 2, wn = wave / 2;
+  const int64_t arow_bytes = K / 4 * 3;  // global code row stride (MX6)
+  const int64_t brow_bytes = K / 4;      // global weight row stride (MX4)
+  const int nk = (int)(K / BK);          // a multiple of NST
+
+  // Tiles of this block: r P + slot (P blocks, a multiple of 8); slot gives
+  // each XCD a contiguous range of each round's tiles, walked in M-groups of
+  // 8 so that an XCD's blocks share codes and weights in its L2.
+  const int G = tilesM * tilesN, P = gridDim.x, b = blockIdx.x;
+  const int slot = (b % 8) * (P / 8) + b / 8;
+  const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
+  auto tile_of = [&](int r, int64_t& m0, int64_t& n0) {
+    const int L = r * P + slot;
+    constexpr int GROUP_M = 8;
+    const int per_group = GROUP_M * tilesN;
+    const int first_m = (L / per_group) * GROUP_M;
+    const int gsz = min(GROUP_M, tilesM - first_m);
+    m0 = (int64_t)(first_m + (L % per_group) % gsz) * BM;
+    n0 = (int64_t)((L % per_group) / gsz) * BN;
+  };
+
+  auto mswz = [](int r, int u) { return u ^ ((r >> MSH) & (MU - 1)); };
+  auto tswz = [](int r, int u) { return u ^ ((r >> TSH) & (TU - 1)); };
+  auto bswz = [](int r, int u) { return u ^ ((r >> BSH) & (BU - 1)); };
+  // Lane l of load j of wave w fills physical unit 64 (w + NW j) + l of a
+  // stage array: row p / U, physical unit l % U, holding logical unit
+  // (l % U) ^ swizzle(row).  Rows past the end lie beyond the buffer's
+  // range and read as zero (a zero code).
+  constexpr int MJR = 64 * NW / MU, TJR = 64 * NW / TU, BJR = 64 * NW / BU;  // rows between loads j, j + 1
+  const int mr0 = (64 * wave + lane) / MU, tr0 = (64 * wave + lane) / TU, br0 = (64 * wave + lane) / BU;
+  const uint32_t moff0 = (uint32_t)mr0 * (uint32_t)arow_bytes + 16u * (uint32_t)mswz(mr0, lane % MU);
+  const uint32_t toff0 = (uint32_t)tr0 * (uint32_t)arow_bytes + 64u + 16u * (uint32_t)tswz(tr0, lane % TU);
+  const uint32_t boff0 = (uint32_t)br0 * (uint32_t)brow_bytes + 16u * (uint32_t)bswz(br0, lane % BU);
+  const uint32_t mstep = (uint32_t)MJR * (uint32_t)arow_bytes, tstep = (uint32_t)TJR * (uint32_t)arow_bytes;
+  const uint32_t bstep = (uint32_t)BJR * (uint32_t)brow_bytes;
+  constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
+
+  int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
+  __amdgpu_buffer_rsrc_t rA, rB;
+  auto set_tile = [&](int r) {
+    int64_t m0 = 0, n0 = 0;
+    if (r < ntiles) tile_of(r, m0, n0);
+    const int arows = r < ntiles ? (int)min<int64_t>(BM, M - m0) : 0;
+    const int brows = r < ntiles ? (int)min<int64_t>(BN, N - n0) : 0;
+    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + m0 * arow_bytes), (short)0,
+                                           (int)(arows * arow_bytes), 0x00020000);
+    rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes),
+                                           (short)0, (int)(brows * brow_bytes), 0x00020000);
+  };
+  auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
+    uint8_t* const Md = mbuf(bi);
+    uint8_t* const Td = tbuf(bi);
+    uint8_t* const Bd = bbuf(bi);
+    const bool live = dr < ntiles;
+    const uint32_t vm = live ? moff0 + (uint32_t)dk * 96u : kOut;
+    const uint32_t vt = live ? toff0 + (uint32_t)dk * 96u : kOut;
+    const uint32_t vb = live ? boff0 + (uint32_t)dk * BROW : kOut;
+#pragma unroll
+    for (int j = 0; j < MDMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * mstep, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < TDMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vt + j * tstep, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < BDMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+    if (++dk == nk) {
+      dk = 0;
+      set_tile(++dr);
+    }
+  };
+
+  v16f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
+
+  const int fr = lane % 32, h = lane / 32;
+  const int ar = wm * WM + fr, br = wn * WN + fr;
+  const int mbase0 = ar * MROW + 16 * mswz(ar, 2 * h), mbase1 = ar * MROW + 16 * mswz(ar, 2 * h + 1);
+  const int tbase = ar * TROW + 16 * tswz(ar, h);
+  const int bbase = br * BROW + 16 * bswz(br, h);
+  constexpr int MFRAG = 32 * MROW, TFRAG = 32 * TROW, BFRAG = 32 * BROW;  // bytes between fragments
+
+  // a stage's fragments: per weight fragment one unit (both steps); per
+  // code fragment and step the main unit and the tail half, read straight
+  // into the six operand registers
+  struct Frag {
+    uint4 w[FN];
+    v6i c0[FM], c1[FM];
+  };
+  auto read_frag = [&]<int I>(Frag& f, std::integral_constant<int, I> bi) {
+    const uint8_t* Mb = mbuf(bi);
+    const uint8_t* Tb = tbuf(bi);
+    const uint8_t* Bb = bbuf(bi);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) f.w[i] = *reinterpret_cast<const uint4*>(Bb + bbase + BFRAG * i);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const uint4 a = *reinterpret_cast<const uint4*>(Mb + mbase0 + MFRAG * j);
+      const uint2 ta = *reinterpret_cast<const uint2*>(Tb + tbase + TFRAG * j);
+      f.c0[j] = v6i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)ta.x, (int)ta.y};
+      const uint4 c = *reinterpret_cast<const uint4*>(Mb + mbase1 + MFRAG * j);
+      const uint2 tc = *reinterpret_cast<const uint2*>(Tb + tbase + 8 + TFRAG * j);
+      f.c1[j] = v6i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, (int)tc.x, (int)tc.y};
+    }
+  };
+  // weights of step t: words 2t, 2t+1 of the unit -> four E2M1 words
+  auto decw = [&](v4i (&wf)[FN], const uint4 (&w)[FN], int t) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const uint32_t w0 = t == 0 ? w[i].x : w[i].z, w1 = t == 0 ? w[i].y : w[i].w;
+      wf[i] = v4i{(int)(w0 & 0xAAAAAAAAu), (int)((w0 << 1) & 0xAAAAAAAAu), (int)(w1 & 0xAAAAAAAAu),
+                  (int)((w1 << 1) & 0xAAAAAAAAu)};
+    }
+  };
+  // the operand registers beyond the format's width (4 for E2M1, 6 for
+  // E3M2) are not read: left undefined
+  auto step = [&](const v4i (&wf)[FN], const v6i (&cf)[FM]) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const v8i b8 = __builtin_shufflevector(cf[j], cf[j], 0, 1, 2, 3, 4, 5, -1, -1);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const v8i a8 = __builtin_shufflevector(wf[i], wf[i], 0, 1, 2, 3, -1, -1, -1, -1);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 3, 0, 0, 0, 0);
+      }
+    }
+  };
+  auto bar = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto epilogue = [&](int r) {
+    // r and the lane's coordinates made opaque here: nothing of the epilogue
+    // (addresses included) is computed early and kept live through the loop
+    asm volatile("" : "+s"(r));
+    int fr = lane % 32, h = lane / 32;
+    asm volatile("" : "+v"(fr), "+v"(h));
+    int64_t m0, n0;
+    tile_of(r, m0, n0);
+    const float al = *alpha;
+    if constexpr (STAGE_OUT) {
+      uint8_t* const Ow = Os + wave * 32 * OROW;
+      constexpr int U = WN * 2 / 16;  // 16-byte units per staged row
+      const bool wide = (ldo & 7) == 0;
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * WM + 32 * j + fr;
+        const float sc = m < M ? scales[m] * al : 0.0f;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16f& a = acc[i][j];
+            const uint32_t lo = bf16_rne(sc * a[4 * q]) | (bf16_rne(sc * a[4 * q + 1]) << 16);
+            const uint32_t hi = bf16_rne(sc * a[4 * q + 2]) | (bf16_rne(sc * a[4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(Ow + fr * OROW + 2 * (32 * i + 8 * q + 4 * h)) = make_uint2(lo, hi);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one fragment's values live at a time
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is the wave's own: no barrier
+#pragma unroll
+        for (int pp = 0; pp < 32 * U / 64; ++pp) {
+          const int row = lane / U + (64 / U) * pp, u = lane % U;
+          const int64_t mm = m0 + wm * WM + 32 * j + row, nn = n0 + wn * WN + 8 * u;
+          const uint4 v = *reinterpret_cast<const uint4*>(Ow + row * OROW + 16 * u);
+          if (mm < M && nn < N) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(out) + mm * ldo + nn;
+            if (wide) {
+              *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+              reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+              reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+            }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next row's writes
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * WM + 32 * j + fr;
+        if (m < M) {
+          const float sc = scales[m] * al;
+#pragma unroll
+          for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t n = n0 + wn * WN + 32 * i + 8 * q + 4 * h;
+              const v16f& a = acc[i][j];
+              if (n < N) store4f<OUT>(out, m * ldo + n, a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3], sc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one fragment row's values live at a time
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
+  };
+
+  if (ntiles == 0) return;
+  set_tile(0);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (stage_load(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, NST>{});
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * DPS) : "memory");
+  bar();
+  Frag f0, f1;
+  v4i wf0[FN], wf1[FN];
+  read_frag(f0, std::integral_constant<int, 0>{});
+  decw(wf0, f0.w, 0);
+  // Stage Q of a group of NST: buffer Q, fragments f0 / f1 by parity.  The
+  // weight operands of the next step are formed while a step's MFMAs run
+  // (an MFMA whose operand was just written by the VALU waits for it).
+  auto body = [&]<int Q>(std::integral_constant<int, Q>) {
+    Frag& cur = (Q % 2 == 0) ? f0 : f1;
+    Frag& nxt = (Q % 2 == 0) ? f1 : f0;
+    step(wf0, cur.c0);
+    decw(wf1, cur.w, 1);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
+    bar();
+    stage_load(std::integral_constant<int, Q>{});
+    read_frag(nxt, std::integral_constant<int, (Q + 1) % NST>{});
+    step(wf1, cur.c1);
+    decw(wf0, nxt.w, 0);
+  };
+  const int groups_per_tile = nk / NST;
+  for (int r = 0; r < ntiles; ++r) {
+    for (int gq = 0; gq < groups_per_tile; ++gq) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (body(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, NST>{});
+    }
+    epilogue(r);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
+// Ternary layout of the library (c = q + 1 at bits 8b + 2s of each word,
+// weight 4s + b) -> MX4 layout; one thread per word.
+__global__ void k_prepare_mx4(const uint32_t* __restrict__ wp, int64_t n_words, uint32_t* __restrict__ wq) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_words) return;
+  const uint32_t w = wp[i];
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t c = (w >> (8 * (j & 3) + 2 * (j >> 2))) & 3u;  // weight j: s = j / 4, b = j % 4
+    const uint32_t nz = c != 1u, neg = c == 0u;
+    const int n = j & 7, hi = j >> 3;  // k < 8: bits 4n+1, 4n+3; else 4n, 4n+2
+    o |= (nz << (4 * n + 1 - hi)) | (neg << (4 * n + 3 - hi));
+  }
+  wq[i] = o;
+}
+
+}  // namespace
+
+hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t* wq, hipStream_t s) {
+  const int64_t n_words = N * (K / 16);
+  if (n_words == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prepare_mx4, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, s, wp, n_words, wq);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t* wq, const float* alpha, int64_t M,
+                          int64_t N, int64_t K, int out_kind, void* out, int64_t ldo, int cu_count, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int bn = g256 >= cu_count ? 256 : 128;
+  const int tm = (int)((M + 255) / 256), tn = (int)((N + bn - 1) / bn);
+  const int64_t G = (int64_t)tm * tn;
+  const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
+  const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+#define HBL_MX(OUT, BN)                                                                                          \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN>), dim3((unsigned)P), dim3(256), 0, s, c, scales, wq, alpha, M, N, K, \
+                     out, ldo, tm, tn)
+  if (bn == 256) {
+    if (out_kind == 0) HBL_MX(0, 256); else if (out_kind == 1) HBL_MX(1, 256); else HBL_MX(2, 256);
+  } else {
+    if (out_kind == 0) HBL_MX(0, 128); else if (out_kind == 1) HBL_MX(1, 128); else HBL_MX(2, 128);
+  }
+#undef HBL_MX
+  return hipGetLastError();
+}
+
+}  // namespace hbl

@@ -44,6 +44,33 @@ constexpr float kSqrt7 = 2.6457513110645907f;
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Four INT4 codes (the bytes of w, two's complement, in [-8, 7]) as four
+// 6-bit E3M2 floats (1 sign, 3 exponent bits with bias 3, 2 mantissa bits:
+// 1 = 0b001100, 2 = 0b010000, 3 = 0b010010, ..., 7 = 0b010111,
+// 8 = 0b011000), code j at bits 6 j of the 24-bit result.  The low nibble of
+// a code byte indexes a 16-entry table held in four words: entries 0..7
+// (codes 0..7) and 8..15 (codes -8..-1) are picked by byte permutes and
+// merged by the index's bit 3.
+__device__ __forceinline__ uint32_t mx6_chunk(uint32_t w) {
+  const uint32_t idx = w & 0x0f0f0f0fu;
+  const uint32_t sel = idx & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, sel);  // 0, 12, 16, 18, 20, 21, 22, 23
+  const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, sel);  // 56, 55, 54, 53, 52, 50, 48, 44
+  const uint32_t hb = (idx >> 3) & 0x01010101u;
+  const uint32_t m = (hb << 8) - hb;  // 0xff in the bytes of negative codes
+  const uint32_t b = (pos & ~m) | (neg & m);
+  return (b & 0x3fu) | ((b >> 2) & (0x3fu << 6)) | ((b >> 4) & (0x3fu << 12)) | ((b >> 6) & (0x3fu << 18));
+}
+
+// The 192-bit field of 32 codes from its eight 24-bit chunks (chunk i at
+// bit 24 i), stored MX6-style: the first 16 bytes at main, the last 8 at
+// tail.
+__device__ __forceinline__ void mx6_store(const uint32_t (&c)[8], uint8_t* main, uint8_t* tail) {
+  *reinterpret_cast<uint4*>(main) =
+      make_uint4(c[0] | (c[1] << 24), (c[1] >> 8) | (c[2] << 16), (c[2] >> 16) | (c[3] << 8), c[4] | (c[5] << 24));
+  *reinterpret_cast<uint2*>(tail) = make_uint2((c[5] >> 8) | (c[6] << 16), (c[6] >> 16) | (c[7] << 8));
+}
+
 // Loads 8 consecutive elements starting at p (16-byte aligned) as fp32.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* p, float* v) {
@@ -417,6 +444,10 @@ __device__ __forceinline__ int swz16(int e) {  // float index -> swizzled float 
 // layout (lane l holds 8 consecutive elements of chunk l % 32 of its column
 // group), and the result is written to LDS as groups of 4 consecutive
 // elements, in the same swizzled layout as the register path.
+// OUT: 0 = codes (BITS 8 or 4), 1 = fp32 rotated values, 2 = INT4 codes as
+// MX6 operands of the FP6 x FP4 matmul (BITS 4): per row, blocks of 128
+// codes in 96 bytes, group g of 32 codes as a 192-bit field (code e at bit
+// 6 e) whose first 16 bytes sit at byte 16 g, its last 8 at byte 64 + 8 g.
 template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 __global__ void __launch_bounds__(256, 2)
 k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
@@ -658,7 +689,24 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         return p01 | p23;
       };
       int qs[4] = {0, 0, 0, 0};  // four independent row-sum chains
-      if constexpr (!HAD) {
+      if constexpr (!HAD && OUT == 2) {
+        // the thread's 64 elements are contiguous: groups 2t and 2t + 1
+        uint32_t ch[2][8];
+#pragma unroll
+        for (int gi = 0; gi < 16; ++gi) {
+          const uint32_t w = quant4(v + 4 * gi);
+          qs[gi % 4] = __builtin_amdgcn_sdot4((int)w, 0x01010101, qs[gi % 4], false);
+          ch[gi / 8][gi % 8] = mx6_chunk(w);
+        }
+        if (live) {
+          uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + m * (int64_t)(K / 4 * 3);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * t + q;
+            mx6_store(ch[q], dst + 96 * (g >> 2) + 16 * (g & 3), dst + 96 * (g >> 2) + 64 + 8 * (g & 3));
+          }
+        }
+      } else if constexpr (!HAD) {
         // the thread's 64 elements are contiguous: pack and store directly
 #pragma unroll
         for (int gq = 0; gq < 8; ++gq) {
@@ -686,7 +734,9 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           const uint32_t w = quant4(v + 4 * gi);
           qs[gi % 4] = __builtin_amdgcn_sdot4((int)w, 0x01010101, qs[gi % 4], false);
           const int e = last_e(gi);
-          if constexpr (BITS == 8) {
+          if constexpr (OUT == 2) {
+            *reinterpret_cast<uint32_t*>(C8 + e) = mx6_chunk(w);  // one word per 4 codes, as for INT8
+          } else if constexpr (BITS == 8) {
             *reinterpret_cast<uint32_t*>(C8 + e) = w;
           } else {
             *reinterpret_cast<uint32_t*>(C8 + e) = (w & 0x0f0f0f0fu) << (4 * ((e >> 2) & 1));
@@ -694,7 +744,17 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         }
         __syncthreads();
         if (live) {
-          if constexpr (BITS == 8) {
+          if constexpr (OUT == 2) {
+            uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + m * (int64_t)(K / 4 * 3);
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const int g = t + T * qq;  // group of 32 codes: 8 chunk words
+              const uint4 a = *reinterpret_cast<const uint4*>(C8 + 32 * g);
+              const uint4 b = *reinterpret_cast<const uint4*>(C8 + 32 * g + 16);
+              const uint32_t ch[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+              mx6_store(ch, dst + 96 * (g >> 2) + 16 * (g & 3), dst + 96 * (g >> 2) + 64 + 8 * (g & 3));
+            }
+          } else if constexpr (BITS == 8) {
             int8_t* dst = reinterpret_cast<int8_t*>(codes) + m * (int64_t)K;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
@@ -834,9 +894,25 @@ hipError_t launch_fq(const void* x, int64_t M, int64_t ldx, void* codes, float* 
 }
 
 template <int LOG2K, bool NORM>
+hipError_t dispatch_quant_mx(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, void* codes,
+                             float* scales, int32_t* rowsum, const float* gain, int cu, hipStream_t s) {
+  if constexpr (LOG2K >= 10) {
+#define HBL_MXQ(B16, HAD) \
+  return launch_fq64<LOG2K, B16, 4, HAD, 2, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, cu, s)
+    if (bf16) { if (had) HBL_MXQ(true, true); else HBL_MXQ(true, false); }
+    else { if (had) HBL_MXQ(false, true); else HBL_MXQ(false, false); }
+#undef HBL_MXQ
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int LOG2K, bool NORM>
 hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, int bits,
                           void* codes, float* scales, int32_t* rowsum, const float* gain, int cu,
                           hipStream_t s) {
+  if constexpr (!NORM)  // MX6 codes are written without the normalisation layer
+    if (bits == 6) return dispatch_quant_mx<LOG2K, NORM>(x, bf16, M, ldx, had, codes, scales, rowsum, gain, cu, s);
 #define HBL_FQ(B16, BITS, HAD)                                                                              \
   if constexpr (LOG2K >= 10)                                                                                \
     return launch_fq64<LOG2K, B16, BITS, HAD, 0, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, cu, \
@@ -879,8 +955,10 @@ int ilog2(int K);
 template <bool NORM>
 hipError_t quant_by_k(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, bool hadamard, int bits,
                       void* codes, float* scales, int32_t* rowsum, const float* gain, int cu, hipStream_t s) {
-  if ((K & (K - 1)) != 0)  // only reachable without the rotation (the ABI layer rejects it otherwise)
+  if ((K & (K - 1)) != 0) {  // only reachable without the rotation (the ABI layer rejects it otherwise)
+    if (bits == 6) return hipErrorInvalidValue;  // MX6 codes: K a power of two >= 1024
     return launch_plain<NORM>(x, x_bf16, M, K, ldx, bits, codes, scales, rowsum, gain, s);
+  }
 #define HBL_QK(L) \
   case L: return dispatch_quant<L, NORM>(x, x_bf16, M, ldx, hadamard, bits, codes, scales, rowsum, gain, cu, s);
   switch (ilog2(K)) {

@@ -250,6 +250,67 @@ int hbl_ternarize_weights_rotated(const void* w, int w_dtype, int64_t N, int64_t
                                   uint32_t* w_packed, float* alpha, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* =====================================================================
+ * INT4 on the FP6 x FP4 matrix cores.
+ *
+ * INT4 activation codes in [-8, 7] are exact 6-bit floats E3M2 (OCP MX
+ * "BF6": sign, 3 exponent bits with bias 3, 2 mantissa bits) and ternary
+ * weights exact 4-bit floats E2M1 (sign, 2 exponent bits with bias 1, 1
+ * mantissa bit); every product is an integer of magnitude <= 8 and the
+ * fp32 accumulator of v_mfma_f32_32x32x64_f8f6f4 holds every partial sum
+ * exactly (|sum| <= 8 K < 2^24).  The matmul is therefore the same exact
+ * integer matmul as hbl_ternary_gemm (same int32 values, same bf16
+ * outputs), at twice the per-clock rate of the int8 matrix cores.  It is
+ * the INT4 path of Eq. 8-9 (§3.4) on gfx950's low-precision matrix cores.
+ *
+ * Operand layouts (bit-exact contract):
+ *   MX6 codes: per token row K * 3 / 4 bytes, in blocks of 128 codes (96
+ *       bytes).  Group g = 0..3 of a block holds codes 32 g .. 32 g + 31 as
+ *       a 192-bit little-endian field, code e at bits [6 e, 6 e + 6) as an
+ *       E3M2 float (0 = 0b000000, 1 = 0b001100, 2 = 0b010000,
+ *       3 = 0b010010, 4 = 0b010100, 5 = 0b010101, 6 = 0b010110,
+ *       7 = 0b010111, 8 = 0b011000, bit 5 the sign); the field's first 16
+ *       bytes sit at byte 16 g of the block, its last 8 at byte 64 + 8 g.
+ *   MX4 weights: uint32 [N][K/16]; word w holds k = 16 w .. 16 w + 15: for
+ *       n = 0..7, bit 4n+1 = (q[16w+n] != 0), bit 4n+3 = (q[16w+n] < 0),
+ *       bit 4n = (q[16w+8+n] != 0), bit 4n+2 = (q[16w+8+n] < 0), so that
+ *       word & 0xAAAAAAAA and (word << 1) & 0xAAAAAAAA are the E2M1 codes of
+ *       the two halves.  Same size as the ternary layout.
+ * ===================================================================== */
+
+/* hbl_prepare_weights_mx -- ternary layout (hbl_ternarize_weights) to the
+ * MX4 layout.  Offline, once per matrix.  Shapes: N >= 1, K % 16 == 0. */
+int hbl_prepare_weights_mx(const uint32_t* w_packed, int64_t N, int64_t K,
+                           uint32_t* w_mx, void* stream);
+
+/* hbl_hadamard_quant_mx -- hbl_hadamard_quant with bits = 4 (Eq. 8, after
+ * the rotation with HBL_HADAMARD), codes written in the MX6 layout:
+ * codes_mx [M][K * 3 / 4] bytes, scales [M] (beta / sqrt(7)).  The same
+ * codes and scales as hbl_hadamard_quant(..., bits = 4).
+ * Shapes: K a power of two, 1024 <= K <= HBL_MAX_K; ldx as there. */
+int hbl_hadamard_quant_mx(const void* x, int x_dtype, int64_t M, int64_t K,
+                          int64_t ldx, int flags, void* codes_mx, float* scales,
+                          void* stream);
+
+/* hbl_ternary_gemm_mx -- hbl_ternary_gemm for MX6 codes and MX4 weights:
+ *   out[m][n] = (scales[m] * alpha) * sum_k q_x[m][k] q_w[n][k]
+ * (HBL_OUT_I32: the exact sum).  No row sums are needed.
+ * Shapes: N >= 16, N % 16 == 0; K >= 512, K % 512 == 0; ldo as there. */
+int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales,
+                        const uint32_t* w_mx, const float* alpha, int64_t M,
+                        int64_t N, int64_t K, int out_dtype, void* out,
+                        int64_t ldo, void* stream);
+
+/* hbl_forward_mx -- the INT4 layer of Eq. 9 on this path:
+ * hbl_hadamard_quant_mx then hbl_ternary_gemm_mx (bf16 output), the same
+ * result as hbl_forward(..., bits = 4).  ws: at least
+ * hbl_forward_mx_workspace_size(M, K) bytes (MX6 codes and scales).
+ * Shapes: the union of the two calls' rules. */
+size_t hbl_forward_mx_workspace_size(int64_t M, int64_t K);
+int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                   int64_t N, int flags, const uint32_t* w_mx, const float* alpha,
+                   void* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

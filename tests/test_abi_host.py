@@ -183,3 +183,31 @@ def test_ternarize_rotated_errors(hbl):
     assert t(None, 0, 64, 256, B, C, D, need, None) == hbl.ERR_NULL
     assert t(A, 0, 64, 256, B, C, D, need - 1, None) == hbl.ERR_WORKSPACE
     assert t(A + 2, 0, 64, 256, B, C, D, need, None) == hbl.ERR_ALIGN
+
+
+def test_mx_entry_point_errors(hbl):
+    lib = hbl.lib()
+    q = lib.hbl_hadamard_quant_mx
+    assert q(A, 1, 4, 512, 512, 1, B, C, None) == hbl.ERR_SHAPE          # K below 1024
+    assert "FP6 x FP4" in last(hbl)
+    assert q(A, 1, 4, 3072, 3072, 0, B, C, None) == hbl.ERR_SHAPE        # not a power of two
+    assert q(A, 1, 4, 1024, 1024, 2, B, C, None) == hbl.ERR_MODE
+    assert q(A, 1, 4, 1024, 1024, 1, None, C, None) == hbl.ERR_NULL
+    assert q(A, 1, 0, 1024, 1024, 1, B, C, None) == hbl.OK
+    g = lib.hbl_ternary_gemm_mx
+    assert g(A, B, C, D, 4, 64, 768, 0, F, 64, None) == hbl.ERR_SHAPE     # K % 512
+    assert g(A, B, C, D, 4, 40, 1024, 0, F, 40, None) == hbl.ERR_SHAPE    # N % 16
+    assert g(A, B, C, D, 4, 64, 1024, 5, F, 64, None) == hbl.ERR_MODE
+    assert g(A, B, None, D, 4, 64, 1024, 0, F, 64, None) == hbl.ERR_NULL
+    assert g(A + 8, B, C, D, 4, 64, 1024, 0, F, 64, None) == hbl.ERR_ALIGN
+    assert g(A, B, C, D, 0, 64, 1024, 0, F, 64, None) == hbl.OK
+    need = lib.hbl_forward_mx_workspace_size(10, 1024)
+    assert need >= 10 * 768 + 40 and need % 256 == 0
+    f = lib.hbl_forward_mx
+    assert f(A, 1, 10, 1024, 1024, 64, 1, B, C, D, 64, E, need - 1, None) == hbl.ERR_WORKSPACE
+    assert f(A, 1, 10, 2048, 2048, 64, 1, B, C, D, 64, E, need, None) == hbl.ERR_WORKSPACE
+    assert f(A, 1, 10, 1024, 1024, 64, 1, None, C, D, 64, E, need, None) == hbl.ERR_NULL
+    p = lib.hbl_prepare_weights_mx
+    assert p(A, 64, 100, B, None) == hbl.ERR_SHAPE
+    assert p(None, 64, 256, B, None) == hbl.ERR_NULL
+    assert p(A, 64, 256, B + 4, None) == hbl.ERR_ALIGN

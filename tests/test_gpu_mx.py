@@ -1,0 +1,140 @@
+"""GPU parity of the INT4 path on the FP6 x FP4 matrix cores, through the C
+ABI: MX4 weight preparation, MX6 codes, the matmul (bit-exact int32 on the
+oracle's codes), and the whole layer against both the oracle and the int8
+matrix-core path (whose bf16 outputs it must reproduce bit for bit, since
+both compute the same exact integer sums and the same rescale)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mx_util
+import oracle
+import workloads
+from parity_util import bf16_to_f64, check_codes, check_output, check_scales, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(hbl, N, K, seed):
+    w = workloads.gaussian_weights(seed, N + K, N, K)
+    packed, alpha = hbl.ternarize_weights(to_device(w))
+    return w, packed, alpha, hbl.prepare_weights_mx(packed, K)
+
+
+@pytest.mark.parametrize("N,K", [(16, 512), (272, 1024), (4096, 4096)])
+def test_prepare_weights_mx(hbl, N, K):
+    w, packed, alpha, wq = _weights(hbl, N, K, 1)
+    _, _, q = oracle.ternarize(w)
+    assert np.array_equal(wq.cpu().numpy().view(np.uint32), mx_util.encode_mx4(q))
+
+
+@pytest.mark.parametrize("log2k", [10, 11, 12, 13, 14])
+@pytest.mark.parametrize("had", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_mx_codes(hbl, log2k, had, dtype):
+    K = 1 << log2k
+    x = workloads.random_rows(800 + log2k, 37, K, "t3", as_bf16=(dtype == "bf16"))
+    xd = to_device(x)
+    cm, sm = hbl.hadamard_quant_mx(xd, hadamard=had)
+    q4, s4, _ = hbl.hadamard_quant(xd, 4, hadamard=had)
+    torch.cuda.synchronize()
+    got = mx_util.decode_mx6(cm.cpu().numpy(), K)
+    # the same codes and scales as the INT4 layout, bit for bit
+    assert np.array_equal(got, oracle.unpack_int4(q4.cpu().numpy().view(np.uint32), K).astype(np.float64))
+    assert np.array_equal(sm.cpu().numpy(), s4.cpu().numpy())
+    # and the oracle's, to the code rule
+    oq, os_, _, xr = oracle.quantize(x, 4, hadamard=had, want_xr=True)
+    check_codes(got.astype(np.int8), oracle.unpack_int4(oq, K), xr, 4, f"mx K={K} had={had} {dtype}")
+    check_scales(sm.cpu().numpy(), os_, "mx scales")
+
+
+@pytest.mark.parametrize("M", [1, 5, 100, 256, 300])
+@pytest.mark.parametrize("N,K", [(16, 512), (48, 1024), (272, 2048)])
+def test_gemm_mx_exact_on_oracle_codes(hbl, M, N, K):
+    x = workloads.random_rows(M + N + K, M, K, "t3", as_bf16=True)
+    oq, os_, _ = oracle.quantize(x, 4, hadamard=False)
+    q8 = oracle.unpack_int4(oq, K)
+    w, packed, alpha, wq = _weights(hbl, N, K, 2)
+    codes = torch.from_numpy(mx_util.encode_mx6(q8)).cuda()
+    acc = hbl.ternary_gemm_mx(codes, torch.from_numpy(os_).cuda(), wq, alpha, K, out_dtype=hbl.OUT_I32)
+    o_packed, _, _ = oracle.ternarize(w)
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(oq, 4, o_packed, K))
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_gemm_mx_equals_int8_path(hbl, out_dtype):
+    M, N, K = 300, 528, 4096
+    x = to_device(workloads.random_rows(41, M, K, "t3"))
+    _, packed, alpha, wq = _weights(hbl, N, K, 3)
+    od = hbl.OUT_BF16 if out_dtype == "bf16" else hbl.OUT_F32
+    cm, sm = hbl.hadamard_quant_mx(x)
+    q4, s4, r4 = hbl.hadamard_quant(x, 4)
+    a = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=od)
+    b = hbl.ternary_gemm(q4, 4, s4, r4, packed, alpha, K, out_dtype=od)
+    assert torch.equal(a.view(torch.int16) if od == hbl.OUT_BF16 else a.view(torch.int32),
+                       b.view(torch.int16) if od == hbl.OUT_BF16 else b.view(torch.int32))
+
+
+def test_gemm_mx_strided_output(hbl):
+    M, N, K, pad = 261, 256, 1024, 8
+    x = to_device(workloads.random_rows(43, M, K, "t3"))
+    _, packed, alpha, wq = _weights(hbl, N, K, 4)
+    cm, sm = hbl.hadamard_quant_mx(x)
+    big = torch.full((M, N + pad), 7, dtype=torch.bfloat16, device="cuda")
+    hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out=big[:, :N])
+    ref = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K)
+    assert torch.equal(big[:, :N].contiguous().view(torch.int16), ref.view(torch.int16))
+    assert torch.all(big[:, N:] == 7)
+
+
+def test_forward_mx_small(hbl):
+    M, N, K = 70, 128, 1024
+    x_np = workloads.random_rows(45, M, K, "t3")
+    w, packed, alpha, wq = _weights(hbl, N, K, 5)
+    y = hbl.forward_mx(to_device(x_np), wq, alpha)
+    y_int = hbl.forward(to_device(x_np), packed, alpha, 4)
+    assert torch.equal(y.view(torch.int16), y_int.view(torch.int16))
+    o_packed, o_alpha, _ = oracle.ternarize(w)
+    check_output(bf16_to_f64(y), oracle.forward(x_np, o_packed, o_alpha, 4, hadamard=True), "forward_mx small")
+
+
+def test_forward_mx_zero_tokens(hbl):
+    _, packed, alpha, wq = _weights(hbl, 32, 1024, 6)
+    x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    assert hbl.forward_mx(x, wq, alpha).shape == (0, 32)
+
+
+@pytest.mark.parametrize("name", ["wo_7b", "wdown_7b"])
+def test_forward_mx_full_size(hbl, name):
+    c = getattr(workloads, name)()
+    x_np, w_np = c["x"], c["w"]
+    M, K = x_np.shape
+    packed, alpha = hbl.ternarize_weights(to_device(w_np))
+    wq = hbl.prepare_weights_mx(packed, K)
+    x = to_device(x_np)
+    y = hbl.forward_mx(x, wq, alpha)
+    y_int = hbl.forward(x, packed, alpha, 4)
+    assert torch.equal(y.view(torch.int16), y_int.view(torch.int16)), f"{name}: FP6 x FP4 and int8 paths differ"
+    del y_int
+    o_packed, o_alpha, _ = oracle.ternarize(w_np)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).choice(M, 6, replace=False)]))
+    y64 = oracle.forward(np.ascontiguousarray(x_np[rows]), o_packed, o_alpha, 4, hadamard=True)
+    check_output(bf16_to_f64(y[torch.from_numpy(rows).cuda()]), y64, f"{name} forward_mx")
+
+
+def test_gemm_mx_full_tile_grid_exact(hbl):
+    # 256 x 256 tiles (the grid fills the chip): int32 sums on sampled rows
+    M, N, K = 4096, 4096, 4096
+    x_np = workloads.random_rows(47, M, K, "t3")
+    w, packed, alpha, wq = _weights(hbl, N, K, 7)
+    cm, sm = hbl.hadamard_quant_mx(to_device(x_np))
+    acc = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=hbl.OUT_I32)
+    rows = np.array([0, 1, 255, 256, 2047, 4095])
+    oq, _, _ = oracle.quantize(np.ascontiguousarray(x_np[rows]), 4, hadamard=True)
+    gq = mx_util.decode_mx6(cm.cpu().numpy()[rows], K).astype(np.int8)
+    o_packed, _, _ = oracle.ternarize(w)
+    # on the GPU's own codes (identical to the oracle's up to ties)
+    assert np.array_equal(acc.cpu().numpy()[rows], oracle.gemm_i32(oracle.pack_int4(gq), 4, o_packed, K))
+    assert np.abs(gq.astype(int) - oracle.unpack_int4(oq, K).astype(int)).max() <= 1

@@ -492,3 +492,33 @@ def test_rotated_gaussian_weights_statistics():
     assert abs(alpha / (s * math.sqrt(2 / math.pi)) - 1) < 3e-3
     p0 = 2 * norm.cdf(0.5 * math.sqrt(2 / math.pi)) - 1
     assert abs((q == 0).mean() - p0) < 3e-3
+
+
+# ------------------------------------------- element formats of the FP6 x FP4 path
+# The test-side encoders of the MX6 / MX4 layouts derive their tables from
+# the OCP MX element-format definitions; pin those against hand-worked
+# values (E3M2: 7 = 1.75 * 2^2 -> exponent 5, mantissa 3 -> 0b010111).
+
+def test_e3m2_and_e2m1_tables():
+    import mx_util
+    assert mx_util.E3M2_OF[7] == 0b010111 and mx_util.E3M2_OF[-8] == 0b111000
+    assert mx_util.E3M2_OF[1] == 0b001100 and mx_util.E3M2_OF[3] == 0b010010
+    assert mx_util.e3m2_value(0b000001) == 0.0625  # subnormal: 2^-2 * 1/4
+    assert sorted(mx_util.E3M2_OF) == list(range(-8, 9))
+    assert mx_util.E2M1_OF == {0: 0, 1: 0b0010, -1: 0b1010}
+    assert mx_util.e2m1_value(0b0111) == 6.0
+
+
+def test_mx_layout_round_trips():
+    import mx_util
+    rng = np.random.default_rng(17)
+    q = rng.integers(-8, 8, (5, 512)).astype(np.int8)
+    b = mx_util.encode_mx6(q)
+    assert b.shape == (5, 384)
+    assert np.array_equal(mx_util.decode_mx6(b, 512), q.astype(np.float64))
+    # code e of group 1 of block 0 sits at bits 6 e of the field whose first
+    # 16 bytes start at byte 16 and whose last 8 start at byte 72
+    field = int.from_bytes(bytes(b[0, 16:32]) + bytes(b[0, 72:80]), "little")
+    assert all((field >> (6 * e)) & 63 == mx_util.E3M2_OF[int(q[0, 32 + e])] for e in range(32))
+    t = rng.integers(-1, 2, (7, 64)).astype(np.int8)
+    assert np.array_equal(mx_util.decode_mx4(mx_util.encode_mx4(t), 64), t.astype(np.float64))
