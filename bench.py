@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "H-BitLinear tokens/sec & effective TOPS at 7B shapes; % HBM BW / % i8 MFMA peak"
 HBM_PEAK_GBS = 8000.0
 I8_PEAK_TOPS = 5000.0
+MX_PEAK_TOPS = 10100.0  # dense FP6/FP4 matrix cores, vendor figure
 MEASURED = os.path.join(ROOT, "profiles", "measured.json")
 
 
@@ -60,7 +61,8 @@ def counter_traffic(workload, which):
     c = measured().get("counters", {}).get(workload)
     if not c:
         return None
-    src = {"gemm": "bit_quantization_amd/csrc/k_gemm.hip", "quant": "bit_quantization_amd/csrc/k_quant.hip"}[which]
+    src = {"gemm": "bit_quantization_amd/csrc/k_gemm.hip", "quant": "bit_quantization_amd/csrc/k_quant.hip",
+           "gemm_mx": "bit_quantization_amd/csrc/k_gemm_mx.hip", "quant_mx": "bit_quantization_amd/csrc/k_quant.hip"}[which]
     if _sha256(src) != c.get(f"{which}_source_sha256"):
         return None
     return c[f"{which}_hbm_read_bytes"] + c[f"{which}_hbm_write_bytes"]
@@ -80,6 +82,9 @@ def parse():
     ap.add_argument("--decode-mats", type=int, default=0,
                     help="distinct weight matrices cycled (0: enough for >= 512 MiB)")
     ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both)")
+    ap.add_argument("--path", default="auto", choices=["auto", "int8", "mx"],
+                    help="INT4 layers: int8 matrix cores, or FP6 x FP4 (mx); auto takes mx where it applies "
+                         "(INT4, K a power of two >= 1024, M > 256; smaller M stream the weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
@@ -179,20 +184,28 @@ def layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, reps):
     return t_q, t_g, q_bytes, code_bytes
 
 
-def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
-    M, K = x_np.shape
-    N = w_np.shape[0]
-    x = dev_x(x_np)
-    packed, alpha = hbl.ternarize_weights(torch.from_numpy(w_np).cuda())
-    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = hbl.forward_workspace(M, K, bits, "cuda")
+def layer_roofline_mx(hbl, x, wq, alpha, had, M, N, K, reps):
+    """Per-kernel timing of one layer on the FP6 x FP4 path."""
+    c, s = hbl.hadamard_quant_mx(x, hadamard=had)
+    out = hbl.ternary_gemm_mx(c, s, wq, alpha, K)
+    t_q = time_stream(lambda: hbl.hadamard_quant_mx(x, hadamard=had), reps)
+    t_g = time_stream(lambda: hbl.ternary_gemm_mx(c, s, wq, alpha, K, out=out), reps)
+    code_bytes = M * K * 3 // 4
+    q_bytes = M * K * x.element_size() + code_bytes + 4 * M
+    return t_q, t_g, q_bytes, code_bytes
 
-    def layer():
-        hbl.forward(x, packed, alpha, bits, hadamard=had, out=out, workspace=ws)
 
-    # A step is one whole-layer pass (both kernels).  A HIP graph holds `per`
-    # passes back to back, as a serving loop replays them (per divides the
-    # step count, so exactly `steps` passes are timed).
+def use_mx(args, bits, M, K):
+    if args.path == "int8" or bits != 4:
+        return False
+    ok = K >= 1024 and (K & (K - 1)) == 0 and K % 512 == 0
+    return ok and (args.path == "mx" or M > 256)
+
+
+def time_passes(args, torch, layer):
+    """Seconds per whole-layer pass: a HIP graph holds `per` passes back to
+    back, as a serving loop replays them (per divides the step count, so
+    exactly `steps` passes are timed)."""
     per = max(d for d in range(1, 11) if args.steps % d == 0)
 
     def passes():
@@ -208,9 +221,38 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
     for _ in range(args.steps // per):
         run()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    return (time.perf_counter() - t0) / args.steps, (f"hip graph of {per} passes" if g is not None else "eager")
 
-    t_q, t_g, q_bytes, code_bytes = layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, args.kernel_reps)
+
+def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
+    M, K = x_np.shape
+    N = w_np.shape[0]
+    x = dev_x(x_np)
+    packed, alpha = hbl.ternarize_weights(torch.from_numpy(w_np).cuda())
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mx = use_mx(args, bits, M, K)
+    ws = hbl.forward_workspace(M, K, bits, "cuda")
+
+    def layer_int8():
+        hbl.forward(x, packed, alpha, bits, hadamard=had, out=out, workspace=ws)
+
+    # A step is one whole-layer pass (both kernels) of the product path.
+    if mx:
+        wq = hbl.prepare_weights_mx(packed, K)
+        ws_mx = hbl.forward_mx_workspace(M, K, "cuda")
+
+        def layer():
+            hbl.forward_mx(x, wq, alpha, hadamard=had, out=out, workspace=ws_mx)
+    else:
+        layer = layer_int8
+    dt, launch = time_passes(args, torch, layer)
+
+    if mx:
+        t_q, t_g, q_bytes, code_bytes = layer_roofline_mx(hbl, x, wq, alpha, had, M, N, K, args.kernel_reps)
+        # the same layer on the int8 matrix cores, timed the same way, for comparison
+        dt_int8, _ = time_passes(args, torch, layer_int8)
+    else:
+        t_q, t_g, q_bytes, code_bytes = layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, args.kernel_reps)
     ops = 2.0 * M * N * K
     gemm_tops = ops / t_g / 1e12
     w_bytes = N * K // 4
@@ -219,6 +261,27 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
     int4_like = peaks.get("i8_mfma_tops_int4_like") if bits == 4 else peaks.get("i8_mfma_tops_int8_like")
     hbm_meas = peaks.get("hbm_read_gbs")
     wl = args.workload
+    if mx:
+        mx_best = peaks.get("fp6fp4_mfma_tops_best")
+        mx_like = peaks.get("fp6fp4_mfma_tops_int4_like")
+        roofline = {"bound": "mfma", "kernel": "k_gemm_mx (FP6 x FP4 ternary matmul)", "achieved": gemm_tops,
+                    "peak": MX_PEAK_TOPS, "unit": "TOP/s", "frac": gemm_tops / MX_PEAK_TOPS,
+                    "traffic": counter_traffic(wl, "gemm_mx"), "avg_kernel_us": t_g * 1e6,
+                    "algorithmic_ops_per_launch": ops,
+                    "measured_peak": {"fp6fp4_mfma_tops": mx_best, "frac": gemm_tops / mx_best if mx_best else None,
+                                      "fp6fp4_mfma_tops_same_operand_bits": mx_like,
+                                      "frac_same_operand_bits": gemm_tops / mx_like if mx_like else None,
+                                      "i8_mfma_tops": best, "frac_of_i8": gemm_tops / best if best else None,
+                                      "source": "profiles/peaks.md"}}
+    else:
+        roofline = {"bound": "mfma", "kernel": "k_gemm_pt (ternary matmul)", "achieved": gemm_tops,
+                    "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": gemm_tops / I8_PEAK_TOPS,
+                    "traffic": counter_traffic(wl, "gemm"), "avg_kernel_us": t_g * 1e6,
+                    "algorithmic_ops_per_launch": ops,
+                    "measured_peak": {"i8_mfma_tops": best, "frac": gemm_tops / best if best else None,
+                                      "i8_mfma_tops_same_operand_bits": int4_like,
+                                      "frac_same_operand_bits": gemm_tops / int4_like if int4_like else None,
+                                      "source": "profiles/peaks.md"}}
     res = {
         "metric": METRIC,
         "value": M / dt,
@@ -230,19 +293,13 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp6xfp4" if mx else "i8",
         "data": "synthetic",
         "config": {"workload": label, "M": M, "K": K, "N": N, "bits": bits, "hadamard": had,
-                   "x_dtype": "bf16" if x_np.dtype == np.uint16 else "f32"},
+                   "x_dtype": "bf16" if x_np.dtype == np.uint16 else "f32",
+                   "path": "FP6 x FP4 matrix cores (exact)" if mx else "int8 matrix cores"},
         "effective_tops": ops / dt / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_pt (ternary matmul)", "achieved": gemm_tops,
-                     "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": gemm_tops / I8_PEAK_TOPS,
-                     "traffic": counter_traffic(wl, "gemm"), "avg_kernel_us": t_g * 1e6,
-                     "algorithmic_ops_per_launch": ops,
-                     "measured_peak": {"i8_mfma_tops": best, "frac": gemm_tops / best if best else None,
-                                       "i8_mfma_tops_same_operand_bits": int4_like,
-                                       "frac_same_operand_bits": gemm_tops / int4_like if int4_like else None,
-                                       "source": "profiles/peaks.md"}},
+        "roofline": roofline,
         "fused": {"effective_tops": ops / dt / 1e12,
                   "frac_of_measured_i8_peak": ops / dt / 1e12 / best if best else None,
                   "frac_of_published_i8_peak": ops / dt / 1e12 / I8_PEAK_TOPS},
@@ -251,10 +308,13 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
                          "achieved_gbs": q_bytes / t_q / 1e9,
                          "frac": q_bytes / t_q / 1e9 / HBM_PEAK_GBS,
                          "frac_of_measured_read_peak": q_bytes / t_q / 1e9 / hbm_meas if hbm_meas else None,
-                         "traffic": counter_traffic(wl, "quant")},
+                         "traffic": counter_traffic(wl, "quant_mx" if mx else "quant")},
         "gemm_bytes_min": code_bytes + w_bytes + 2 * M * N,
-        "launch": f"hip graph of {per} passes" if g is not None else "eager",
+        "launch": launch,
     }
+    if mx:
+        res["int8_path"] = {"ms_per_step": dt_int8 * 1e3, "tokens_per_s": M / dt_int8,
+                            "effective_tops": ops / dt_int8 / 1e12}
     return res
 
 
@@ -395,16 +455,23 @@ def run_block(args, hbl, torch):
         out[name] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     results = []
     for bits in ([8, 4] if args.bits == 0 else [args.bits]):
+        mx = use_mx(args, bits, M, 4096)  # every input width here (4096, 16384) qualifies
         qbuf = {}
         for inp, had, layers in groups:
             K = dict(workloads.BLOCK_7B_INPUTS)[inp]
-            shape, dt = hbl.codes_shape(M, K, bits)
+            shape, dt = ((M, K // 4 * 3), torch.uint8) if mx else hbl.codes_shape(M, K, bits)
             qbuf[inp] = (torch.empty(shape, dtype=dt, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda"),
                          torch.empty(M, dtype=torch.int32, device="cuda"))
+        wmx = {name: hbl.prepare_weights_mx(ws[name][0], K) for name, K, N, had in workloads.BLOCK_7B_LAYERS} if mx else {}
 
         def quant(inp, had):
             q, sc, rs = qbuf[inp]
             x = xs[inp]
+            if mx:
+                hbl._check(hbl.lib().hbl_hadamard_quant_mx(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
+                                                           hbl.HADAMARD if had else 0, q.data_ptr(), sc.data_ptr(),
+                                                           hbl._stream()), "hbl_hadamard_quant_mx")
+                return
             hbl._check(hbl.lib().hbl_hadamard_quant(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
                                                     hbl.HADAMARD if had else 0, bits, q.data_ptr(), sc.data_ptr(),
                                                     rs.data_ptr(), hbl._stream()), "hbl_hadamard_quant")
@@ -413,7 +480,10 @@ def run_block(args, hbl, torch):
             q, sc, rs = qbuf[inp]
             p, a = ws[layer]
             K = dict(workloads.BLOCK_7B_INPUTS)[inp]
-            hbl.ternary_gemm(q, bits, sc, rs, p, a, K, out=out[layer])
+            if mx:
+                hbl.ternary_gemm_mx(q, sc, wmx[layer], a, K, out=out[layer])
+            else:
+                hbl.ternary_gemm(q, bits, sc, rs, p, a, K, out=out[layer])
 
         def step():
             for inp, had, layers in groups:
@@ -436,7 +506,8 @@ def run_block(args, hbl, torch):
                 per["gemm " + layer] = time_stream(lambda: gemm(inp, layer), args.kernel_reps) * 1e6
         ops = sum(2.0 * M * K * N for _, K, N, _ in workloads.BLOCK_7B_LAYERS)
         gemm_us = sum(v for k, v in per.items() if k.startswith("gemm"))
-        results.append({"bits": bits, "tokens_per_s": M / dt, "ms_per_step": dt * 1e3, "effective_tops": ops / dt / 1e12,
+        results.append({"bits": bits, "path": "FP6 x FP4 matrix cores" if mx else "int8 matrix cores",
+                        "tokens_per_s": M / dt, "ms_per_step": dt * 1e3, "effective_tops": ops / dt / 1e12,
                         "gemm_only_tops": ops / (gemm_us * 1e-6) / 1e12, "kernel_us": per})
     return {"metric": METRIC, "workload": "block_7b: the 7 linears of a 7B block, M=65536", "results": results}
 

@@ -5,6 +5,9 @@
 //     on register-resident operands, reading the same registers or rotating
 //     over four sets, for five kinds of operand bits (the datapath's
 //     switching activity, hence its power and clock, depends on them);
+//   * dense FP6 x FP4 matrix-core throughput (v_mfma_f32_32x32x64_f8f6f4,
+//     E2M1 first operand, E3M2 second: the INT4 matmul's formats), one and
+//     four waves per SIMD, for operands like the matmul's and random bits;
 //   * HBM read bandwidth: one streaming read of 2 GiB;
 //   * the streaming floor of one launch: graph replays of launches that each
 //     read 16 MiB or 4 MiB from buffers cycled through more memory than the
@@ -22,6 +25,9 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 #define CK(x)                                                                                  \
   do {                                                                                         \
@@ -82,6 +88,72 @@ __global__ void __launch_bounds__(256) k_mfma(int iters, const uint32_t* __restr
   if (threadIdx.x == 0) {
     clk[2 * blockIdx.x] = t1 - t0;
     clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// FP6 x FP4: per thread 40 words, four 4-word E2M1 operands then four
+// 6-word E3M2 operands, rotated as in k_mfma.
+template <int NACC>
+__global__ void __launch_bounds__(256) k_mfma_mx(int iters, const uint32_t* __restrict__ ops, int* __restrict__ sink,
+                                                 long long* __restrict__ clk) {
+  v4i a[4];
+  v6i b[4];
+  const uint32_t* src = ops + (size_t)(blockIdx.x * 256 + threadIdx.x) * 40;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = v4i{(int)src[4 * i], (int)src[4 * i + 1], (int)src[4 * i + 2], (int)src[4 * i + 3]};
+    b[i] = v6i{(int)src[16 + 6 * i], (int)src[17 + 6 * i], (int)src[18 + 6 * i], (int)src[19 + 6 * i],
+               (int)src[20 + 6 * i], (int)src[21 + 6 * i]};
+  }
+  const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  v16f acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = v16f{};
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) {
+        const v4i& x = a[(i + u) % 4];
+        const v6i& y = b[(i + 2 * u) % 4];
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1),
+                                                                 __builtin_shufflevector(y, y, 0, 1, 2, 3, 4, 5, -1, -1),
+                                                                 acc[i], 4, 3, 0, 0, 0, 0);
+      }
+  }
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) s += (int)acc[i][0] ^ (int)acc[i][15];
+  const long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// FP6 x FP4 operand bits, per thread 16 E2M1 words then 24 E3M2 words:
+//   0 like the INT4 matmul: E2M1 nibbles of random ternary weights, E3M2
+//     codes of random integers in [-8, 7] (one per byte)
+//   1 random bits
+__global__ void k_fill_mx(uint32_t* p, size_t n, int mode) {
+  static constexpr uint8_t kE3M2[16] = {56, 55, 54, 53, 52, 50, 48, 44, 0, 12, 16, 18, 20, 21, 22, 23};  // -8 .. 7
+  static constexpr uint8_t kE2M1[3] = {10, 0, 2};                                                     // -1, 0, 1
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    uint64_t z = (uint64_t)i * 0x9E3779B97F4A7C15ull + 777u;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    uint32_t v = (uint32_t)z;
+    if (mode == 0) {
+      v = 0;
+      if (i % 40 < 16) {
+        for (int j = 0; j < 8; ++j) v |= (uint32_t)kE2M1[((z >> (5 * j)) & 31) % 3] << (4 * j);
+      } else {
+        for (int j = 0; j < 4; ++j) v |= (uint32_t)kE3M2[(z >> (8 * j)) & 15] << (8 * j);
+      }
+    }
+    p[i] = v;
   }
 }
 
@@ -180,6 +252,40 @@ int main() {
       mfma(k_mfma<4, true, false>, "32x32x32 fixed regs", 65536.0, 4, mode, wps);
       mfma(k_mfma<4, true, true>, "32x32x32 rotating", 65536.0, 4, mode, wps);
     }
+  // ---- FP6 x FP4 matrix cores
+  {
+    const size_t nmx = (size_t)max_blocks * 256 * 40;
+    uint32_t* mx;
+    CK(hipMalloc(&mx, nmx * 4));
+    static const char* kMxData[] = {"INT4-like", "random"};
+    for (int wps : {1, 4})
+      for (int mode = 0; mode < 2; ++mode) {
+        const int blocks = wps * cus, iters = 2048, nacc = 4;
+        hipLaunchKernelGGL(k_fill_mx, dim3(1024), dim3(256), 0, 0, mx, nmx, mode);
+        hipLaunchKernelGGL(k_mfma_mx<4>, dim3(blocks), dim3(256), 0, 0, iters, mx, sink, clk);
+        CK(hipDeviceSynchronize());
+        hipEvent_t a, b;
+        CK(hipEventCreate(&a));
+        CK(hipEventCreate(&b));
+        const int reps = 5;
+        CK(hipEventRecord(a, 0));
+        for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(k_mfma_mx<4>, dim3(blocks), dim3(256), 0, 0, iters, mx, sink, clk);
+        CK(hipEventRecord(b, 0));
+        CK(hipEventSynchronize(b));
+        float ms;
+        CK(hipEventElapsedTime(&ms, a, b));
+        std::vector<long long> h((size_t)blocks * 2);
+        CK(hipMemcpy(h.data(), clk, h.size() * 8, hipMemcpyDeviceToHost));
+        double c = 0, r = 0;
+        for (size_t i = 0; i < h.size(); i += 2) { c += (double)h[i]; r += (double)h[i + 1]; }
+        const double total = (double)reps * blocks * 4 * iters * nacc * 131072.0;
+        const double ghz = c / (r * 10.0), tops = total / (ms * 1e-3) / 1e12;
+        std::printf("mfma fp4 x bf6 32x32x64 %d wave(s)/SIMD %-14s operands: %7.1f TOP/s at %.2f GHz (%.0f ops/clock/SIMD of 4096)\n",
+                    wps, kMxData[mode], tops, ghz, tops * 1e12 / (ghz * 1e9 * 4 * cus));
+        std::fflush(stdout);
+      }
+    CK(hipFree(mx));
+  }
   CK(hipFree(ops));
   CK(hipFree(sink));
   CK(hipFree(clk));
