@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both)")
     ap.add_argument("--path", default="auto", choices=["auto", "int8", "mx"],
                     help="INT4 layers: int8 matrix cores, or FP6 x FP4 (mx); auto takes mx where it applies "
-                         "(INT4, K a power of two >= 1024, M > 256; smaller M stream the weights)")
+                         "(INT4, K a power of two >= 1024, M > 128; smaller M stream the weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
@@ -199,7 +199,7 @@ def use_mx(args, bits, M, K):
     if args.path == "int8" or bits != 4:
         return False
     ok = K >= 1024 and (K & (K - 1)) == 0 and K % 512 == 0
-    return ok and (args.path == "mx" or M > 256)
+    return ok and (args.path == "mx" or M > 128)
 
 
 def time_passes(args, torch, layer):
@@ -381,19 +381,22 @@ def run_decode(args, hbl, torch):
 
 
 def run_msweep(args, hbl, torch):
-    """Layer time against the token count M = 1 ... 256 at the two 7B input
+    """Layer time against the token count M = 1 ... 4096 at the two 7B input
     widths (K = 4096 and 16384, N = 4096), for four layer kinds:
       bitlinear_a8   plain BitLinear, INT8 codes, no rotation (the b1.58 layer)
       hbitlinear_a8  H-BitLinear, INT8 codes
-      hbitlinear_a4  H-BitLinear, INT4 codes
+      hbitlinear_a4  H-BitLinear, INT4 codes, on the path the library takes
+                     for that M (weight streaming up to 128 tokens, then the
+                     FP6 x FP4 matmul)
       norm_hbitlinear_a4  H-BitLinear INT4 with the RMSNorm layer in front
+                     (int8 matrix cores)
     Each time is one whole layer call (quantisation kernel + matmul kernel),
     averaged over HIP-graph replays that cycle enough distinct weight
     matrices (>= 512 MiB) that the weights stream from HBM.  The break-even
-    batch is the smallest M at which the rotated INT4 layer is no slower than
-    the plain INT8 one."""
+    batch is the smallest M from which on the rotated INT4 layer is no slower
+    than the plain INT8 one."""
     import workloads
-    Ms = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+    Ms = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
     kinds = [("bitlinear_a8", 8, False, False), ("hbitlinear_a8", 8, True, False),
              ("hbitlinear_a4", 4, True, False), ("norm_hbitlinear_a4", 4, True, True)]
     table, breakeven = [], {}
@@ -403,37 +406,48 @@ def run_msweep(args, hbl, torch):
         base = [hbl.ternarize_weights(torch.from_numpy(workloads.decode_weights(K, N, i)).cuda()) for i in range(10)]
         mats = [(base[i % 10][0].clone(), base[i % 10][1].clone()) for i in range(n_mats)]
         del base
+        mats_mx = [hbl.prepare_weights_mx(p, K) for p, _ in mats]
         gain = torch.from_numpy(np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32)).cuda()
-        breakeven[K] = None
+        rows = []
         for M in Ms:
-            x = dev_x(workloads.decode_inputs(K, M))
+            x = dev_x(workloads.student_t_rows(workloads.SEEDS["decode"], 7000 + M, M, K, None, 1.0))
             out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             row = {"K": K, "N": N, "M": M}
             for name, bits, had, norm in kinds:
-                ws = hbl.forward_workspace(M, K, bits, "cuda")
+                mx = not norm and use_mx(args, bits, M, K)
+                ws = hbl.forward_mx_workspace(M, K, "cuda") if mx else hbl.forward_workspace(M, K, bits, "cuda")
 
                 def all_mats():
-                    for p, a in mats:
-                        if norm:
+                    for (p, a), q in zip(mats, mats_mx):
+                        if mx:
+                            hbl.forward_mx(x, q, a, hadamard=had, out=out, workspace=ws)
+                        elif norm:
                             hbl.norm_forward(x, p, a, bits, gain=gain, hadamard=had, out=out, workspace=ws)
                         else:
                             hbl.forward(x, p, a, bits, hadamard=had, out=out, workspace=ws)
 
                 t = time_stream(all_mats, 2) / n_mats
                 row[f"{name}_us"] = t * 1e6
+                if name == "hbitlinear_a4":
+                    row["a4_path"] = "FP6 x FP4" if mx else ("weight streaming" if M <= 128 else "int8 matrix cores")
             row["rotation_overhead_a8"] = row["hbitlinear_a8_us"] / row["bitlinear_a8_us"] - 1.0
             row["a4_vs_bitlinear_a8"] = row["hbitlinear_a4_us"] / row["bitlinear_a8_us"]
-            if breakeven[K] is None and row["hbitlinear_a4_us"] <= row["bitlinear_a8_us"]:
-                breakeven[K] = M
-            table.append(row)
+            rows.append(row)
             print(json.dumps({"progress": row}), file=sys.stderr, flush=True)
-        del mats
+            del x, out
+        breakeven[K] = None
+        for i in range(len(rows)):
+            if all(r["hbitlinear_a4_us"] <= r["bitlinear_a8_us"] for r in rows[i:]):
+                breakeven[K] = rows[i]["M"]
+                break
+        table += rows
+        del mats, mats_mx
         torch.cuda.empty_cache()
     return {
         "metric": "H-BitLinear vs BitLinear layer time over the token count (break-even batch)",
-        "value": breakeven[4096], "unit": "tokens (smallest M where H-BitLinear INT4 <= BitLinear INT8, K=4096)",
+        "value": breakeven[16384], "unit": "tokens (smallest M from which H-BitLinear INT4 <= BitLinear INT8, K=16384)",
         "n_gpus": 1, "higher_is_better": False, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": "msweep: M = 1..256, K in {4096, 16384}, N = 4096, weights cycled from HBM"},
+        "config": {"workload": "msweep: M = 1..4096, K in {4096, 16384}, N = 4096, weights cycled from HBM"},
         "breakeven_m": {str(k): v for k, v in breakeven.items()}, "sweep": table,
     }
 

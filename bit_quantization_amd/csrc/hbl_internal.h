@@ -41,6 +41,6 @@ hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t
                               hipStream_t s);
 
 // Token counts up to this take the weight-streaming kernel.
-constexpr int kGemvMaxM = 16;
+constexpr int kGemvMaxM = 128;
 
 }  // namespace hbl

@@ -12,11 +12,12 @@
 //     c = q + 1 in {0, 1, 2}, so the MFMA sums q_x * c; the epilogue
 //     subtracts sum_k q_x (the token's row sum of codes) to obtain
 //     sum_k q_x * q_w exactly.
-//   k_gemv -- token counts up to 16 (decode).  Bandwidth-bound: each block
+//   k_gemv -- token counts up to 128 (decode and small batches).  Each block
 //     owns 16 output features and streams their packed weights once with
 //     16-byte loads; the 4 waves of a block split K and are reduced through
-//     LDS.  The tokens are the 16 columns of the MFMA's second operand
-//     (columns beyond M are zero).
+//     LDS.  The tokens, in groups of 16, are the 16 columns of the MFMA's
+//     second operand (columns beyond M are zero); each decoded weight
+//     fragment serves every group.
 //
 // In both kernels the MFMA's first operand is the weight fragment and its
 // second the activation fragment, so each lane ends with four consecutive
@@ -630,22 +631,26 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
 // Decode: M <= 16 tokens, one block per 16 output features.
 constexpr int kGemvBatch = 8;  // 16-byte weight loads in flight per lane
 
-template <int BITS, int OUT>
+// MG groups of 16 tokens (M <= 16 MG): every block streams its 16 features'
+// weights once and applies each decoded weight fragment to all token groups,
+// whose codes are read from the L2 (every block reads all of them).
+template <int BITS, int OUT, int MG>
 __global__ void __launch_bounds__(256)
 k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
        const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
        const float* __restrict__ alpha, int M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo) {
-  __shared__ v4i red[3][64];
+  __shared__ v4i red[MG][3][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int fr = lane % 16, g = lane / 16;
   const int64_t KW = K / 16;
   const int64_t steps = (KW + 15) / 16;  // a step is 16 words (256 k) per row
   const uint32_t* wrow = wp + (n0 + fr) * KW;
-  const bool mlive = fr < M;
 
-  v4i acc = {0, 0, 0, 0};
+  v4i acc[MG];
+#pragma unroll
+  for (int tg = 0; tg < MG; ++tg) acc[tg] = v4i{0, 0, 0, 0};
   for (int64_t s0 = wave; s0 < steps; s0 += 4 * kGemvBatch) {
     uint4 w[kGemvBatch];
 #pragma unroll
@@ -660,51 +665,66 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
       // Skip only whole steps (a wave-uniform test): an MFMA always runs on
       // all 64 lanes, so lanes past the end of K feed zeros instead.
       if (s0 + 4 * b >= steps) continue;
-      // activation codes for k = 16*kw .. 16*kw + 63 of token fr
-      uint32_t x[16];
-      if (mlive && kw < KW) {
-        if constexpr (BITS == 8) {
-          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + fr * K + 16 * kw);
+      const uint32_t ws[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
+      v4i a[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 u = p[i];
-            x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
-          }
-        } else {
-          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(codes) + fr * (K / 8) + 2 * kw);
+      for (int i = 0; i < 4; ++i)
+        a[i] = v4i{(int)(ws[i] & 0x03030303u), (int)((ws[i] >> 2) & 0x03030303u),
+                   (int)((ws[i] >> 4) & 0x03030303u), (int)((ws[i] >> 6) & 0x03030303u)};
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const uint4 u = p[i];
-            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+      for (int tg = 0; tg < MG; ++tg) {
+        const int tok = 16 * tg + fr;
+        if (MG > 1 && 16 * tg >= M) break;  // wave-uniform: no token of this group
+        // activation codes for k = 16*kw .. 16*kw + 63 of token tok
+        uint32_t x[16];
+        if (tok < M && kw < KW) {
+          if constexpr (BITS == 8) {
+            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + tok * K + 16 * kw);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              x[8 * i + 2 * q] = sext_nibbles(ww[q] & 0x0f0f0f0fu);
-              x[8 * i + 2 * q + 1] = sext_nibbles((ww[q] >> 4) & 0x0f0f0f0fu);
+            for (int i = 0; i < 4; ++i) {
+              const uint4 u = p[i];
+              x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+            }
+          } else {
+            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(codes) + tok * (K / 8) + 2 * kw);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint4 u = p[i];
+              const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                x[8 * i + 2 * q] = sext_nibbles(ww[q] & 0x0f0f0f0fu);
+                x[8 * i + 2 * q + 1] = sext_nibbles((ww[q] >> 4) & 0x0f0f0f0fu);
+              }
             }
           }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = 0;
         }
-      } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = 0;
-      }
-      const uint32_t ws[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i a = {(int)(ws[i] & 0x03030303u), (int)((ws[i] >> 2) & 0x03030303u),
-                       (int)((ws[i] >> 4) & 0x03030303u), (int)((ws[i] >> 6) & 0x03030303u)};
-        const v4i bx = {(int)x[4 * i], (int)x[4 * i + 1], (int)x[4 * i + 2], (int)x[4 * i + 3]};
-        acc = mfma16x16x64(a, bx, acc);
+        for (int i = 0; i < 4; ++i) {
+          const v4i bx = {(int)x[4 * i], (int)x[4 * i + 1], (int)x[4 * i + 2], (int)x[4 * i + 3]};
+          acc[tg] = mfma16x16x64(a[i], bx, acc[tg]);
+        }
       }
     }
   }
-  if (wave > 0) red[wave - 1][lane] = acc;
+#pragma unroll
+  for (int tg = 0; tg < MG; ++tg)
+    if (wave > 0) red[tg][wave - 1][lane] = acc[tg];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) acc += red[i][lane];
-    if (fr < M) {
-      const float sc = scales[fr] * *alpha;
-      store4<OUT>(out, fr * ldo + n0 + 4 * g, acc, rowsum[fr], sc);
+    for (int tg = 0; tg < MG; ++tg) {
+      v4i t = acc[tg];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) t += red[tg][i][lane];
+      const int tok = 16 * tg + fr;
+      if (tok < M) {
+        const float sc = scales[tok] * *alpha;
+        store4<OUT>(out, tok * ldo + n0 + 4 * g, t, rowsum[tok], sc);
+      }
     }
   }
 }
@@ -882,8 +902,17 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 #undef HBL_DOT
   }
   if (M <= kGemvMaxM) {
-    hipLaunchKernelGGL((k_gemv<BITS, OUT>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales,
-                       rowsum, wp, alpha, (int)M, N, K, out, ldo);
+    // weight streaming with the tokens in groups of 16: every CU busy (one
+    // block per 16 features) where the matrix-core tiles would leave most
+    // of them idle
+#define HBL_GV(MG)                                                                                              \
+  hipLaunchKernelGGL((k_gemv<BITS, OUT, MG>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales, rowsum, wp, \
+                     alpha, (int)M, N, K, out, ldo)
+    if (M <= 16) HBL_GV(1);
+    else if (M <= 32) HBL_GV(2);
+    else if (M <= 64) HBL_GV(4);
+    else HBL_GV(8);
+#undef HBL_GV
     return hipGetLastError();
   }
   if (K % 512 == 0) {

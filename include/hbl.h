@@ -195,8 +195,9 @@ int hbl_norm_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
  *            HBL_OUT_I32 writes acc itself (for exact checks).
  * out: [M][ldo] of out_dtype; ldo >= N, ldo % 4 == 0.
  * Shapes: N >= 16, N % 16 == 0, K >= 64, K % 64 == 0.
- * Token counts M <= 16 take a bandwidth-oriented kernel that streams the
- * weights once; larger M take the matrix-core kernel.
+ * Token counts M <= 128 take a kernel that streams the weights once (one
+ * block per 16 output features, the tokens in groups of 16); larger M take
+ * the matrix-core tile kernel.
  * ------------------------------------------------------------------- */
 int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
                      const int32_t* rowsum, const uint32_t* w_packed,

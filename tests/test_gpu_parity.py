@@ -134,7 +134,7 @@ def _dev_codes(codes, bits):
     return torch.from_numpy(codes).cuda() if bits == 8 else torch.from_numpy(codes.view(np.int32)).cuda()
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 17, 100, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 17, 33, 100, 129, 256, 300])
 @pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (256, 256), (272, 1024), (64, 2048)])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_gemm_exact_on_oracle_codes(hbl, M, N, K, bits):
