@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         _lib.hbo_norm_quantize.argtypes = [P, I, I64, I64, I64, P, I, I, P, P, P, P]
         _lib.hbo_hadamard_backward.argtypes = [P, I, I64, I64, I64, P]
         _lib.hbo_ternarize_rotated.argtypes = [P, I, I64, I64, P, P, P, P]
+        _lib.hbo_kv_quant.argtypes = [P, I, I64, I64, I64, I64, I, I, P, P, P, P]
+        _lib.hbo_kv_dequant.argtypes = [P, P, I64, I64, I, P]
         _lib.hbo_ternarize.argtypes = [P, I, I64, I64, P, P, P]
         _lib.hbo_gemm_i32.argtypes = [P, I, P, I64, I64, I64, P]
         _lib.hbo_dequant_output.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
@@ -269,3 +271,28 @@ def f32_to_bf16(a: np.ndarray) -> np.ndarray:
     f = lib().hbo_f32_to_bf16
     flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
     return np.array([f(float(v)) for v in flat], np.uint16).reshape(np.shape(a))
+
+
+def kv_quant(x: np.ndarray, bits: int, keep_bos8: bool = True):
+    """Post-RoPE QKV / KV-cache quantiser on x [B][S][H][D] (fp32 or bf16
+    bits).  Returns (codes uint8 [B][S][H][D*bits/8], scales [B][S][H],
+    bos_codes uint8 [B][H][D], bos_scales [B][H]); the BOS arrays are zero
+    without keep_bos8."""
+    x = np.ascontiguousarray(x)
+    B, S, H, D = x.shape
+    codes = np.zeros((B, S, H, D * bits // 8), np.uint8)
+    scales = np.zeros((B, S, H), np.float32)
+    bos = np.zeros((B, H, D), np.uint8)
+    bos_s = np.zeros((B, H), np.float32)
+    _check(lib().hbo_kv_quant(_p(x), _dtype_code(x), B, S, H, D, bits, int(keep_bos8), _p(codes), _p(scales),
+                              _p(bos), _p(bos_s)), "kv_quant")
+    return codes, scales, bos, bos_s
+
+
+def kv_dequant(codes: np.ndarray, scales: np.ndarray, D: int, bits: int) -> np.ndarray:
+    """(u - 2^(b-1)) * scale per group; codes [..][D*bits/8], scales [..]."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, D * bits // 8)
+    sc = np.ascontiguousarray(scales, dtype=np.float32).reshape(-1)
+    out = np.empty((c.shape[0], D), np.float64)
+    _check(lib().hbo_kv_dequant(_p(c), _p(sc), c.shape[0], D, bits, _p(out)), "kv_dequant")
+    return out.reshape(tuple(scales.shape) + (D,))

@@ -483,6 +483,99 @@ int hbo_forward(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
   return rc;
 }
 
+/* ------------------------------------------------------------------ */
+/* Post-RoPE QKV / KV-cache quantiser  [BNv2 §3.4 "QKV Attention       */
+/* Quantization: Post-RoPE INT4/3-bit"]                                 */
+/* ------------------------------------------------------------------ */
+
+/* Reading (the pages say "unsigned integers using the absmax function" and
+ * describe the unsigned range as the signed one shifted): each group of D
+ * elements (one head of one token) is quantised with the absmax quantiser
+ * of Eq. 7 at b bits, Q = 2^(b-1) - 1:
+ *   gamma = max |x|,  v = RoundClip(x * Q / (gamma + eps), -2^(b-1), 2^(b-1) - 1),
+ *   u = v + 2^(b-1) in [0, 2^b - 1],   scale = gamma / Q,
+ * so x ~ (u - 2^(b-1)) * scale.  The factor Q/(gamma+eps) is one fp32 value
+ * per group, as in Eq. 7.
+ * Packing (bit-exact contract with the library): b = 8 one byte per code;
+ * b = 4 two codes per byte, code 2i in the low nibble; b = 3 eight codes per
+ * three bytes, code j of the group of 8 at bits [3j, 3j + 3) of the 24-bit
+ * little-endian value.  A group of D codes takes D * b / 8 bytes. */
+static void kv_quant_group(const void *x, int x_dtype, int64_t off, int64_t D, int bits,
+                           uint8_t *codes, float *scale) {
+  float gamma = 0.0f;
+  for (int64_t k = 0; k < D; k++) {
+    float a = fabsf(load_elem(x, x_dtype, off + k));
+    if (a > gamma) gamma = a;
+  }
+  const int half = 1 << (bits - 1);
+  const float q = (float)(half - 1);
+  const float f = q / (gamma + HBO_EPS);
+  *scale = gamma / q;
+  memset(codes, 0, (size_t)(D * bits / 8));
+  for (int64_t k = 0; k < D; k++) {
+    const float v = round_clip(load_elem(x, x_dtype, off + k) * f, (float)-half, (float)(half - 1));
+    const unsigned u = (unsigned)((int)v + half);
+    if (bits == 8) {
+      codes[k] = (uint8_t)u;
+    } else if (bits == 4) {
+      codes[k / 2] |= (uint8_t)(u << (4 * (k % 2)));
+    } else {
+      const int64_t g = k / 8, j = k % 8, bit = 24 * g + 3 * j;
+      for (int t = 0; t < 3; t++)
+        if ((u >> t) & 1u) codes[(bit + t) / 8] |= (uint8_t)(1u << ((bit + t) % 8));
+    }
+  }
+}
+
+/* x: [B][S][H][D] (fp32 or bf16), contiguous.  codes: [B][S][H][D*bits/8]
+ * bytes, scales: [B][S][H].  With keep_bos8, position 0 of every sequence
+ * (the [BOS] token, whose KV heads the pages keep at 8 bits) is also
+ * quantised at 8 bits into bos_codes [B][H][D] and bos_scales [B][H].
+ * Returns 0, or 2 for a bad shape / mode. */
+int hbo_kv_quant(const void *x, int x_dtype, int64_t B, int64_t S, int64_t H, int64_t D, int bits,
+                 int keep_bos8, uint8_t *codes, float *scales, uint8_t *bos_codes, float *bos_scales) {
+  if (B < 0 || S < 1 || H < 1 || D < 8 || D % 8 != 0) return 2;
+  if (bits != 3 && bits != 4 && bits != 8) return 2;
+  const int64_t cb = D * bits / 8;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < B * S; t++) {
+    for (int64_t h = 0; h < H; h++) {
+      const int64_t g = t * H + h;
+      kv_quant_group(x, x_dtype, g * D, D, bits, codes + g * cb, scales + g);
+      if (keep_bos8 && t % S == 0) {
+        const int64_t b = t / S;
+        kv_quant_group(x, x_dtype, g * D, D, 8, bos_codes + (b * H + h) * D, bos_scales + b * H + h);
+      }
+    }
+  }
+  return 0;
+}
+
+/* Inverse of the packing and the shift: x_hat = (u - 2^(b-1)) * scale, fp64
+ * [G][D] for G groups. */
+int hbo_kv_dequant(const uint8_t *codes, const float *scales, int64_t G, int64_t D, int bits, double *x_hat) {
+  if (G < 0 || D < 8 || D % 8 != 0 || (bits != 3 && bits != 4 && bits != 8)) return 2;
+  const int64_t cb = D * bits / 8;
+  const int half = 1 << (bits - 1);
+  for (int64_t g = 0; g < G; g++) {
+    const uint8_t *c = codes + g * cb;
+    for (int64_t k = 0; k < D; k++) {
+      unsigned u;
+      if (bits == 8) {
+        u = c[k];
+      } else if (bits == 4) {
+        u = (c[k / 2] >> (4 * (k % 2))) & 15u;
+      } else {
+        const int64_t bit = 24 * (k / 8) + 3 * (k % 8);
+        u = 0;
+        for (int t = 0; t < 3; t++) u |= (unsigned)((c[(bit + t) / 8] >> ((bit + t) % 8)) & 1u) << t;
+      }
+      x_hat[g * D + k] = ((double)u - half) * (double)scales[g];
+    }
+  }
+  return 0;
+}
+
 /* Number of OpenMP threads the parallel loops above use (1 without OpenMP). */
 int hbo_num_threads(void) {
 #ifdef _OPENMP

@@ -522,3 +522,72 @@ def test_mx_layout_round_trips():
     assert all((field >> (6 * e)) & 63 == mx_util.E3M2_OF[int(q[0, 32 + e])] for e in range(32))
     t = rng.integers(-1, 2, (7, 64)).astype(np.int8)
     assert np.array_equal(mx_util.decode_mx4(mx_util.encode_mx4(t), 64), t.astype(np.float64))
+
+
+# ------------------------------------------- QKV / KV-cache quantiser (f4)
+# Reading: Eq. 7's absmax quantiser at b bits, Q = 2^(b-1) - 1, shifted into
+# [0, 2^b - 1] (the pages' "unsigned integers using the absmax function").
+# Pins: a hand-worked head (golden/kv_quant_cases.txt), the range and the
+# position of the extreme element, zero at the zero point, the rounding
+# bound |x - x_hat| <= scale / 2, the uniform-noise closed form of the mean
+# squared error, and the [BOS] copy at 8 bits.
+
+def test_golden_kv_quant_case():
+    _, kv = read_golden("kv_quant_cases.txt")
+    x = np.array([float(v) for v in kv["x"]], np.float32).reshape(1, 1, 1, 8)
+    for b in (3, 4):
+        codes, scales, _, _ = oracle.kv_quant(x, b, keep_bos8=False)
+        assert codes.ravel().tolist() == [int(v) for v in kv[f"b{b}.bytes"]]
+        assert abs(float(scales.ravel()[0]) - float(kv[f"b{b}.scale"][0])) < 1e-7
+        # the packed bytes decode to the listed codes
+        xh = oracle.kv_dequant(codes, scales, 8, b).ravel()
+        u = np.rint(xh / float(scales.ravel()[0])).astype(int) + (1 << (b - 1))
+        assert u.tolist() == [int(v) for v in kv[f"b{b}.codes"]]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_kv_quant_invariants(bits):
+    rng = np.random.default_rng(60 + bits)
+    B, S, H, D = 2, 5, 3, 128
+    x = (rng.standard_normal((B, S, H, D)) * rng.uniform(0.1, 10, (B, S, H, 1))).astype(np.float32)
+    x[0, 1, 2] = 0.0                       # an all-zero head
+    codes, scales, _, _ = oracle.kv_quant(x, bits, keep_bos8=False)
+    half, q = 1 << (bits - 1), (1 << (bits - 1)) - 1
+    xh = oracle.kv_dequant(codes, scales, D, bits)
+    gamma = np.abs(x).max(axis=-1)
+    np.testing.assert_allclose(scales, gamma / q, rtol=1e-6)
+    u = np.rint(np.where(scales[..., None] > 0, xh / np.maximum(scales[..., None], 1e-30), 0)).astype(int) + half
+    assert u.min() >= 0 and u.max() <= (1 << bits) - 1
+    # the extreme element of every non-zero head sits at half +- q
+    idx = np.abs(x).argmax(axis=-1)
+    ext = np.take_along_axis(u, idx[..., None], axis=-1)[..., 0]
+    nz = gamma > 0
+    assert np.all(np.isin(ext[nz], [half - q, half + q]))
+    assert np.all(u[0, 1, 2] == half) and scales[0, 1, 2] == 0
+    # rounding bound (no element clips: |x f| <= q < half)
+    err = np.abs(xh - x.astype(np.float64))
+    assert np.all(err <= scales[..., None].astype(np.float64) * (0.5 + 1e-5) + 1e-12)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_kv_quant_mse_closed_form(bits):
+    # rounding noise uniform on [-s/2, s/2]: E|x - x_hat|^2 = s^2 / 12
+    rng = np.random.default_rng(70 + bits)
+    x = rng.standard_normal((4, 64, 8, 128)).astype(np.float32)
+    codes, scales, _, _ = oracle.kv_quant(x, bits, keep_bos8=False)
+    xh = oracle.kv_dequant(codes, scales, 128, bits)
+    mse = ((xh - x) ** 2).mean(axis=-1)
+    ratio = mse.mean() / (scales.astype(np.float64) ** 2 / 12).mean()
+    assert abs(ratio - 1) < 0.05
+
+
+def test_kv_quant_bos_kept_at_8_bits():
+    rng = np.random.default_rng(80)
+    B, S, H, D = 3, 4, 2, 64
+    x = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    codes, scales, bos, bos_s = oracle.kv_quant(x, 3, keep_bos8=True)
+    c8, s8, _, _ = oracle.kv_quant(np.ascontiguousarray(x[:, :1]), 8, keep_bos8=False)
+    assert np.array_equal(bos, c8[:, 0]) and np.array_equal(bos_s, s8[:, 0])
+    # the low-bit slot of position 0 is written too
+    c3, _, _, _ = oracle.kv_quant(np.ascontiguousarray(x[:, :1]), 3, keep_bos8=False)
+    assert np.array_equal(codes[:, :1], c3)
