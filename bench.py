@@ -12,9 +12,10 @@ back-to-back launches on the stream it runs on; ``cpu_baseline`` is the CPU
 oracle timed on a bounded sample of rows of the same workload.
 
 Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b,
-msweep (layer time over token counts 1-256 for BitLinear INT8 against
+msweep (layer time over token counts 1-4096 for BitLinear INT8 against
 H-BitLinear INT8/INT4, and the break-even batch where the rotated INT4 layer
-catches up), and copy (a plain device copy of known size, to calibrate the
+catches up), kvcache (the post-RoPE K/V quantiser on one 7B layer's cache
+states), and copy (a plain device copy of known size, to calibrate the
 HBM traffic counters).
 """
 from __future__ import annotations
@@ -74,14 +75,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wo_7b",
-                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "msweep", "copy"])
+                    choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "msweep", "kvcache", "copy"])
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="copy: bytes moved per launch (calibrates the HBM traffic counters)")
     ap.add_argument("--decode-m", type=int, default=1)
     ap.add_argument("--decode-k", type=int, default=16384)
     ap.add_argument("--decode-mats", type=int, default=0,
                     help="distinct weight matrices cycled (0: enough for >= 512 MiB)")
-    ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both)")
+    ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both); kvcache: 3 or 4 (0: 4)")
     ap.add_argument("--path", default="auto", choices=["auto", "int8", "mx"],
                     help="INT4 layers: int8 matrix cores, or FP6 x FP4 (mx); auto takes mx where it applies "
                          "(INT4, K a power of two >= 1024, M > 128; smaller M stream the weights)")
@@ -452,6 +453,48 @@ def run_msweep(args, hbl, torch):
     }
 
 
+def run_kvcache(args, hbl, torch):
+    """The post-RoPE QKV / KV-cache quantiser on one 7B layer's K and V
+    states: 64 sequences x 1024 positions x 32 heads x 128 (bf16), b-bit
+    codes with the [BOS] position kept at 8 bits.  A step quantises K and V."""
+    import workloads
+    B, S, H, D = 64, 1024, 32, 128
+    bits = args.bits if args.bits in (3, 4) else 4
+    rows = B * S * H
+    kv = []
+    for i in range(2):
+        x_np = workloads.student_t_rows(workloads.SEEDS["decode"], 9000 + i, rows, D, None, 1.0)
+        kv.append(dev_x(x_np).view(B, S, H, D))
+    outs = [(torch.empty((B, S, H, D * bits // 8), dtype=torch.uint8, device="cuda"),
+             torch.empty((B, S, H), dtype=torch.float32, device="cuda"),
+             torch.empty((B, H, D), dtype=torch.uint8, device="cuda"),
+             torch.empty((B, H), dtype=torch.float32, device="cuda")) for _ in range(2)]
+
+    def quant(i):
+        c, s_, bc, bs = outs[i]
+        x = kv[i]
+        hbl._check(hbl.lib().hbl_kv_quant(x.data_ptr(), hbl.DTYPE_BF16, B, S, H, D, bits, 1, c.data_ptr(),
+                                          s_.data_ptr(), bc.data_ptr(), bs.data_ptr(), hbl._stream()),
+                   "hbl_kv_quant")
+
+    dt, launch = time_passes(args, torch, lambda: (quant(0), quant(1)))
+    t_k = time_stream(lambda: quant(0), args.kernel_reps)
+    elems = B * S * H * D
+    k_bytes = elems * 2 + elems * bits // 8 + 4 * B * S * H + B * H * (D + 4)
+    gbs = k_bytes / t_k / 1e9
+    hbm = measured().get("peaks", {}).get("hbm_read_gbs")
+    return {"metric": "post-RoPE K/V cache quantiser throughput", "value": B * S / dt, "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"kvcache: K and V of one 7B layer, {B} x {S} positions x {H} heads x {D}, "
+                                   f"{bits}-bit codes, BOS at 8 bits", "B": B, "S": S, "H": H, "D": D, "bits": bits},
+            "roofline": {"bound": "hbm", "kernel": "k_kv_quant", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "avg_kernel_us": t_k * 1e6,
+                         "algorithmic_bytes_per_launch": k_bytes,
+                         "measured_peak": {"hbm_read_gbs": hbm, "frac": gbs / hbm if hbm else None}},
+            "launch": launch}
+
+
 def run_block(args, hbl, torch):
     """The seven linears of one 7B block at M = 65536 tokens: Q/K/V share one
     quantisation of their input, up/gate another; Wo and Wdown rotate their
@@ -563,6 +606,10 @@ def main():
 
     if args.workload == "msweep":
         print(json.dumps(run_msweep(args, hbl, torch)), flush=True)
+        return
+
+    if args.workload == "kvcache":
+        print(json.dumps(run_kvcache(args, hbl, torch)), flush=True)
         return
 
     c = {"tiny": workloads.tiny, "wo_7b": workloads.wo_7b, "wdown_7b": workloads.wdown_7b}[args.workload]()

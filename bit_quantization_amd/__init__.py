@@ -63,6 +63,7 @@ _SIGS = {
     "hbl_ternary_gemm_mx": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
     "hbl_forward_mx_workspace_size": ([_I64, _I64], _SZ),
     "hbl_forward_mx": ([_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
+    "hbl_kv_quant": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -314,3 +315,21 @@ def forward_mx(x: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, hadamard:
                                _ptr(out), out.stride(0), _ptr(workspace), workspace.numel(), _stream()),
            "hbl_forward_mx")
     return out
+
+
+def kv_quant(x: torch.Tensor, bits: int, keep_bos8: bool = True):
+    """Post-RoPE QKV / KV-cache quantiser on x [B][S][H][D] (contiguous).
+    Returns (codes uint8 [B][S][H][D*bits/8], scales [B][S][H], bos_codes
+    uint8 [B][H][D], bos_scales [B][H]); the BOS tensors are empty without
+    keep_bos8."""
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B][S][H][D] tensor")
+    B, S, H, D = x.shape
+    codes = torch.empty((B, S, H, D * bits // 8), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, S, H), dtype=torch.float32, device=x.device)
+    bos = torch.empty((B, H, D) if keep_bos8 else (0,), dtype=torch.uint8, device=x.device)
+    bos_s = torch.empty((B, H) if keep_bos8 else (0,), dtype=torch.float32, device=x.device)
+    _check(_lib.hbl_kv_quant(_ptr(x), _x_dtype(x), B, S, H, D, bits, int(keep_bos8), _ptr(codes), _ptr(scales),
+                             _ptr(bos) if keep_bos8 else None, _ptr(bos_s) if keep_bos8 else None, _stream()),
+           "hbl_kv_quant")
+    return codes, scales, bos, bos_s

@@ -380,6 +380,29 @@ int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx
   return HBL_OK;
 }
 
+int hbl_kv_quant(const void* x, int x_dtype, int64_t B, int64_t S, int64_t H, int64_t D, int bits, int keep_bos8,
+                 void* codes, float* scales, void* bos_codes, float* bos_scales, void* stream) {
+  g_last_error.clear();
+  if (x_dtype != HBL_DTYPE_F32 && x_dtype != HBL_DTYPE_BF16)
+    return fail(HBL_ERR_MODE, "x_dtype %d is neither HBL_DTYPE_F32 nor HBL_DTYPE_BF16", x_dtype);
+  if (bits != 3 && bits != 4 && bits != 8) return fail(HBL_ERR_MODE, "bits = %d is not 3, 4 or 8", bits);
+  if (B < 0 || S < 1 || H < 1) return fail(HBL_ERR_SHAPE, "need B >= 0, S >= 1, H >= 1");
+  if (!is_pow2(D) || D < 32 || D > 2048)
+    return fail(HBL_ERR_SHAPE, "D = %lld must be a power of two in [32, 2048]", (long long)D);
+  if (B * S * H > ((int64_t)1 << 40)) return fail(HBL_ERR_SHAPE, "B x S x H is too large");
+  if (B == 0) return HBL_OK;
+  if (!x || !codes || !scales) return fail(HBL_ERR_NULL, "x, codes and scales must be non-NULL");
+  if (keep_bos8 && (!bos_codes || !bos_scales))
+    return fail(HBL_ERR_NULL, "keep_bos8 needs bos_codes and bos_scales");
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales) || !aligned16(bos_codes) || !aligned4(bos_scales))
+    return fail(HBL_ERR_ALIGN, "x, codes and bos_codes must be 16-byte aligned, scales 4-byte aligned");
+  hipError_t e = hbl::launch_kv_quant(x, x_dtype == HBL_DTYPE_BF16, B, S, H, (int)D, bits, keep_bos8 != 0, codes,
+                                      scales, bos_codes, bos_scales, cu_count_cached(),
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv quantise launch");
+  return HBL_OK;
+}
+
 size_t hbl_ternarize_rotated_workspace_size(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0) return 0;
   return round256(sizeof(float) * (size_t)N * (size_t)K) + hbl_ternarize_workspace_size(N, K);

@@ -40,6 +40,11 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
 hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t* wq,
                               hipStream_t s);
 
+// post-RoPE QKV / KV-cache quantiser (k_kvquant.hip); D a power of two in [32, 2048]
+hipError_t launch_kv_quant(const void* x, bool x_bf16, int64_t B, int64_t S, int64_t H, int D,
+                           int bits, int keep_bos8, void* codes, float* scales, void* bos_codes,
+                           float* bos_scales, int cu_count, hipStream_t s);
+
 // Token counts up to this take the weight-streaming kernel.
 constexpr int kGemvMaxM = 128;
 

@@ -251,6 +251,33 @@ int hbl_ternarize_weights_rotated(const void* w, int w_dtype, int64_t N, int64_t
                                   uint32_t* w_packed, float* alpha, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * hbl_kv_quant -- post-RoPE QKV / KV-cache quantiser (§3.4 "QKV Attention
+ * Quantization: Post-RoPE INT4/3-bit"): every head of every token is
+ * quantised to unsigned b-bit integers with the absmax function, without
+ * calibration; the KV heads of the [BOS] token are kept at 8 bits.
+ * The pages give no formula for the unsigned mapping; this library reads it
+ * as Eq. 7's absmax quantiser at b bits shifted into [0, 2^b - 1]:
+ *   gamma = max |x| over the head's D elements, Q = 2^(b-1) - 1,
+ *   u = RoundClip(x * Q / (gamma + eps), -2^(b-1), 2^(b-1) - 1) + 2^(b-1),
+ *   scale = gamma / Q,  so that x ~ (u - 2^(b-1)) * scale.
+ * x: [B][S][H][D] contiguous (B sequences of S positions, H heads of D
+ *    elements), x_dtype F32 or BF16, 16-byte aligned.
+ * bits: 3, 4 or 8.
+ * codes: out, [B][S][H][D * bits / 8] bytes: bits 8 one byte per code;
+ *    bits 4 code 2i in the low nibble of byte i; bits 3 eight codes per
+ *    three bytes, code j of the eight at bits [3j, 3j + 3) of their 24-bit
+ *    little-endian value.  16-byte aligned.
+ * scales: out, float [B][S][H].
+ * keep_bos8: nonzero -- position 0 of every sequence (the [BOS] token) is
+ *    also written at 8 bits to bos_codes [B][H][D] bytes and bos_scales
+ *    float [B][H] (its low-bit slot in codes is written as well).
+ * Shapes: D a power of two, 32 <= D <= 2048; S, H >= 1; B == 0 is a no-op.
+ * ------------------------------------------------------------------- */
+int hbl_kv_quant(const void* x, int x_dtype, int64_t B, int64_t S, int64_t H,
+                 int64_t D, int bits, int keep_bos8, void* codes, float* scales,
+                 void* bos_codes, float* bos_scales, void* stream);
+
 /* =====================================================================
  * INT4 on the FP6 x FP4 matrix cores.
  *

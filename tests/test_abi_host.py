@@ -211,3 +211,16 @@ def test_mx_entry_point_errors(hbl):
     assert p(A, 64, 100, B, None) == hbl.ERR_SHAPE
     assert p(None, 64, 256, B, None) == hbl.ERR_NULL
     assert p(A, 64, 256, B + 4, None) == hbl.ERR_ALIGN
+
+
+def test_kv_quant_errors(hbl):
+    lib = hbl.lib()
+    q = lib.hbl_kv_quant
+    assert q(A, 1, 2, 4, 8, 128, 5, 1, B, C, D, E, None) == hbl.ERR_MODE      # bits
+    assert q(A, 3, 2, 4, 8, 128, 4, 1, B, C, D, E, None) == hbl.ERR_MODE      # dtype
+    assert q(A, 1, 2, 4, 8, 96, 4, 1, B, C, D, E, None) == hbl.ERR_SHAPE      # D not a power of two
+    assert q(A, 1, 2, 4, 8, 4096, 4, 1, B, C, D, E, None) == hbl.ERR_SHAPE    # D above 2048
+    assert q(A, 1, 2, 0, 8, 128, 4, 1, B, C, D, E, None) == hbl.ERR_SHAPE     # S
+    assert q(A, 1, 2, 4, 8, 128, 4, 1, B, C, None, E, None) == hbl.ERR_NULL   # BOS buffers needed
+    assert q(A + 8, 1, 2, 4, 8, 128, 4, 0, B, C, None, None, None) == hbl.ERR_ALIGN
+    assert q(A, 1, 0, 4, 8, 128, 4, 1, B, C, D, E, None) == hbl.OK             # B = 0
