@@ -188,7 +188,7 @@ def layer_roofline(hbl, x, packed, alpha, bits, had, M, N, K, reps):
 def layer_roofline_mx(hbl, x, wq, alpha, had, M, N, K, reps):
     """Per-kernel timing of one layer on the FP6 x FP4 path."""
     c, s = hbl.hadamard_quant_mx(x, hadamard=had)
-    out = hbl.ternary_gemm_mx(c, s, wq, alpha, K)
+    out = hbl.ternary_gemm_mx(c, s, wq, alpha, K, N=N)
     t_q = time_stream(lambda: hbl.hadamard_quant_mx(x, hadamard=had), reps)
     t_g = time_stream(lambda: hbl.ternary_gemm_mx(c, s, wq, alpha, K, out=out), reps)
     code_bytes = M * K * 3 // 4
@@ -516,7 +516,7 @@ def run_block(args, hbl, torch):
         qbuf = {}
         for inp, had, layers in groups:
             K = dict(workloads.BLOCK_7B_INPUTS)[inp]
-            shape, dt = ((M, K // 4 * 3), torch.uint8) if mx else hbl.codes_shape(M, K, bits)
+            shape, dt = (((M + 255) // 256 * 256, K // 4 * 3), torch.uint8) if mx else hbl.codes_shape(M, K, bits)
             qbuf[inp] = (torch.empty(shape, dtype=dt, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda"),
                          torch.empty(M, dtype=torch.int32, device="cuda"))
         wmx = {name: hbl.prepare_weights_mx(ws[name][0], K) for name, K, N, had in workloads.BLOCK_7B_LAYERS} if mx else {}

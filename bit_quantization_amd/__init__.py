@@ -64,6 +64,8 @@ _SIGS = {
     "hbl_forward_mx_workspace_size": ([_I64, _I64], _SZ),
     "hbl_forward_mx": ([_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
     "hbl_kv_quant": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P], _I),
+    "hbl_mx_codes_bytes": ([_I64, _I64], _SZ),
+    "hbl_mx_weights_bytes": ([_I64, _I64], _SZ),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -267,18 +269,20 @@ def norm_forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bit
 # INT4 on the FP6 x FP4 matrix cores (MX6 codes, MX4 weights; include/hbl.h)
 
 def prepare_weights_mx(packed: torch.Tensor, K: int) -> torch.Tensor:
-    """Ternary layout -> MX4 layout (int32 [N][K/16] holding the words)."""
+    """Ternary layout -> MX4 layout: int32 [ceil(N/128)*128][K/16] holding the
+    words in the tiled order of include/hbl.h (rows past N zero)."""
     N = packed.shape[0]
-    wq = torch.empty((N, K // 16), dtype=torch.int32, device=packed.device)
+    wq = torch.empty(((N + 127) // 128 * 128, K // 16), dtype=torch.int32, device=packed.device)
     _check(_lib.hbl_prepare_weights_mx(_ptr(packed), N, K, _ptr(wq), _stream()), "hbl_prepare_weights_mx")
     return wq
 
 
 def hadamard_quant_mx(x: torch.Tensor, hadamard: bool = True):
-    """INT4 quantisation (Eq. 8) with MX6 codes: (codes uint8 [M][3K/4],
-    scales float32 [M])."""
+    """INT4 quantisation (Eq. 8) with MX6 codes: (codes uint8
+    [ceil(M/256)*256][3K/4] in the tiled order of include/hbl.h, scales
+    float32 [M])."""
     M, K, ldx = _rows(x)
-    codes = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device)
+    codes = torch.empty(((M + 255) // 256 * 256, K // 4 * 3), dtype=torch.uint8, device=x.device)
     scales = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(_lib.hbl_hadamard_quant_mx(_ptr(x), _x_dtype(x), M, K, ldx, HADAMARD if hadamard else 0, _ptr(codes),
                                       _ptr(scales), _stream()), "hbl_hadamard_quant_mx")
@@ -286,10 +290,12 @@ def hadamard_quant_mx(x: torch.Tensor, hadamard: bool = True):
 
 
 def ternary_gemm_mx(codes: torch.Tensor, scales: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, K: int,
-                    out_dtype: int = OUT_BF16, out: torch.Tensor | None = None) -> torch.Tensor:
-    """The FP6 x FP4 matmul with the rescale of Eq. 9."""
-    M = codes.shape[0]
-    N = wq.shape[0]
+                    out_dtype: int = OUT_BF16, out: torch.Tensor | None = None, N: int | None = None) -> torch.Tensor:
+    """The FP6 x FP4 matmul with the rescale of Eq. 9 (M = len(scales); N
+    defaults to the rows of the prepared weights, which are padded to 128:
+    pass the matrix's N, or an ``out`` of that width)."""
+    M = scales.shape[0]
+    N = out.shape[1] if out is not None else (N if N is not None else wq.shape[0])
     if out is None:
         out = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=codes.device)
     _check(_lib.hbl_ternary_gemm_mx(_ptr(codes), _ptr(scales), _ptr(wq), _ptr(alpha), M, N, K, out_dtype, _ptr(out),
@@ -302,11 +308,14 @@ def forward_mx_workspace(M: int, K: int, device) -> torch.Tensor:
 
 
 def forward_mx(x: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, hadamard: bool = True,
-               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               N: int | None = None) -> torch.Tensor:
     """The INT4 layer of Eq. 9 on the FP6 x FP4 matrix cores: bf16 [M][N],
-    the same values as forward(x, packed, alpha, 4, hadamard)."""
+    the same values as forward(x, packed, alpha, 4, hadamard).  N defaults to
+    the prepared weights' (128-padded) rows: pass the matrix's N, or an
+    ``out`` of that width."""
     M, K, ldx = _rows(x)
-    N = wq.shape[0]
+    N = out.shape[1] if out is not None else (N if N is not None else wq.shape[0])
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:

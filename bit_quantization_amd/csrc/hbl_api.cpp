@@ -297,10 +297,20 @@ int hbl_norm_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t l
                       stream);
 }
 
+size_t hbl_mx_codes_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0) return 0;
+  return (size_t)((M + 255) / 256 * 256) * (size_t)(K / 4 * 3);
+}
+
+size_t hbl_mx_weights_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)((N + 127) / 128 * 128) * (size_t)(K / 4);
+}
+
 int hbl_prepare_weights_mx(const uint32_t* w_packed, int64_t N, int64_t K, uint32_t* w_mx, void* stream) {
   g_last_error.clear();
-  if (N < 1 || K < 16 || K % 16 != 0)
-    return fail(HBL_ERR_SHAPE, "need N >= 1 and K a positive multiple of 16 (N = %lld, K = %lld)", (long long)N,
+  if (N < 1 || K < 128 || K % 128 != 0)
+    return fail(HBL_ERR_SHAPE, "need N >= 1 and K a positive multiple of 128 (N = %lld, K = %lld)", (long long)N,
                 (long long)K);
   if (!w_packed || !w_mx) return fail(HBL_ERR_NULL, "w_packed and w_mx must be non-NULL");
   if (!aligned16(w_packed) || !aligned16(w_mx)) return fail(HBL_ERR_ALIGN, "w_packed and w_mx must be 16-byte aligned");
@@ -349,7 +359,7 @@ int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales, const uint32_
 
 size_t hbl_forward_mx_workspace_size(int64_t M, int64_t K) {
   if (M < 0 || K <= 0) return 0;
-  return round256((size_t)M * (size_t)(K / 4 * 3)) + round256(sizeof(float) * (size_t)M);
+  return round256(hbl_mx_codes_bytes(M, K)) + round256(sizeof(float) * (size_t)M);
 }
 
 int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
@@ -370,7 +380,7 @@ int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx
     return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
   if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
   void* codes = ws;
-  float* scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)M * (size_t)(K / 4 * 3)));
+  float* scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(hbl_mx_codes_bytes(M, K)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, (flags & HBL_HADAMARD) != 0,
                                             6, codes, scales, nullptr, false, nullptr, cu_count_cached(), s);

@@ -11,18 +11,26 @@
 // K <= 2^21).  So v_mfma_f32_32x32x64_f8f6f4 computes the integer matmul
 // exactly, at twice the rate per clock of the int8 matrix cores.
 //
-// Operand layouts (both produced by this library; see include/hbl.h):
-//   codes, "MX6": per token row K * 3/4 bytes, in blocks of 128 codes
-//     (96 bytes).  Group g = 0..3 of a block holds codes 32 g .. 32 g + 31 as
-//     a 192-bit field, code e at bits 6 e .. 6 e + 5 (little endian); its
-//     first 16 bytes sit at byte 16 g of the block, its last 8 bytes at
-//     byte 64 + 8 g.  The split keeps every LDS read 16-byte aligned.
-//   weights, "MX4": uint32 [N][K/16], word w holds k = 16 w .. 16 w + 15
-//     with two bits per weight: for n = 0..7, bit 4n+1 = (q_{16w+n} != 0),
+// Operand layouts (both produced by this library; see include/hbl.h): each
+// stage of the matmul (256 token rows or 128 feature rows x 128 k) is stored
+// as the LDS image the kernel needs, so that its stage loads are contiguous
+// 1 KB copies.
+//   codes, "MX6": groups of 32 codes as 192-bit fields (code e at bits 6 e,
+//     little endian) in 24 KB tiles of 256 rows x 128 codes: a 16 KB main
+//     area (the first 16 bytes of each group; row r, group gi at unit
+//     4 r + (gi ^ ((r >> 2) & 3))) and an 8 KB tail area (the last 8 bytes;
+//     row r, groups 2 u and 2 u + 1 in the halves of unit
+//     2 r + (u ^ ((r >> 3) & 1))).  Tiles run over the stages of a 256-row
+//     block, then the blocks; the buffer holds whole blocks.
+//   weights, "MX4": uint32 words, two bits per weight: for a word holding
+//     k = 16 w .. 16 w + 15 and n = 0..7, bit 4n+1 = (q_{16w+n} != 0),
 //     bit 4n+3 = (q_{16w+n} < 0), bit 4n = (q_{16w+8+n} != 0),
-//     bit 4n+2 = (q_{16w+8+n} < 0).  Then word & 0xAAAAAAAA holds the E2M1
+//     bit 4n+2 = (q_{16w+8+n} < 0); word & 0xAAAAAAAA then holds the E2M1
 //     codes of k = 16w .. 16w+7 (nibble n, sign at bit 3, exponent bit at
 //     bit 1) and (word << 1) & 0xAAAAAAAA those of k = 16w+8 .. 16w+15.
+//     4 KB tiles of 128 rows x 128 k: row r's units (64 k each) at
+//     2 r + (u ^ ((r >> 3) & 1)); tiles over the stages of a block, then the
+//     blocks; rows past N are zero.
 //
 // Kernel structure (k_gemm_mx): persistent, one block of 4 waves (2 x 2) per
 // CU, one wave per SIMD, block tile 256 tokens x BN features (BN = 256 when
@@ -103,6 +111,8 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
                 "staging must divide evenly");
   constexpr int DPS = MDMA + TDMA + BDMA;  // loads per wave per stage
   constexpr int MSZ = BM * MROW, TSZ = BM * TROW, BSZ = BN * BROW;
+  static_assert(BM == 256 && MSZ == 16384 && TSZ == 8192 && BN % 128 == 0,
+                "the MX6 tile is 256 rows x 128 codes, the MX4 tile 128 rows x 128 weights");
   __shared__ __attribute__((aligned(1024))) uint8_t Am0[MSZ], Am1[MSZ], Am2[MSZ], Am3[MSZ];
   __shared__ __attribute__((aligned(1024))) uint8_t At0[TSZ], At1[TSZ], At2[TSZ], At3[TSZ];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
@@ -145,17 +155,14 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   auto mswz = [](int r, int u) { return u ^ ((r >> MSH) & (MU - 1)); };
   auto tswz = [](int r, int u) { return u ^ ((r >> TSH) & (TU - 1)); };
   auto bswz = [](int r, int u) { return u ^ ((r >> BSH) & (BU - 1)); };
-  // Lane l of load j of wave w fills physical unit 64 (w + NW j) + l of a
-  // stage array: row p / U, physical unit l % U, holding logical unit
-  // (l % U) ^ swizzle(row).  Rows past the end lie beyond the buffer's
-  // range and read as zero (a zero code).
-  constexpr int MJR = 64 * NW / MU, TJR = 64 * NW / TU, BJR = 64 * NW / BU;  // rows between loads j, j + 1
-  const int mr0 = (64 * wave + lane) / MU, tr0 = (64 * wave + lane) / TU, br0 = (64 * wave + lane) / BU;
-  const uint32_t moff0 = (uint32_t)mr0 * (uint32_t)arow_bytes + 16u * (uint32_t)mswz(mr0, lane % MU);
-  const uint32_t toff0 = (uint32_t)tr0 * (uint32_t)arow_bytes + 64u + 16u * (uint32_t)tswz(tr0, lane % TU);
-  const uint32_t boff0 = (uint32_t)br0 * (uint32_t)brow_bytes + 16u * (uint32_t)bswz(br0, lane % BU);
-  const uint32_t mstep = (uint32_t)MJR * (uint32_t)arow_bytes, tstep = (uint32_t)TJR * (uint32_t)arow_bytes;
-  const uint32_t bstep = (uint32_t)BJR * (uint32_t)brow_bytes;
+  // The MX6 and MX4 layouts store each stage as the LDS image (rows in
+  // 16-byte units, XOR-swizzled by row), so lane l of load j of wave w copies
+  // the 16 contiguous bytes of physical unit 64 (w + NW j) + l: every load
+  // instruction moves 1 KB of consecutive addresses.  Codes: 24 KB per
+  // 256-row block and stage (16 KB main area, then 8 KB tail area); weights:
+  // 4 KB per 128-row block and stage.
+  const uint32_t cl0 = 16u * (uint32_t)(64 * wave + lane);
+  const uint32_t wblk = (uint32_t)(K / BK) * 4096u;  // bytes of one 128-row weight block
   constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
 
   int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
@@ -163,10 +170,12 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   auto set_tile = [&](int r) {
     int64_t m0 = 0, n0 = 0;
     if (r < ntiles) tile_of(r, m0, n0);
-    const int arows = r < ntiles ? (int)min<int64_t>(BM, M - m0) : 0;
-    const int brows = r < ntiles ? (int)min<int64_t>(BN, N - n0) : 0;
+    // the code buffer holds whole 256-row blocks (rows past M are padding,
+    // their outputs are not stored); the weight buffer whole 128-row blocks
+    const int64_t wrows = (N + 127) / 128 * 128;
+    const int brows = r < ntiles ? (int)min<int64_t>(BN, wrows - n0) : 0;
     rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + m0 * arow_bytes), (short)0,
-                                           (int)(arows * arow_bytes), 0x00020000);
+                                           r < ntiles ? (int)(BM * arow_bytes) : 0, 0x00020000);
     rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes),
                                            (short)0, (int)(brows * brow_bytes), 0x00020000);
   };
@@ -175,18 +184,17 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     uint8_t* const Td = tbuf(bi);
     uint8_t* const Bd = bbuf(bi);
     const bool live = dr < ntiles;
-    const uint32_t vm = live ? moff0 + (uint32_t)dk * 96u : kOut;
-    const uint32_t vt = live ? toff0 + (uint32_t)dk * 96u : kOut;
-    const uint32_t vb = live ? boff0 + (uint32_t)dk * BROW : kOut;
+    const uint32_t vm = live ? (uint32_t)dk * 24576u + cl0 : kOut;
+    const uint32_t vb = live ? (uint32_t)dk * 4096u + cl0 : kOut;
 #pragma unroll
     for (int j = 0; j < MDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * mstep, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * 4096u, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < TDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vt + j * tstep, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vm + 16384u + j * 4096u, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < BDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * wblk, 0, 0, 0);
     if (++dk == nk) {
       dk = 0;
       set_tile(++dr);
@@ -367,28 +375,41 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
 }
 
 // Ternary layout of the library (c = q + 1 at bits 8b + 2s of each word,
-// weight 4s + b) -> MX4 layout; one thread per word.
-__global__ void k_prepare_mx4(const uint32_t* __restrict__ wp, int64_t n_words, uint32_t* __restrict__ wq) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_words) return;
-  const uint32_t w = wp[i];
-  uint32_t o = 0;
+// weight 4s + b) -> MX4 words in the tiled stage images; one thread per
+// output word.  Output word w4 of tile (block nb of 128 rows, stage s of 128
+// k) at physical unit p = w4 / 4: row r = p / 2 of the block, logical unit
+// u = (p % 2) ^ ((r >> 3) & 1), i.e. k = 128 s + 64 u + 16 (w4 % 4) ..+ 15.
+// Rows past N are zero.
+__global__ void k_prepare_mx4(const uint32_t* __restrict__ wp, int64_t N, int64_t K, int64_t n_out,
+                              uint32_t* __restrict__ wq) {
+  const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n_out) return;
+  const int64_t stages = K / 128;
+  const int64_t tile = o >> 10, within = o & 1023;
+  const int64_t nb = tile / stages, st = tile % stages;
+  const int p = (int)(within >> 2), wi = (int)(within & 3);
+  const int r = p >> 1, u = (p & 1) ^ ((r >> 3) & 1);
+  const int64_t n = nb * 128 + r;
+  uint32_t res = 0;
+  if (n < N) {
+    const uint32_t w = wp[n * (K / 16) + st * 8 + u * 4 + wi];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t c = (w >> (8 * (j & 3) + 2 * (j >> 2))) & 3u;  // weight j: s = j / 4, b = j % 4
-    const uint32_t nz = c != 1u, neg = c == 0u;
-    const int n = j & 7, hi = j >> 3;  // k < 8: bits 4n+1, 4n+3; else 4n, 4n+2
-    o |= (nz << (4 * n + 1 - hi)) | (neg << (4 * n + 3 - hi));
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t c = (w >> (8 * (j & 3) + 2 * (j >> 2))) & 3u;  // weight j: s = j / 4, b = j % 4
+      const uint32_t nz = c != 1u, neg = c == 0u;
+      const int nn = j & 7, hi = j >> 3;  // k < 8: bits 4n+1, 4n+3; else 4n, 4n+2
+      res |= (nz << (4 * nn + 1 - hi)) | (neg << (4 * nn + 3 - hi));
+    }
   }
-  wq[i] = o;
+  wq[o] = res;
 }
 
 }  // namespace
 
 hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t* wq, hipStream_t s) {
-  const int64_t n_words = N * (K / 16);
-  if (n_words == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prepare_mx4, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, s, wp, n_words, wq);
+  const int64_t n_out = (N + 127) / 128 * 128 * (K / 16);
+  if (n_out == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prepare_mx4, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, wp, N, K, n_out, wq);
   return hipGetLastError();
 }
 

@@ -62,6 +62,25 @@ __device__ __forceinline__ uint32_t mx6_chunk(uint32_t w) {
   return (b & 0x3fu) | ((b >> 2) & (0x3fu << 6)) | ((b >> 4) & (0x3fu << 12)) | ((b >> 6) & (0x3fu << 18));
 }
 
+// Byte offsets of group g (32 codes) of token row m in the MX6 layout: the
+// codes of 256-row block B = m / 256 and stage s = g / 4 (128 codes) form one
+// 24 KB tile, a 16 KB main area (the first 16 bytes of each group: row r =
+// m % 256 at units 4 r .. 4 r + 3, group gi = g % 4 at unit
+// 4 r + (gi ^ ((r >> 2) & 3))) and an 8 KB tail area (the last 8 bytes: row r
+// at units 2 r, 2 r + 1, groups 2 u, 2 u + 1 in the two halves of unit
+// 2 r + (u ^ ((r >> 3) & 1))).  That is the matmul's LDS stage image, so its
+// stage loads are plain contiguous copies.
+__device__ __forceinline__ int64_t mx6_main_off(int64_t m, int g, int K) {
+  const int64_t tile = (m >> 8) * (K / 128) + (g >> 2);
+  const int r = (int)(m & 255), gi = g & 3;
+  return tile * 24576 + 16 * (4 * r + (gi ^ ((r >> 2) & 3)));
+}
+__device__ __forceinline__ int64_t mx6_tail_off(int64_t m, int g, int K) {
+  const int64_t tile = (m >> 8) * (K / 128) + (g >> 2);
+  const int r = (int)(m & 255), gi = g & 3;
+  return tile * 24576 + 16384 + 16 * (2 * r + ((gi >> 1) ^ ((r >> 3) & 1))) + 8 * (gi & 1);
+}
+
 // The 192-bit field of 32 codes from its eight 24-bit chunks (chunk i at
 // bit 24 i), stored MX6-style: the first 16 bytes at main, the last 8 at
 // tail.
@@ -445,9 +464,9 @@ __device__ __forceinline__ int swz16(int e) {  // float index -> swizzled float 
 // group), and the result is written to LDS as groups of 4 consecutive
 // elements, in the same swizzled layout as the register path.
 // OUT: 0 = codes (BITS 8 or 4), 1 = fp32 rotated values, 2 = INT4 codes as
-// MX6 operands of the FP6 x FP4 matmul (BITS 4): per row, blocks of 128
-// codes in 96 bytes, group g of 32 codes as a 192-bit field (code e at bit
-// 6 e) whose first 16 bytes sit at byte 16 g, its last 8 at byte 64 + 8 g.
+// MX6 operands of the FP6 x FP4 matmul (BITS 4): groups of 32 codes as
+// 192-bit fields (code e at bit 6 e), placed in 24 KB tiles of 256 rows x 128
+// codes (mx6_main_off, mx6_tail_off).
 template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 __global__ void __launch_bounds__(256, 2)
 k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
@@ -699,11 +718,11 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           ch[gi / 8][gi % 8] = mx6_chunk(w);
         }
         if (live) {
-          uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + m * (int64_t)(K / 4 * 3);
+          uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int g = 2 * t + q;
-            mx6_store(ch[q], dst + 96 * (g >> 2) + 16 * (g & 3), dst + 96 * (g >> 2) + 64 + 8 * (g & 3));
+            mx6_store(ch[q], dst + mx6_main_off(m, g, K), dst + mx6_tail_off(m, g, K));
           }
         }
       } else if constexpr (!HAD) {
@@ -745,14 +764,14 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         __syncthreads();
         if (live) {
           if constexpr (OUT == 2) {
-            uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + m * (int64_t)(K / 4 * 3);
+            uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
               const int g = t + T * qq;  // group of 32 codes: 8 chunk words
               const uint4 a = *reinterpret_cast<const uint4*>(C8 + 32 * g);
               const uint4 b = *reinterpret_cast<const uint4*>(C8 + 32 * g + 16);
               const uint32_t ch[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-              mx6_store(ch, dst + 96 * (g >> 2) + 16 * (g & 3), dst + 96 * (g >> 2) + 64 + 8 * (g & 3));
+              mx6_store(ch, dst + mx6_main_off(m, g, K), dst + mx6_tail_off(m, g, K));
             }
           } else if constexpr (BITS == 8) {
             int8_t* dst = reinterpret_cast<int8_t*>(codes) + m * (int64_t)K;

@@ -291,30 +291,46 @@ int hbl_kv_quant(const void* x, int x_dtype, int64_t B, int64_t S, int64_t H,
  * outputs), at twice the per-clock rate of the int8 matrix cores.  It is
  * the INT4 path of Eq. 8-9 (§3.4) on gfx950's low-precision matrix cores.
  *
- * Operand layouts (bit-exact contract):
- *   MX6 codes: per token row K * 3 / 4 bytes, in blocks of 128 codes (96
- *       bytes).  Group g = 0..3 of a block holds codes 32 g .. 32 g + 31 as
- *       a 192-bit little-endian field, code e at bits [6 e, 6 e + 6) as an
+ * Operand layouts (bit-exact contract).  Each is stored as the matmul's
+ * LDS stage images, so that its stage loads are contiguous copies.
+ *   MX6 codes: groups of 32 codes (k = 32 g .. 32 g + 31 of a token row) as
+ *       192-bit little-endian fields, code e at bits [6 e, 6 e + 6) as an
  *       E3M2 float (0 = 0b000000, 1 = 0b001100, 2 = 0b010000,
  *       3 = 0b010010, 4 = 0b010100, 5 = 0b010101, 6 = 0b010110,
- *       7 = 0b010111, 8 = 0b011000, bit 5 the sign); the field's first 16
- *       bytes sit at byte 16 g of the block, its last 8 at byte 64 + 8 g.
- *   MX4 weights: uint32 [N][K/16]; word w holds k = 16 w .. 16 w + 15: for
- *       n = 0..7, bit 4n+1 = (q[16w+n] != 0), bit 4n+3 = (q[16w+n] < 0),
+ *       7 = 0b010111, 8 = 0b011000, bit 5 the sign).  Tile (B, s) of 24576
+ *       bytes holds token rows 256 B .. 256 B + 255 and codes
+ *       128 s .. 128 s + 127 at byte offset (B * (K / 128) + s) * 24576: for
+ *       row r = m % 256 and group gi = g % 4 of the tile, the field's first
+ *       16 bytes at 16 * (4 r + (gi ^ ((r >> 2) & 3))), its last 8 bytes at
+ *       16384 + 16 * (2 r + ((gi >> 1) ^ ((r >> 3) & 1))) + 8 * (gi & 1).
+ *       The buffer holds whole 256-row blocks: hbl_mx_codes_bytes(M, K)
+ *       bytes (rows past M are padding, never read into an output).
+ *   MX4 weights: uint32 words, two bits per weight: for the word of
+ *       k = 16 w .. 16 w + 15 of a feature row and n = 0..7,
+ *       bit 4n+1 = (q[16w+n] != 0), bit 4n+3 = (q[16w+n] < 0),
  *       bit 4n = (q[16w+8+n] != 0), bit 4n+2 = (q[16w+8+n] < 0), so that
- *       word & 0xAAAAAAAA and (word << 1) & 0xAAAAAAAA are the E2M1 codes of
- *       the two halves.  Same size as the ternary layout.
+ *       word & 0xAAAAAAAA and (word << 1) & 0xAAAAAAAA are the E2M1 codes
+ *       of the two halves.  Tile (b, s) of 4096 bytes holds feature rows
+ *       128 b .. 128 b + 127 and k = 128 s .. 128 s + 127 at byte offset
+ *       (b * (K / 128) + s) * 4096: row r's k = 128 s + 64 u .. + 63 (four
+ *       words) at 16 * (2 r + (u ^ ((r >> 3) & 1))).  Rows past N are
+ *       zero; the buffer holds hbl_mx_weights_bytes(N, K) bytes.
  * ===================================================================== */
 
+/* Buffer sizes of the two layouts. */
+size_t hbl_mx_codes_bytes(int64_t M, int64_t K);
+size_t hbl_mx_weights_bytes(int64_t N, int64_t K);
+
 /* hbl_prepare_weights_mx -- ternary layout (hbl_ternarize_weights) to the
- * MX4 layout.  Offline, once per matrix.  Shapes: N >= 1, K % 16 == 0. */
+ * MX4 layout (w_mx: hbl_mx_weights_bytes(N, K) bytes).  Offline, once per
+ * matrix.  Shapes: N >= 1, K % 128 == 0. */
 int hbl_prepare_weights_mx(const uint32_t* w_packed, int64_t N, int64_t K,
                            uint32_t* w_mx, void* stream);
 
 /* hbl_hadamard_quant_mx -- hbl_hadamard_quant with bits = 4 (Eq. 8, after
  * the rotation with HBL_HADAMARD), codes written in the MX6 layout:
- * codes_mx [M][K * 3 / 4] bytes, scales [M] (beta / sqrt(7)).  The same
- * codes and scales as hbl_hadamard_quant(..., bits = 4).
+ * codes_mx hbl_mx_codes_bytes(M, K) bytes, scales [M] (beta / sqrt(7)).  The
+ * same codes and scales as hbl_hadamard_quant(..., bits = 4).
  * Shapes: K a power of two, 1024 <= K <= HBL_MAX_K; ldx as there. */
 int hbl_hadamard_quant_mx(const void* x, int x_dtype, int64_t M, int64_t K,
                           int64_t ldx, int flags, void* codes_mx, float* scales,

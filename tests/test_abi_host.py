@@ -201,14 +201,18 @@ def test_mx_entry_point_errors(hbl):
     assert g(A, B, None, D, 4, 64, 1024, 0, F, 64, None) == hbl.ERR_NULL
     assert g(A + 8, B, C, D, 4, 64, 1024, 0, F, 64, None) == hbl.ERR_ALIGN
     assert g(A, B, C, D, 0, 64, 1024, 0, F, 64, None) == hbl.OK
+    # whole 256-row code blocks and 128-row weight blocks
+    assert lib.hbl_mx_codes_bytes(10, 1024) == 256 * 768 and lib.hbl_mx_codes_bytes(257, 1024) == 512 * 768
+    assert lib.hbl_mx_weights_bytes(130, 1024) == 256 * 256 and lib.hbl_mx_weights_bytes(128, 1024) == 128 * 256
     need = lib.hbl_forward_mx_workspace_size(10, 1024)
-    assert need >= 10 * 768 + 40 and need % 256 == 0
+    assert need >= 256 * 768 + 40 and need % 256 == 0
     f = lib.hbl_forward_mx
     assert f(A, 1, 10, 1024, 1024, 64, 1, B, C, D, 64, E, need - 1, None) == hbl.ERR_WORKSPACE
     assert f(A, 1, 10, 2048, 2048, 64, 1, B, C, D, 64, E, need, None) == hbl.ERR_WORKSPACE
     assert f(A, 1, 10, 1024, 1024, 64, 1, None, C, D, 64, E, need, None) == hbl.ERR_NULL
     p = lib.hbl_prepare_weights_mx
     assert p(A, 64, 100, B, None) == hbl.ERR_SHAPE
+    assert p(A, 64, 64, B, None) == hbl.ERR_SHAPE      # K % 128
     assert p(None, 64, 256, B, None) == hbl.ERR_NULL
     assert p(A, 64, 256, B + 4, None) == hbl.ERR_ALIGN
 

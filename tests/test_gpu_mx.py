@@ -40,7 +40,7 @@ def test_quant_mx_codes(hbl, log2k, had, dtype):
     cm, sm = hbl.hadamard_quant_mx(xd, hadamard=had)
     q4, s4, _ = hbl.hadamard_quant(xd, 4, hadamard=had)
     torch.cuda.synchronize()
-    got = mx_util.decode_mx6(cm.cpu().numpy(), K)
+    got = mx_util.decode_mx6(cm.cpu().numpy(), K, 37)
     # the same codes and scales as the INT4 layout, bit for bit
     assert np.array_equal(got, oracle.unpack_int4(q4.cpu().numpy().view(np.uint32), K).astype(np.float64))
     assert np.array_equal(sm.cpu().numpy(), s4.cpu().numpy())
@@ -58,7 +58,7 @@ def test_gemm_mx_exact_on_oracle_codes(hbl, M, N, K):
     q8 = oracle.unpack_int4(oq, K)
     w, packed, alpha, wq = _weights(hbl, N, K, 2)
     codes = torch.from_numpy(mx_util.encode_mx6(q8)).cuda()
-    acc = hbl.ternary_gemm_mx(codes, torch.from_numpy(os_).cuda(), wq, alpha, K, out_dtype=hbl.OUT_I32)
+    acc = hbl.ternary_gemm_mx(codes, torch.from_numpy(os_).cuda(), wq, alpha, K, out_dtype=hbl.OUT_I32, N=N)
     o_packed, _, _ = oracle.ternarize(w)
     assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(oq, 4, o_packed, K))
 
@@ -71,7 +71,7 @@ def test_gemm_mx_equals_int8_path(hbl, out_dtype):
     od = hbl.OUT_BF16 if out_dtype == "bf16" else hbl.OUT_F32
     cm, sm = hbl.hadamard_quant_mx(x)
     q4, s4, r4 = hbl.hadamard_quant(x, 4)
-    a = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=od)
+    a = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=od, N=N)
     b = hbl.ternary_gemm(q4, 4, s4, r4, packed, alpha, K, out_dtype=od)
     assert torch.equal(a.view(torch.int16) if od == hbl.OUT_BF16 else a.view(torch.int32),
                        b.view(torch.int16) if od == hbl.OUT_BF16 else b.view(torch.int32))
@@ -84,7 +84,7 @@ def test_gemm_mx_strided_output(hbl):
     cm, sm = hbl.hadamard_quant_mx(x)
     big = torch.full((M, N + pad), 7, dtype=torch.bfloat16, device="cuda")
     hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out=big[:, :N])
-    ref = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K)
+    ref = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, N=N)
     assert torch.equal(big[:, :N].contiguous().view(torch.int16), ref.view(torch.int16))
     assert torch.all(big[:, N:] == 7)
 
@@ -93,7 +93,7 @@ def test_forward_mx_small(hbl):
     M, N, K = 70, 128, 1024
     x_np = workloads.random_rows(45, M, K, "t3")
     w, packed, alpha, wq = _weights(hbl, N, K, 5)
-    y = hbl.forward_mx(to_device(x_np), wq, alpha)
+    y = hbl.forward_mx(to_device(x_np), wq, alpha, N=N)
     y_int = hbl.forward(to_device(x_np), packed, alpha, 4)
     assert torch.equal(y.view(torch.int16), y_int.view(torch.int16))
     o_packed, o_alpha, _ = oracle.ternarize(w)
@@ -103,7 +103,7 @@ def test_forward_mx_small(hbl):
 def test_forward_mx_zero_tokens(hbl):
     _, packed, alpha, wq = _weights(hbl, 32, 1024, 6)
     x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
-    assert hbl.forward_mx(x, wq, alpha).shape == (0, 32)
+    assert hbl.forward_mx(x, wq, alpha, N=32).shape == (0, 32)
 
 
 @pytest.mark.parametrize("name", ["wo_7b", "wdown_7b"])
@@ -130,10 +130,10 @@ def test_gemm_mx_full_tile_grid_exact(hbl):
     x_np = workloads.random_rows(47, M, K, "t3")
     w, packed, alpha, wq = _weights(hbl, N, K, 7)
     cm, sm = hbl.hadamard_quant_mx(to_device(x_np))
-    acc = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=hbl.OUT_I32)
+    acc = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out_dtype=hbl.OUT_I32, N=N)
     rows = np.array([0, 1, 255, 256, 2047, 4095])
     oq, _, _ = oracle.quantize(np.ascontiguousarray(x_np[rows]), 4, hadamard=True)
-    gq = mx_util.decode_mx6(cm.cpu().numpy()[rows], K).astype(np.int8)
+    gq = mx_util.decode_mx6(cm.cpu().numpy(), K, rows).astype(np.int8)
     o_packed, _, _ = oracle.ternarize(w)
     # on the GPU's own codes (identical to the oracle's up to ties)
     assert np.array_equal(acc.cpu().numpy()[rows], oracle.gemm_i32(oracle.pack_int4(gq), 4, o_packed, K))

@@ -512,16 +512,35 @@ def test_e3m2_and_e2m1_tables():
 def test_mx_layout_round_trips():
     import mx_util
     rng = np.random.default_rng(17)
-    q = rng.integers(-8, 8, (5, 512)).astype(np.int8)
+    q = rng.integers(-8, 8, (261, 512)).astype(np.int8)
     b = mx_util.encode_mx6(q)
-    assert b.shape == (5, 384)
-    assert np.array_equal(mx_util.decode_mx6(b, 512), q.astype(np.float64))
-    # code e of group 1 of block 0 sits at bits 6 e of the field whose first
-    # 16 bytes start at byte 16 and whose last 8 start at byte 72
-    field = int.from_bytes(bytes(b[0, 16:32]) + bytes(b[0, 72:80]), "little")
-    assert all((field >> (6 * e)) & 63 == mx_util.E3M2_OF[int(q[0, 32 + e])] for e in range(32))
-    t = rng.integers(-1, 2, (7, 64)).astype(np.int8)
-    assert np.array_equal(mx_util.decode_mx4(mx_util.encode_mx4(t), 64), t.astype(np.float64))
+    assert b.shape == (512, 384)  # two 256-row blocks
+    assert np.array_equal(mx_util.decode_mx6(b, 512, 261), q.astype(np.float64))
+    assert not b.reshape(-1)[mx_util._mx6_offsets(512, 512)[0][261:]].any()  # padding rows
+    # row 5, group 1 of the first 128-code stage: r = 5, gi = 1; its first 16
+    # bytes at 16 (4 r + (gi ^ (r >> 2 & 3))) = 16 * 20, its last 8 at
+    # 16384 + 16 (2 r + (0 ^ (r >> 3 & 1))) + 8 = 16384 + 168
+    flat = b.reshape(-1)
+    field = int.from_bytes(bytes(flat[320:336]) + bytes(flat[16552:16560]), "little")
+    assert all((field >> (6 * e)) & 63 == mx_util.E3M2_OF[int(q[5, 32 + e])] for e in range(32))
+    # row 300 (second block, r = 44), group 5 (second stage, gi = 1): tile
+    # 1 * 4 + 1 = 5; r >> 2 & 3 = 3 -> slot 4 r + 2; r >> 3 & 1 = 1 -> tail slot 2 r + 1
+    q300 = rng.integers(-8, 8, (301, 512)).astype(np.int8)
+    b300 = mx_util.encode_mx6(q300).reshape(-1)
+    field = int.from_bytes(bytes(b300[5 * 24576 + 16 * 178:5 * 24576 + 16 * 178 + 16])
+                           + bytes(b300[5 * 24576 + 16384 + 16 * 89 + 8:5 * 24576 + 16384 + 16 * 89 + 16]), "little")
+    assert all((field >> (6 * e)) & 63 == mx_util.E3M2_OF[int(q300[300, 160 + e])] for e in range(32))
+    # MX4: round trip with padding, and one word placed by hand: row 9
+    # (r >> 3 & 1 = 1), k = 64 .. 79 (stage 0, half u = 1 -> slot 2 r + 0,
+    # word 0) -> word 4 * 18
+    t = rng.integers(-1, 2, (130, 256)).astype(np.int8)
+    w = mx_util.encode_mx4(t)
+    assert w.shape == (256, 16)
+    assert np.array_equal(mx_util.decode_mx4(w, 256, 130), t.astype(np.float64))
+    word = int(w.reshape(-1)[72])
+    for n in range(8):
+        for v, bit in ((int(t[9, 64 + n]), 4 * n + 1), (int(t[9, 72 + n]), 4 * n)):
+            assert (word >> bit) & 1 == (v != 0) and (word >> (bit + 2)) & 1 == (v < 0)
 
 
 # ------------------------------------------- QKV / KV-cache quantiser (f4)
