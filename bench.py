@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--bits", type=int, default=0, help="block_7b: 8 or 4 (0: both); kvcache: 3 or 4 (0: 4)")
     ap.add_argument("--path", default="auto", choices=["auto", "int8", "mx"],
                     help="INT4 layers: int8 matrix cores, or FP6 x FP4 (mx); auto takes mx where it applies "
-                         "(INT4, K a power of two >= 1024, M > 128; smaller M stream the weights)")
+                         "(INT4, K a power of two >= 1024, M K >= 2^19; smaller M K stream the weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
@@ -200,7 +200,10 @@ def use_mx(args, bits, M, K):
     if args.path == "int8" or bits != 4:
         return False
     ok = K >= 1024 and (K & (K - 1)) == 0 and K % 512 == 0
-    return ok and (args.path == "mx" or M > 128)
+    # the FP6 x FP4 layer (K split over the partial sums below 256 tiles)
+    # beats weight streaming from M K >= 2^19 (M >= 128 at K = 4096, M >= 32
+    # at K = 16384)
+    return ok and (args.path == "mx" or M * K >= 1 << 19)
 
 
 def time_passes(args, torch, layer):
@@ -232,7 +235,7 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
     packed, alpha = hbl.ternarize_weights(torch.from_numpy(w_np).cuda())
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     mx = use_mx(args, bits, M, K)
-    ws = hbl.forward_workspace(M, K, bits, "cuda")
+    ws = hbl.forward_workspace(M, N, K, bits, "cuda")
 
     def layer_int8():
         hbl.forward(x, packed, alpha, bits, hadamard=had, out=out, workspace=ws)
@@ -240,7 +243,7 @@ def run_layer(args, hbl, torch, x_np, w_np, bits, had, label):
     # A step is one whole-layer pass (both kernels) of the product path.
     if mx:
         wq = hbl.prepare_weights_mx(packed, K)
-        ws_mx = hbl.forward_mx_workspace(M, K, "cuda")
+        ws_mx = hbl.forward_mx_workspace(M, N, K, "cuda")
 
         def layer():
             hbl.forward_mx(x, wq, alpha, hadamard=had, out=out, workspace=ws_mx)
@@ -332,7 +335,7 @@ def run_decode(args, hbl, torch):
     bits = 8
     q, s, rs = hbl.hadamard_quant(x, bits)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = hbl.forward_workspace(M, K, bits, "cuda")
+    ws = hbl.forward_workspace(M, N, K, bits, "cuda")
 
     # one graph holds one decode call per matrix (cycling the matrices);
     # a step is one call
@@ -416,7 +419,7 @@ def run_msweep(args, hbl, torch):
             row = {"K": K, "N": N, "M": M}
             for name, bits, had, norm in kinds:
                 mx = not norm and use_mx(args, bits, M, K)
-                ws = hbl.forward_mx_workspace(M, K, "cuda") if mx else hbl.forward_workspace(M, K, bits, "cuda")
+                ws = hbl.forward_mx_workspace(M, N, K, "cuda") if mx else hbl.forward_workspace(M, N, K, bits, "cuda")
 
                 def all_mats():
                     for (p, a), q in zip(mats, mats_mx):

@@ -51,7 +51,7 @@ _SIGS = {
     "hbl_hadamard_f32": ([_P, _I, _I64, _I64, _I64, _P, _P], _I),
     "hbl_hadamard_quant": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P], _I),
     "hbl_ternary_gemm": ([_P, _I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
-    "hbl_forward_workspace_size": ([_I64, _I64, _I], _SZ),
+    "hbl_forward_workspace_size": ([_I64, _I64, _I64, _I], _SZ),
     "hbl_forward": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
     "hbl_hadamard_backward_f32": ([_P, _I, _I64, _I64, _I64, _P, _P], _I),
     "hbl_norm_hadamard_quant": ([_P, _I, _I64, _I64, _I64, _P, _I, _I, _P, _P, _P, _P], _I),
@@ -61,7 +61,7 @@ _SIGS = {
     "hbl_prepare_weights_mx": ([_P, _I64, _I64, _P, _P], _I),
     "hbl_hadamard_quant_mx": ([_P, _I, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "hbl_ternary_gemm_mx": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
-    "hbl_forward_mx_workspace_size": ([_I64, _I64], _SZ),
+    "hbl_forward_mx_workspace_size": ([_I64, _I64, _I64], _SZ),
     "hbl_forward_mx": ([_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
     "hbl_kv_quant": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P], _I),
     "hbl_mx_codes_bytes": ([_I64, _I64], _SZ),
@@ -229,8 +229,8 @@ def ternary_gemm(codes: torch.Tensor, bits: int, scales: torch.Tensor, rowsum: t
     return out
 
 
-def forward_workspace(M: int, K: int, bits: int, device) -> torch.Tensor:
-    return torch.empty(max(1, _lib.hbl_forward_workspace_size(M, K, bits)), dtype=torch.uint8, device=device)
+def forward_workspace(M: int, N: int, K: int, bits: int, device) -> torch.Tensor:
+    return torch.empty(max(1, _lib.hbl_forward_workspace_size(M, N, K, bits)), dtype=torch.uint8, device=device)
 
 
 def forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: int, hadamard: bool = True,
@@ -242,7 +242,7 @@ def forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: in
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
-        workspace = forward_workspace(M, K, bits, x.device)
+        workspace = forward_workspace(M, N, K, bits, x.device)
     _check(_lib.hbl_forward(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, bits,
                             _ptr(packed), _ptr(alpha), _ptr(out), out.stride(0), _ptr(workspace),
                             workspace.numel(), _stream()), "hbl_forward")
@@ -258,7 +258,7 @@ def norm_forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bit
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
-        workspace = forward_workspace(M, K, bits, x.device)
+        workspace = forward_workspace(M, N, K, bits, x.device)
     _check(_lib.hbl_norm_forward(_ptr(x), _x_dtype(x), M, K, ldx, _gain(gain, K), N,
                                  HADAMARD if hadamard else 0, bits, _ptr(packed), _ptr(alpha), _ptr(out),
                                  out.stride(0), _ptr(workspace), workspace.numel(), _stream()), "hbl_norm_forward")
@@ -303,8 +303,8 @@ def ternary_gemm_mx(codes: torch.Tensor, scales: torch.Tensor, wq: torch.Tensor,
     return out
 
 
-def forward_mx_workspace(M: int, K: int, device) -> torch.Tensor:
-    return torch.empty(max(1, _lib.hbl_forward_mx_workspace_size(M, K)), dtype=torch.uint8, device=device)
+def forward_mx_workspace(M: int, N: int, K: int, device) -> torch.Tensor:
+    return torch.empty(max(1, _lib.hbl_forward_mx_workspace_size(M, N, K)), dtype=torch.uint8, device=device)
 
 
 def forward_mx(x: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, hadamard: bool = True,
@@ -319,7 +319,7 @@ def forward_mx(x: torch.Tensor, wq: torch.Tensor, alpha: torch.Tensor, hadamard:
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
-        workspace = forward_mx_workspace(M, K, x.device)
+        workspace = forward_mx_workspace(M, N, K, x.device)
     _check(_lib.hbl_forward_mx(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, _ptr(wq), _ptr(alpha),
                                _ptr(out), out.stride(0), _ptr(workspace), workspace.numel(), _stream()),
            "hbl_forward_mx")

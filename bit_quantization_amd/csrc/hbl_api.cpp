@@ -152,7 +152,7 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, 
   if (!w_packed || !alpha || !y) return fail(HBL_ERR_NULL, "w_packed, alpha and y must be non-NULL");
   if (!aligned16(w_packed) || !aligned16(y) || !aligned4(alpha))
     return fail(HBL_ERR_ALIGN, "w_packed and y must be 16-byte aligned");
-  const size_t need = codes_region(M, K, bits);
+  const size_t need = codes_region(M, K, bits) + round256(hbl::gemm_partial_bytes(M, N, K));
   if (!ws || ws_bytes < need)
     return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
   if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -165,8 +165,10 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, 
                                             (flags & HBL_HADAMARD) != 0, bits, codes, scales, rowsum, norm, gain,
                                             cu_count_cached(), s);
   if (e != hipSuccess) return hip_fail(e, "quantise launch");
-  e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy,
-                               cu_count_cached(), s);
+  const size_t part_bytes = hbl::gemm_partial_bytes(M, N, K);
+  void* part = part_bytes ? base + codes_region(M, K, bits) : nullptr;
+  e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K, HBL_OUT_BF16, y, ldy, part,
+                               part_bytes, cu_count_cached(), s);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return HBL_OK;
 }
@@ -272,15 +274,15 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales, const int
       !aligned4(rowsum) || !aligned4(alpha))
     return fail(HBL_ERR_ALIGN, "codes, w_packed and out must be 16-byte aligned");
   hipError_t e = hbl::launch_ternary_gemm(codes, bits, scales, rowsum, w_packed, alpha, M, N, K,
-                                          out_dtype, out, ldo, cu_count_cached(),
+                                          out_dtype, out, ldo, nullptr, 0, cu_count_cached(),
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return HBL_OK;
 }
 
-size_t hbl_forward_workspace_size(int64_t M, int64_t K, int bits) {
-  if (M < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
-  return codes_region(M, K, bits);
+size_t hbl_forward_workspace_size(int64_t M, int64_t N, int64_t K, int bits) {
+  if (M < 0 || N < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
+  return codes_region(M, K, bits) + round256(hbl::gemm_partial_bytes(M, N, K));
 }
 
 int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
@@ -351,15 +353,16 @@ int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales, const uint32_
     return fail(HBL_ERR_ALIGN, "codes_mx, w_mx and out must be 16-byte aligned");
   if ((K / 4 * 3) * 256 > (int64_t)INT_MAX)  // a 256-row tile is addressed with 32-bit offsets
     return fail(HBL_ERR_SHAPE, "K = %lld is too large for the FP6 x FP4 path", (long long)K);
-  hipError_t e = hbl::launch_gemm_mx(codes_mx, scales, w_mx, alpha, M, N, K, out_dtype, out, ldo, cu_count_cached(),
-                                     static_cast<hipStream_t>(stream));
+  hipError_t e = hbl::launch_gemm_mx(codes_mx, scales, w_mx, alpha, M, N, K, out_dtype, out, ldo, nullptr, 0,
+                                     cu_count_cached(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return HBL_OK;
 }
 
-size_t hbl_forward_mx_workspace_size(int64_t M, int64_t K) {
-  if (M < 0 || K <= 0) return 0;
-  return round256(hbl_mx_codes_bytes(M, K)) + round256(sizeof(float) * (size_t)M);
+size_t hbl_forward_mx_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  return round256(hbl_mx_codes_bytes(M, K)) + round256(sizeof(float) * (size_t)M) +
+         round256(hbl::gemm_mx_partial_bytes(M, N, K));
 }
 
 int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int64_t N, int flags,
@@ -375,17 +378,21 @@ int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx
   if (!w_mx || !alpha || !y) return fail(HBL_ERR_NULL, "w_mx, alpha and y must be non-NULL");
   if (!aligned16(w_mx) || !aligned16(y) || !aligned4(alpha))
     return fail(HBL_ERR_ALIGN, "w_mx and y must be 16-byte aligned");
-  const size_t need = hbl_forward_mx_workspace_size(M, K);
+  const size_t need = hbl_forward_mx_workspace_size(M, N, K);
   if (!ws || ws_bytes < need)
     return fail(HBL_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
   if (!aligned16(ws)) return fail(HBL_ERR_ALIGN, "workspace is not 16-byte aligned");
   void* codes = ws;
-  float* scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(hbl_mx_codes_bytes(M, K)));
+  const size_t codes_end = round256(hbl_mx_codes_bytes(M, K));
+  float* scales = reinterpret_cast<float*>(static_cast<char*>(ws) + codes_end);
+  void* part = static_cast<char*>(ws) + codes_end + round256(sizeof(float) * (size_t)M);
+  const size_t part_bytes = hbl::gemm_mx_partial_bytes(M, N, K);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hbl::launch_hadamard_quant(x, x_dtype == HBL_DTYPE_BF16, M, (int)K, ldx, (flags & HBL_HADAMARD) != 0,
                                             6, codes, scales, nullptr, false, nullptr, cu_count_cached(), s);
   if (e != hipSuccess) return hip_fail(e, "quantise launch");
-  e = hbl::launch_gemm_mx(codes, scales, w_mx, alpha, M, N, K, HBL_OUT_BF16, y, ldy, cu_count_cached(), s);
+  e = hbl::launch_gemm_mx(codes, scales, w_mx, alpha, M, N, K, HBL_OUT_BF16, y, ldy, part_bytes ? part : nullptr,
+                          part_bytes, cu_count_cached(), s);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return HBL_OK;
 }

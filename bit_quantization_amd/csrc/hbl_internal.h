@@ -24,18 +24,75 @@ hipError_t launch_ternarize(const void* w, bool w_bf16, int64_t N, int64_t K,
                             int n_partials, hipStream_t s);
 int ternarize_partials(int64_t N, int64_t K);
 
-// out_kind: 0 bf16, 1 f32, 2 i32 (the HBL_OUT_* values)
+// Tiles and K split of the persistent matmuls (k_gemm_pt, k_gemm_mx):
+// 256 x 256 tiles when they alone fill the chip (cu_count of them), else
+// 256 x 128; below kSplitItems tiles the K range (nk stages of 128) is
+// halved while the items (tile, K slice) fit kSplitItems and each keeps at
+// least 16 stages, and once more (to 8 stages) while they fit half of them.
+// Measured on MI355X at N = 4096 (FP6 x FP4 path, every split
+// bit-identical): K = 4096, M <= 256 best at 4 slices; K = 16384, M <= 256
+// at 8, M = 512 at 4, M = 1024 at 2; from 256 tiles on, none.
+struct SplitPlan {
+  int bn, tm, tn, ksplit;
+  int64_t items() const { return (int64_t)tm * tn * ksplit; }
+};
+constexpr int kSplitItems = 256;
+inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
+  SplitPlan p;
+  const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
+  p.bn = g256 >= cu_count ? 256 : 128;
+  p.tm = (int)((M + 255) / 256);
+  p.tn = (int)((N + p.bn - 1) / p.bn);
+  p.ksplit = 1;
+  const int64_t G = (int64_t)p.tm * p.tn, nk = K / 128;
+  auto ok = [&](int S, int64_t items, int64_t min_stages) {
+    return may_split && p.bn == 128 && G * S <= items && (nk / 4) % S == 0 && nk / S >= min_stages;
+  };
+  while (ok(p.ksplit * 2, kSplitItems, 16)) p.ksplit *= 2;
+  if (ok(p.ksplit * 2, kSplitItems / 2, 8)) p.ksplit *= 2;
+  return p;
+}
+
+#if defined(__HIPCC__)
+// Work item L of a split plan: K slice L / (tilesM tilesN), tile
+// L % (tilesM tilesN); tiles walked in M-groups of 8 so that neighbouring
+// items share code rows or weight rows in an XCD's L2.
+template <int BM, int BN>
+__device__ __forceinline__ void split_item(int L, int tilesM, int tilesN, int64_t& m0, int64_t& n0, int& ks) {
+  const int G = tilesM * tilesN;
+  ks = L / G;
+  const int T = L - ks * G;
+  constexpr int GROUP_M = 8;
+  const int per_group = GROUP_M * tilesN;
+  const int first_m = (T / per_group) * GROUP_M;
+  const int gsz = GROUP_M < tilesM - first_m ? GROUP_M : tilesM - first_m;
+  m0 = (int64_t)(first_m + (T % per_group) % gsz) * BM;
+  n0 = (int64_t)((T % per_group) / gsz) * BN;
+}
+#endif
+
+// out_kind: 0 bf16, 1 f32, 2 i32 (the HBL_OUT_* values).
+// part: scratch for int32 partial sums of a K split of the persistent
+// matmul (part_bytes of it; NULL: no split, and token counts up to
+// kGemvMaxM stream the weights)
 hipError_t launch_ternary_gemm(const void* codes, int bits, const float* scales,
                                const int32_t* rowsum, const uint32_t* wp,
                                const float* alpha, int64_t M, int64_t N,
                                int64_t K, int out_kind, void* out, int64_t ldo,
-                               int cu_count, hipStream_t s);
+                               void* part, size_t part_bytes, int cu_count,
+                               hipStream_t s);
+// bytes of partial sums launch_ternary_gemm uses for a K split (0: none)
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K);
 
 // FP6 x FP4 matmul of MX6 codes and MX4 weights (k_gemm_mx.hip); K % 512 == 0.
+// part: scratch for the exact partial sums of a K split (part_bytes of
+// it); NULL or too small runs the matmul unsplit
 hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t* wq,
                           const float* alpha, int64_t M, int64_t N, int64_t K,
-                          int out_kind, void* out, int64_t ldo, int cu_count,
-                          hipStream_t s);
+                          int out_kind, void* out, int64_t ldo, void* part,
+                          size_t part_bytes, int cu_count, hipStream_t s);
+// bytes of partial sums launch_gemm_mx uses for a K split (0: no split)
+size_t gemm_mx_partial_bytes(int64_t M, int64_t N, int64_t K);
 // ternary layout -> MX4 layout (same size)
 hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t* wq,
                               hipStream_t s);

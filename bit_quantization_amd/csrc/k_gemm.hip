@@ -315,12 +315,21 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 // into distinct banks.
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
+// smallest M K at which the int8 layer takes the split persistent matmul
+constexpr int64_t kSplitMinMK = int64_t(1) << 20;
+
+// int32 partial sums of a split plan's 256 x 128 items (0: no split)
+size_t pt_partial_bytes(const SplitPlan& p) {
+  return p.ksplit > 1 ? (size_t)p.items() * 256 * 128 * sizeof(int32_t) : 0;
+}
+
 template <int BITS, int OUT, int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
 k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
           const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
-          void* __restrict__ out, int64_t ldo, int tilesM, int tilesN) {
+          void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int ksplit,
+          int4* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int BK = 128, NSTEP = BK / 32, NST = 4;  // NST stage buffers; also the unroll
@@ -352,23 +361,19 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   const int wm = wave % 2, wn = wave / 2;
   const int64_t arow_bytes = BITS == 4 ? K / 2 : K;  // global code row stride
   const int64_t brow_bytes = K / 4;                  // global weight row stride
-  const int nk = (int)(K / BK);                      // a multiple of NST
+  const int nks = (int)(K / BK) / ksplit;            // stages of one item (a multiple of NST)
 
-  // Tiles of this block: r P + slot for r = 0, 1, ... (P blocks, a multiple
+  // Items of this block: r P + slot for r = 0, 1, ... (P blocks, a multiple
   // of 8).  Consecutive block ids go to different XCDs; slot gives each XCD
-  // a contiguous range of each round's tiles, which are then walked in
-  // M-groups of 8 so that an XCD's blocks share codes and weights in its L2.
-  const int G = tilesM * tilesN, P = gridDim.x, b = blockIdx.x;
+  // a contiguous range of each round's items (split_item: a tile and one of
+  // ksplit K slices, tiles walked in M-groups of 8 so that an XCD's blocks
+  // share codes and weights in its L2).  With ksplit > 1 an item leaves its
+  // int32 partial sums in part for k_pt_reduce.
+  const int G = tilesM * tilesN * ksplit, P = gridDim.x, b = blockIdx.x;
   const int slot = (b % 8) * (P / 8) + b / 8;
   const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
-  auto tile_of = [&](int r, int64_t& m0, int64_t& n0) {
-    const int L = r * P + slot;
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * tilesN;
-    const int first_m = (L / per_group) * GROUP_M;
-    const int gsz = min(GROUP_M, tilesM - first_m);
-    m0 = (int64_t)(first_m + (L % per_group) % gsz) * BM;
-    n0 = (int64_t)((L % per_group) / gsz) * BN;
+  auto tile_of = [&](int r, int64_t& m0, int64_t& n0, int& ks) {
+    split_item<BM, BN>(r * P + slot, tilesM, tilesN, m0, n0, ks);
   };
 
   auto aswz = [](int r, int u) { return u ^ ((r >> ASH) & (AU - 1)); };
@@ -390,13 +395,19 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   __amdgpu_buffer_rsrc_t rA, rB;
   auto set_tile = [&](int r) {
     int64_t m0 = 0, n0 = 0;
-    if (r < ntiles) tile_of(r, m0, n0);
+    int ks = 0;
+    if (r < ntiles) tile_of(r, m0, n0, ks);
     const int arows = r < ntiles ? (int)min<int64_t>(BM, M - m0) : 0;
     const int brows = r < ntiles ? (int)min<int64_t>(BN, N - n0) : 0;
-    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(codes) + m0 * arow_bytes),
-                                           (short)0, (int)(arows * arow_bytes), 0x00020000);
-    rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wp) + n0 * brow_bytes),
-                                           (short)0, (int)(brows * brow_bytes), 0x00020000);
+    // both ranges start at the item's first column (rows keep their stride;
+    // the range still ends with the tile's last row)
+    const int64_t ka = (int64_t)ks * nks * AROW, kb = (int64_t)ks * nks * BROW;
+    rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(codes) + m0 * arow_bytes + ka), (short)0,
+        arows > 0 ? (int)(arows * arow_bytes - ka) : 0, 0x00020000);
+    rB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wp) + n0 * brow_bytes + kb), (short)0,
+        brows > 0 ? (int)(brows * brow_bytes - kb) : 0, 0x00020000);
   };
   // loads of stage (dr, dk) into buffer I; advances the cursor
   auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
@@ -411,7 +422,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
     for (int j = 0; j < BDMA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
-    if (++dk == nk) {
+    if (++dk == nks) {
       dk = 0;
       set_tile(++dr);
     }
@@ -507,8 +518,28 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     // r made opaque here: nothing of the epilogue is computed early and kept
     // live through the stage loop
     asm volatile("" : "+s"(r));
+    if (BN == 128 && ksplit > 1) {
+      // raw int32 partial sums in fragment order: each store is 1 KB
+      // contiguous (splits use 256 x 128 tiles only)
+      int4* dst = part + ((int64_t)(r * P + slot) * NW + wave) * (FN * FM * 4 * 64) + lane;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16i& a = acc[i][j];
+            dst[((i * FM + j) * 4 + q) * 64] = make_int4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
+      return;
+    }
     int64_t m0, n0;
-    tile_of(r, m0, n0);
+    int ks;
+    tile_of(r, m0, n0, ks);
     const float al = *alpha;
     if constexpr (STAGE_OUT) {
       // bf16 through LDS: for fragment row j the wave writes its 32 tokens x
@@ -614,7 +645,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     mfmas(d0);
     mfmas(d1);
   };
-  const int groups_per_tile = nk / NST;
+  const int groups_per_tile = nks / NST;
   for (int r = 0; r < ntiles; ++r) {
     for (int gq = 0; gq < groups_per_tile; ++gq) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -877,10 +908,68 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
   }
 }
 
+// Sum of the ksplit int32 partial sums of k_gemm_pt's 256 x 128 tiles, then
+// the epilogue of Eq. 9 (/ 16 for INT4, minus the row sum, rescale).  One
+// thread per four outputs of one lane's fragment, reading the partials in
+// the order k_gemm_pt wrote them.
+template <int BITS, int OUT>
+__global__ void __launch_bounds__(256)
+k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, const float* __restrict__ scales,
+            const int32_t* __restrict__ rowsum, const float* __restrict__ alpha, int64_t M, int64_t N,
+            void* __restrict__ out, int64_t ldo) {
+  constexpr int BM = 256, BN = 128, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  const int64_t units = (int64_t)tilesM * tilesN * (BM * BN / 4);
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const int lane = (int)(u % 64);
+  int64_t t = u / 64;
+  const int q = (int)(t % 4);
+  t /= 4;
+  const int ij = (int)(t % (FN * FM));
+  t /= FN * FM;
+  const int wave = (int)(t % 4);
+  const int T = (int)(t / 4);
+  const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
+  int64_t m0, n0;
+  int ks;
+  split_item<BM, BN>(T, tilesM, tilesN, m0, n0, ks);
+  const int64_t m = m0 + wm * WM + 32 * j + fr, n = n0 + wn * WN + 32 * i + 8 * q + 4 * h;
+  if (m >= M || n >= N) return;
+  int4 a = part[u];
+  for (int s = 1; s < ksplit; ++s) {
+    const int4 b = part[u + s * units];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  v4i v = v4i{a.x, a.y, a.z, a.w};
+  if constexpr (BITS == 4) v = v >> 4;  // exact: every product carries a factor 16
+  store4<OUT>(out, m * ldo + n, v, rowsum[m], scales[m] * *alpha);
+}
+
 template <int BITS, int OUT>
 hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t* rowsum,
                            const uint32_t* wp, const float* alpha, int64_t M, int64_t N, int64_t K,
-                           void* out, int64_t ldo, int cu_count, hipStream_t s) {
+                           void* out, int64_t ldo, void* part, size_t part_bytes, int cu_count, hipStream_t s) {
+  // with room for a K split, the persistent matmul beats weight streaming
+  // from M K >= 2^20 (measured at N = 4096: M >= 64 at K = 16384, M >= 256
+  // at K = 4096); 16 tokens or fewer always stream
+  const bool split_ok = part != nullptr && K % 512 == 0 && M > 16 && M * K >= kSplitMinMK &&
+                        part_bytes >= pt_partial_bytes(split_plan(M, N, K, cu_count, true));
+  if (split_ok) {
+    const SplitPlan p = split_plan(M, N, K, cu_count, true);
+    if (p.ksplit > 1) {
+      const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
+      const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
+      int4* pt = static_cast<int4*>(part);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
+                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.ksplit, pt);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t units = (int64_t)p.tm * p.tn * (256 * 128 / 4);
+      hipLaunchKernelGGL((k_pt_reduce<BITS, OUT>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, pt,
+                         p.ksplit, p.tm, p.tn, scales, rowsum, alpha, M, N, out, ldo);
+      return hipGetLastError();
+    }
+  }
   if (M <= 4 && K % 1024 == 0) {
     const int64_t tk = K / 64 < 256 ? K / 64 : 256;
 #define HBL_DOT(MT, TK)                                                                                      \
@@ -901,7 +990,7 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 #undef HBL_DOT_TK
 #undef HBL_DOT
   }
-  if (M <= kGemvMaxM) {
+  if (M <= kGemvMaxM && !split_ok) {
     // weight streaming with the tokens in groups of 16: every CU busy (one
     // block per 16 features) where the matrix-core tiles would leave most
     // of them idle
@@ -925,10 +1014,10 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
     const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
     if (bn == 256) {
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, tm, tn);
+                         wp, alpha, M, N, K, out, ldo, tm, tn, 1, nullptr);
     } else {
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, tm, tn);
+                         wp, alpha, M, N, K, out, ldo, tm, tn, 1, nullptr);
     }
     return hipGetLastError();
   }
@@ -950,12 +1039,19 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 
 }  // namespace
 
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16 || N <= 0 || K % 512 != 0 || M * K < kSplitMinMK) return 0;
+  return pt_partial_bytes(split_plan(M, N, K, kSplitItems, true));
+}
+
 hipError_t launch_ternary_gemm(const void* codes, int bits, const float* scales, const int32_t* rowsum,
                                const uint32_t* wp, const float* alpha, int64_t M, int64_t N, int64_t K,
-                               int out_kind, void* out, int64_t ldo, int cu_count, hipStream_t s) {
+                               int out_kind, void* out, int64_t ldo, void* part, size_t part_bytes, int cu_count,
+                               hipStream_t s) {
   if (M == 0) return hipSuccess;
-#define HBL_G(BITS, OUT) \
-  return launch_bits_out<BITS, OUT>(codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, cu_count, s)
+#define HBL_G(BITS, OUT)                                                                                      \
+  return launch_bits_out<BITS, OUT>(codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, part, part_bytes, \
+                                    cu_count, s)
   if (bits == 8) {
     if (out_kind == 0) HBL_G(8, 0);
     if (out_kind == 1) HBL_G(8, 1);

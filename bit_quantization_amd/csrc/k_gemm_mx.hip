@@ -99,7 +99,7 @@ template <int OUT, int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
 k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, const uint32_t* __restrict__ wq,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
-          int tilesM, int tilesN) {
+          int tilesM, int tilesN, int ksplit, int p16, void* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
@@ -134,23 +134,18 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   const int wm = wave % 2, wn = wave / 2;
   const int64_t arow_bytes = K / 4 * 3;  // global code row stride (MX6)
   const int64_t brow_bytes = K / 4;      // global weight row stride (MX4)
-  const int nk = (int)(K / BK);          // a multiple of NST
+  const int nk = (int)(K / BK);          // stages of the whole K
+  const int nks = nk / ksplit;           // stages of one item (a multiple of NST)
 
-  // Tiles of this block: r P + slot (P blocks, a multiple of 8); slot gives
-  // each XCD a contiguous range of each round's tiles, walked in M-groups of
-  // 8 so that an XCD's blocks share codes and weights in its L2.
-  const int G = tilesM * tilesN, P = gridDim.x, b = blockIdx.x;
+  // Items of this block: r P + slot (P blocks, a multiple of 8); slot gives
+  // each XCD a contiguous range of each round's items.  An item is a tile
+  // and one of ksplit K slices; with ksplit > 1 it leaves its exact partial
+  // sums in part for k_mx_reduce, as int16 when p16 (|sum| <= 8 K / ksplit
+  // fits), else as fp32.
+  const int G = tilesM * tilesN * ksplit, P = gridDim.x, b = blockIdx.x;
   const int slot = (b % 8) * (P / 8) + b / 8;
   const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
-  auto tile_of = [&](int r, int64_t& m0, int64_t& n0) {
-    const int L = r * P + slot;
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * tilesN;
-    const int first_m = (L / per_group) * GROUP_M;
-    const int gsz = min(GROUP_M, tilesM - first_m);
-    m0 = (int64_t)(first_m + (L % per_group) % gsz) * BM;
-    n0 = (int64_t)((L % per_group) / gsz) * BN;
-  };
+  auto tile_of = [&](int r, int64_t& m0, int64_t& n0, int& ks) { split_item<BM, BN>(r * P + slot, tilesM, tilesN, m0, n0, ks); };
 
   auto mswz = [](int r, int u) { return u ^ ((r >> MSH) & (MU - 1)); };
   auto tswz = [](int r, int u) { return u ^ ((r >> TSH) & (TU - 1)); };
@@ -169,15 +164,19 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   __amdgpu_buffer_rsrc_t rA, rB;
   auto set_tile = [&](int r) {
     int64_t m0 = 0, n0 = 0;
-    if (r < ntiles) tile_of(r, m0, n0);
+    int ks = 0;
+    if (r < ntiles) tile_of(r, m0, n0, ks);
     // the code buffer holds whole 256-row blocks (rows past M are padding,
-    // their outputs are not stored); the weight buffer whole 128-row blocks
+    // their outputs are not stored); the weight buffer whole 128-row blocks.
+    // Both ranges start at the item's first stage.
     const int64_t wrows = (N + 127) / 128 * 128;
     const int brows = r < ntiles ? (int)min<int64_t>(BN, wrows - n0) : 0;
-    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + m0 * arow_bytes), (short)0,
-                                           r < ntiles ? (int)(BM * arow_bytes) : 0, 0x00020000);
-    rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes),
-                                           (short)0, (int)(brows * brow_bytes), 0x00020000);
+    const int64_t ka = (int64_t)ks * nks * 24576, kb = (int64_t)ks * nks * 4096;
+    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + m0 * arow_bytes + ka), (short)0,
+                                           r < ntiles ? (int)(BM * arow_bytes - ka) : 0, 0x00020000);
+    rB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes + kb), (short)0,
+        r < ntiles ? (int)(brows * brow_bytes - kb) : 0, 0x00020000);
   };
   auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
     uint8_t* const Md = mbuf(bi);
@@ -195,7 +194,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
 #pragma unroll
     for (int j = 0; j < BDMA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * wblk, 0, 0, 0);
-    if (++dk == nk) {
+    if (++dk == nks) {
       dk = 0;
       set_tile(++dr);
     }
@@ -270,8 +269,45 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     asm volatile("" : "+s"(r));
     int fr = lane % 32, h = lane / 32;
     asm volatile("" : "+v"(fr), "+v"(h));
+    if (BN == 128 && ksplit > 1) {
+      // exact partial sums, in fragment order: each store is 1 KB contiguous
+      // (splits use 256 x 128 tiles only)
+      const int64_t item = r * P + slot;
+      if (p16) {
+        uint4* dst = static_cast<uint4*>(part) + (item * NW + wave) * (FN * FM * 2 * 64) + lane;
+        auto pk = [](float lo, float hi) { return ((uint32_t)(int)lo & 0xffffu) | ((uint32_t)(int)hi << 16); };
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const v16f& a = acc[i][j];
+              const int e = 8 * qq;
+              dst[((i * FM + j) * 2 + qq) * 64] =
+                  make_uint4(pk(a[e], a[e + 1]), pk(a[e + 2], a[e + 3]), pk(a[e + 4], a[e + 5]), pk(a[e + 6], a[e + 7]));
+            }
+      } else {
+        float4* dst = static_cast<float4*>(part) + (item * NW + wave) * (FN * FM * 4 * 64) + lane;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const v16f& a = acc[i][j];
+              dst[((i * FM + j) * 4 + q) * 64] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+            }
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
+      return;
+    }
     int64_t m0, n0;
-    tile_of(r, m0, n0);
+    int ks;
+    tile_of(r, m0, n0, ks);
     const float al = *alpha;
     if constexpr (STAGE_OUT) {
       uint8_t* const Ow = Os + wave * 32 * OROW;
@@ -361,7 +397,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     step(wf1, cur.c1);
     decw(wf0, nxt.w, 0);
   };
-  const int groups_per_tile = nk / NST;
+  const int groups_per_tile = nks / NST;
   for (int r = 0; r < ntiles; ++r) {
     for (int gq = 0; gq < groups_per_tile; ++gq) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -413,25 +449,119 @@ hipError_t launch_prepare_mx4(const uint32_t* wp, int64_t N, int64_t K, uint32_t
   return hipGetLastError();
 }
 
+namespace {
+
+// Sum of the ksplit partial sums of each output (exact integers: any order
+// gives the same value), then the rescale of Eq. 9.  One thread per four
+// (fp32 partials) or eight (int16) outputs of one lane's fragment, reading
+// the partials in the order k_gemm_mx wrote them.
+template <int OUT, int BN, bool P16>
+__global__ void __launch_bounds__(256)
+k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, const float* __restrict__ scales,
+            const float* __restrict__ alpha, int64_t M, int64_t N, void* __restrict__ out, int64_t ldo) {
+  constexpr int BM = 256, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int QU = P16 ? 2 : 4;                        // 16-byte units per fragment and lane
+  const int64_t per_tile = (int64_t)4 * FN * FM * QU * 64;  // units of one tile
+  const int64_t units = (int64_t)tilesM * tilesN * per_tile;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const int lane = (int)(u % 64);
+  int64_t t = u / 64;
+  const int q = (int)(t % QU);
+  t /= QU;
+  const int ij = (int)(t % (FN * FM));
+  t /= FN * FM;
+  const int wave = (int)(t % 4);
+  const int T = (int)(t / 4);
+  const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
+  int64_t m0, n0;
+  int ks;
+  split_item<BM, BN>(T, tilesM, tilesN, m0, n0, ks);
+  const int64_t m = m0 + wm * WM + 32 * j + fr;
+  const int64_t n = n0 + wn * WN + 32 * i + (P16 ? 16 : 8) * q + 4 * h;
+  if (m >= M || n >= N) return;
+  const float sc = scales[m] * *alpha;
+  if constexpr (P16) {
+    const uint4* p = static_cast<const uint4*>(part) + u;
+    int v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < ksplit; ++s) {
+      const uint4 b = p[s * units];
+      const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] += (int)(int16_t)(w[e] & 0xffffu);
+        v[2 * e + 1] += (int)(int16_t)(w[e] >> 16);
+      }
+    }
+    store4f<OUT>(out, m * ldo + n, (float)v[0], (float)v[1], (float)v[2], (float)v[3], sc);
+    if (n + 8 < N) store4f<OUT>(out, m * ldo + n + 8, (float)v[4], (float)v[5], (float)v[6], (float)v[7], sc);
+  } else {
+    const float4* p = static_cast<const float4*>(part) + u;
+    float4 a = p[0];
+    for (int s = 1; s < ksplit; ++s) {
+      const float4 b = p[s * units];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    store4f<OUT>(out, m * ldo + n, a.x, a.y, a.z, a.w, sc);
+  }
+}
+
+struct MxPlan : SplitPlan {
+  bool p16;  // int16 partial sums
+  size_t part_bytes() const { return ksplit > 1 ? (size_t)ksplit * tm * tn * 256 * bn * (p16 ? 2 : 4) : 0; }
+};
+
+MxPlan mx_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
+  MxPlan p;
+  static_cast<SplitPlan&>(p) = split_plan(M, N, K, cu_count, may_split);
+  p.p16 = 8 * (K / p.ksplit) <= 32767;  // |partial sum| <= 8 K / ksplit
+  return p;
+}
+
+}  // namespace
+
+size_t gemm_mx_partial_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return mx_plan(M, N, K, kSplitItems, true).part_bytes();
+}
+
 hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t* wq, const float* alpha, int64_t M,
-                          int64_t N, int64_t K, int out_kind, void* out, int64_t ldo, int cu_count, hipStream_t s) {
+                          int64_t N, int64_t K, int out_kind, void* out, int64_t ldo, void* part, size_t part_bytes,
+                          int cu_count, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int bn = g256 >= cu_count ? 256 : 128;
-  const int tm = (int)((M + 255) / 256), tn = (int)((N + bn - 1) / bn);
-  const int64_t G = (int64_t)tm * tn;
+  // the split is sized for kSplitItems CUs; with a workspace too small for it
+  // (or none) the matmul runs unsplit
+  MxPlan p = mx_plan(M, N, K, cu_count, part != nullptr);
+  if (p.ksplit > 1 && part_bytes < p.part_bytes()) p.ksplit = 1;
+  const int64_t G = (int64_t)p.tm * p.tn * p.ksplit;
   const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, p16 = p.p16 ? 1 : 0;
 #define HBL_MX(OUT, BN)                                                                                          \
   hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN>), dim3((unsigned)P), dim3(256), 0, s, c, scales, wq, alpha, M, N, K, \
-                     out, ldo, tm, tn)
-  if (bn == 256) {
+                     out, ldo, tm, tn, ksplit, p16, part)
+  if (p.bn == 256) {
     if (out_kind == 0) HBL_MX(0, 256); else if (out_kind == 1) HBL_MX(1, 256); else HBL_MX(2, 256);
   } else {
     if (out_kind == 0) HBL_MX(0, 128); else if (out_kind == 1) HBL_MX(1, 128); else HBL_MX(2, 128);
   }
 #undef HBL_MX
+  if (ksplit == 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // splits use 256 x 128 tiles only
+  const int64_t units = (int64_t)tm * tn * 256 * 128 / (p16 ? 8 : 4);
+  const unsigned rb = (unsigned)((units + 255) / 256);
+#define HBL_MXR(OUT, P16)                                                                                      \
+  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, scales, alpha, \
+                     M, N, out, ldo)
+  if (p16) {
+    if (out_kind == 0) HBL_MXR(0, true); else if (out_kind == 1) HBL_MXR(1, true); else HBL_MXR(2, true);
+  } else {
+    if (out_kind == 0) HBL_MXR(0, false); else if (out_kind == 1) HBL_MXR(1, false); else HBL_MXR(2, false);
+  }
+#undef HBL_MXR
   return hipGetLastError();
 }
 

@@ -209,12 +209,16 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
  *   y = bf16( (scale_m * alpha) * sum_k q_x[m][k] q_w[n][k] ),
  * q_x the codes of hbl_hadamard_quant(x, flags, bits).
  * y: out, bf16 [M][ldy]; ldy >= N, ldy % 4 == 0.
- * ws: device workspace of at least hbl_forward_workspace_size(M, K, bits)
- *     bytes; it receives the codes, scales and row sums (scratch).
+ * ws: device workspace of at least hbl_forward_workspace_size(M, N, K,
+ *     bits) bytes; it receives the codes, scales and row sums (scratch)
+ *     and, when the matmul's 256-token tiles would leave most compute
+ *     units idle (fewer than 256 of them, M K >= 2^20, M > 16, K % 512 ==
+ *     0), the int32 partial sums of a split of K (at most 32 MiB); integer
+ *     sums make the output the same bits with or without the split.
  * Shapes: the union of the rules of hbl_hadamard_quant and
  * hbl_ternary_gemm.  Two kernels are enqueued.
  * ------------------------------------------------------------------- */
-size_t hbl_forward_workspace_size(int64_t M, int64_t K, int bits);
+size_t hbl_forward_workspace_size(int64_t M, int64_t N, int64_t K, int bits);
 int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                 int64_t N, int flags, int bits, const uint32_t* w_packed,
                 const float* alpha, void* y, int64_t ldy, void* ws,
@@ -224,7 +228,7 @@ int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
  * hbl_norm_forward -- the whole layer of Eq. 9 with its normalisation:
  * hbl_norm_hadamard_quant(x, gain, flags, bits) then hbl_ternary_gemm.
  * Arguments as hbl_forward plus gain (as hbl_norm_hadamard_quant); the
- * workspace is hbl_forward_workspace_size(M, K, bits) bytes.
+ * workspace is hbl_forward_workspace_size(M, N, K, bits) bytes.
  * ------------------------------------------------------------------- */
 int hbl_norm_forward(const void* x, int x_dtype, int64_t M, int64_t K,
                      int64_t ldx, const float* gain, int64_t N, int flags,
@@ -348,9 +352,13 @@ int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales,
 /* hbl_forward_mx -- the INT4 layer of Eq. 9 on this path:
  * hbl_hadamard_quant_mx then hbl_ternary_gemm_mx (bf16 output), the same
  * result as hbl_forward(..., bits = 4).  ws: at least
- * hbl_forward_mx_workspace_size(M, K) bytes (MX6 codes and scales).
+ * hbl_forward_mx_workspace_size(M, N, K) bytes: the MX6 codes, the scales
+ * and, when the 256-token tiles alone would leave most compute units idle
+ * (fewer than 256 tiles), room for the exact partial sums of a split of K
+ * (at most 32 MiB), whose sum is order-independent, so the output is the
+ * same bits with or without the split.
  * Shapes: the union of the two calls' rules. */
-size_t hbl_forward_mx_workspace_size(int64_t M, int64_t K);
+size_t hbl_forward_mx_workspace_size(int64_t M, int64_t N, int64_t K);
 int hbl_forward_mx(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                    int64_t N, int flags, const uint32_t* w_mx, const float* alpha,
                    void* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream);

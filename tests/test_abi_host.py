@@ -110,9 +110,17 @@ def test_gemm_errors(hbl):
 
 def test_forward_workspace(hbl):
     lib = hbl.lib()
-    need = lib.hbl_forward_workspace_size(10, 256, 4)
+    need = lib.hbl_forward_workspace_size(10, 64, 256, 4)
     assert need >= 10 * 128 + 2 * 40
     assert need % 256 == 0
+    # room for int32 partial sums of a K split of the persistent matmul when
+    # its 256 x 128 tiles leave most CUs idle and M K >= 2^20: M = 64,
+    # N = 4096, K = 16384 -> 32 tiles, 8 slices; M = 32 streams the weights
+    assert lib.hbl_forward_workspace_size(32, 4096, 16384, 8) == 32 * 16384 + 2 * 256
+    assert lib.hbl_forward_workspace_size(64, 4096, 16384, 8) == 64 * 16384 + 2 * 256 + 8 * 32 * 256 * 128 * 4
+    # 16 tokens stream the weights; 256 tiles need no split
+    assert lib.hbl_forward_workspace_size(16, 4096, 16384, 8) == 16 * 16384 + 2 * 256
+    assert lib.hbl_forward_workspace_size(2048, 4096, 4096, 4) == 2048 * 2048 + 2 * 8192
     rc = lib.hbl_forward(A, 1, 10, 256, 256, 64, 1, 4, B, C, D, 64, E, need - 1, None)
     assert rc == hbl.ERR_WORKSPACE
     rc = lib.hbl_forward(A, 1, 10, 256, 256, 64, 1, 4, B, C, D, 64, None, need, None)
@@ -154,7 +162,7 @@ def test_norm_quant_errors(hbl):
 
 def test_norm_forward_errors(hbl):
     lib = hbl.lib()
-    need = lib.hbl_forward_workspace_size(10, 256, 4)
+    need = lib.hbl_forward_workspace_size(10, 64, 256, 4)
     f = lib.hbl_norm_forward
     assert f(A, 1, 10, 256, 256, F + 8, 64, 1, 4, B, C, D, 64, E, need, None) == hbl.ERR_ALIGN
     assert f(A, 1, 10, 256, 256, None, 64, 1, 4, B, C, D, 64, E, need - 1, None) == hbl.ERR_WORKSPACE
@@ -204,8 +212,17 @@ def test_mx_entry_point_errors(hbl):
     # whole 256-row code blocks and 128-row weight blocks
     assert lib.hbl_mx_codes_bytes(10, 1024) == 256 * 768 and lib.hbl_mx_codes_bytes(257, 1024) == 512 * 768
     assert lib.hbl_mx_weights_bytes(130, 1024) == 256 * 256 and lib.hbl_mx_weights_bytes(128, 1024) == 128 * 256
-    need = lib.hbl_forward_mx_workspace_size(10, 1024)
+    need = lib.hbl_forward_mx_workspace_size(10, 64, 1024)
     assert need >= 256 * 768 + 40 and need % 256 == 0
+    # fewer than 256 tiles of 256 x 128: room for a split of K (one tile;
+    # at least 8 stages of 128 per slice, so none at K = 1024; at K = 16384
+    # 16 slices of 256 x 128 int16 partial sums, |sum| <= 8 * 1024)
+    assert lib.hbl_forward_mx_workspace_size(10, 64, 16384) == 256 * 12288 + 256 + 16 * 256 * 128 * 2
+    # M = 1024, N = K = 16384: 128 tiles, 2 slices of 8192 (fp32 partials)
+    assert lib.hbl_forward_mx_workspace_size(1024, 4096, 16384) == 1024 * 12288 + 4096 + 2 * 1024 * 4096 * 4
+    # 256 tiles already: no split
+    big = lib.hbl_forward_mx_workspace_size(4096, 4096, 16384)
+    assert big == 4096 * 12288 + 4096 * 4
     f = lib.hbl_forward_mx
     assert f(A, 1, 10, 1024, 1024, 64, 1, B, C, D, 64, E, need - 1, None) == hbl.ERR_WORKSPACE
     assert f(A, 1, 10, 2048, 2048, 64, 1, B, C, D, 64, E, need, None) == hbl.ERR_WORKSPACE

@@ -138,3 +138,39 @@ def test_gemm_mx_full_tile_grid_exact(hbl):
     # on the GPU's own codes (identical to the oracle's up to ties)
     assert np.array_equal(acc.cpu().numpy()[rows], oracle.gemm_i32(oracle.pack_int4(gq), 4, o_packed, K))
     assert np.abs(gq.astype(int) - oracle.unpack_int4(oq, K).astype(int)).max() <= 1
+
+
+# (M, N, K) -> slices: (1, 4096, 16384) 8, (100, 272, 4096) 4, (256, 4096,
+# 16384) 8, (300, 528, 8192) 8, (1024, 4096, 4096) 2 (int16 partial sums);
+# (200, 4224, 16384) 4 (slices of 4096: fp32 partial sums)
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 16384), (100, 272, 4096), (256, 4096, 16384), (300, 528, 8192),
+                                   (1024, 4096, 4096), (200, 4224, 16384)])
+def test_forward_mx_k_split(hbl, M, N, K):
+    # fewer than 256 tiles: the layer splits K over the workspace's partial
+    # sums; exact integer partials give the unsplit matmul's bits
+    lib = hbl.lib()
+    assert lib.hbl_forward_mx_workspace_size(M, N, K) > lib.hbl_mx_codes_bytes(M, K) + 4 * M + 512
+    x_np = workloads.random_rows(M + 3 * N + K, M, K, "t3")
+    w, packed, alpha, wq = _weights(hbl, N, K, 8)
+    x = to_device(x_np)
+    y = hbl.forward_mx(x, wq, alpha, N=N)
+    cm, sm = hbl.hadamard_quant_mx(x)
+    y1 = hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, N=N)  # no workspace: unsplit
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    y_int = hbl.forward(x, packed, alpha, 4)
+    assert torch.equal(y.view(torch.int16), y_int.view(torch.int16))
+    rows = np.unique(np.array([0, M // 2, M - 1]))
+    o_packed, o_alpha, _ = oracle.ternarize(w)
+    y64 = oracle.forward(np.ascontiguousarray(x_np[rows]), o_packed, o_alpha, 4, hadamard=True)
+    check_output(bf16_to_f64(y[torch.from_numpy(rows).cuda()]), y64, f"k split M={M} N={N} K={K}")
+
+
+def test_forward_mx_k_split_strided_output(hbl):
+    M, N, K, pad = 77, 256, 8192, 24
+    x = to_device(workloads.random_rows(49, M, K, "t3"))
+    _, packed, alpha, wq = _weights(hbl, N, K, 9)
+    big = torch.full((M, N + pad), 3, dtype=torch.bfloat16, device="cuda")
+    hbl.forward_mx(x, wq, alpha, out=big[:, :N])
+    ref = hbl.forward(x, packed, alpha, 4)
+    assert torch.equal(big[:, :N].contiguous().view(torch.int16), ref.view(torch.int16))
+    assert torch.all(big[:, N:] == 3)
