@@ -72,8 +72,10 @@ def counter_traffic(workload, which):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 300 warm-up passes let the clocks settle (the first few hundred launches
+    # of a process run 3-5 % slower)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="wo_7b",
                     choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "msweep", "kvcache", "copy"])
     ap.add_argument("--copy-mib", type=int, default=1024,

@@ -318,6 +318,11 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 // smallest M K at which the int8 layer takes the split persistent matmul
 constexpr int64_t kSplitMinMK = int64_t(1) << 20;
 
+// the plan of k_gemm_pt
+SplitPlan pt_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
+  return split_plan(M, N, K, cu_count, may_split);
+}
+
 // int32 partial sums of a split plan's 256 x 128 items (0: no split)
 size_t pt_partial_bytes(const SplitPlan& p) {
   return p.ksplit > 1 ? (size_t)p.items() * 256 * 128 * sizeof(int32_t) : 0;
@@ -328,7 +333,7 @@ __global__ void __launch_bounds__(256, 1)
 k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
           const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
-          void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int ksplit,
+          void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int gm, int ksplit,
           int4* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
@@ -366,14 +371,14 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   // Items of this block: r P + slot for r = 0, 1, ... (P blocks, a multiple
   // of 8).  Consecutive block ids go to different XCDs; slot gives each XCD
   // a contiguous range of each round's items (split_item: a tile and one of
-  // ksplit K slices, tiles walked in M-groups of 8 so that an XCD's blocks
+  // ksplit K slices, tiles walked in M-groups of gm so that an XCD's blocks
   // share codes and weights in its L2).  With ksplit > 1 an item leaves its
   // int32 partial sums in part for k_pt_reduce.
   const int G = tilesM * tilesN * ksplit, P = gridDim.x, b = blockIdx.x;
   const int slot = (b % 8) * (P / 8) + b / 8;
   const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
   auto tile_of = [&](int r, int64_t& m0, int64_t& n0, int& ks) {
-    split_item<BM, BN>(r * P + slot, tilesM, tilesN, m0, n0, ks);
+    split_item<BM, BN>(r * P + slot, tilesM, tilesN, gm, m0, n0, ks);
   };
 
   auto aswz = [](int r, int u) { return u ^ ((r >> ASH) & (AU - 1)); };
@@ -914,7 +919,7 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
 // the order k_gemm_pt wrote them.
 template <int BITS, int OUT>
 __global__ void __launch_bounds__(256)
-k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, const float* __restrict__ scales,
+k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const int32_t* __restrict__ rowsum, const float* __restrict__ alpha, int64_t M, int64_t N,
             void* __restrict__ out, int64_t ldo) {
   constexpr int BM = 256, BN = 128, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
@@ -932,7 +937,7 @@ k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, c
   const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
   int64_t m0, n0;
   int ks;
-  split_item<BM, BN>(T, tilesM, tilesN, m0, n0, ks);
+  split_item<BM, BN>(T, tilesM, tilesN, gm, m0, n0, ks);
   const int64_t m = m0 + wm * WM + 32 * j + fr, n = n0 + wn * WN + 32 * i + 8 * q + 4 * h;
   if (m >= M || n >= N) return;
   int4 a = part[u];
@@ -953,20 +958,20 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
   // from M K >= 2^20 (measured at N = 4096: M >= 64 at K = 16384, M >= 256
   // at K = 4096); 16 tokens or fewer always stream
   const bool split_ok = part != nullptr && K % 512 == 0 && M > 16 && M * K >= kSplitMinMK &&
-                        part_bytes >= pt_partial_bytes(split_plan(M, N, K, cu_count, true));
+                        part_bytes >= pt_partial_bytes(pt_plan(M, N, K, cu_count, true));
   if (split_ok) {
-    const SplitPlan p = split_plan(M, N, K, cu_count, true);
+    const SplitPlan p = pt_plan(M, N, K, cu_count, true);
     if (p.ksplit > 1) {
       const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
       const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
       int4* pt = static_cast<int4*>(part);
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.ksplit, pt);
+                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t units = (int64_t)p.tm * p.tn * (256 * 128 / 4);
       hipLaunchKernelGGL((k_pt_reduce<BITS, OUT>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, pt,
-                         p.ksplit, p.tm, p.tn, scales, rowsum, alpha, M, N, out, ldo);
+                         p.ksplit, p.tm, p.tn, p.gm, scales, rowsum, alpha, M, N, out, ldo);
       return hipGetLastError();
     }
   }
@@ -1006,18 +1011,15 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
   }
   if (K % 512 == 0) {
     // persistent: one block per CU, 256 x 256 tiles when they fill the chip
-    const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
-    const int bn = g256 >= cu_count ? 256 : 128;
-    const int tm = (int)((M + 255) / 256), tn = (int)((N + bn - 1) / bn);
-    const int64_t G = (int64_t)tm * tn;
+    const SplitPlan p = pt_plan(M, N, K, cu_count, false);
     const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
-    const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
-    if (bn == 256) {
+    const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
+    if (p.bn == 256) {
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, tm, tn, 1, nullptr);
+                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     } else {
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, tm, tn, 1, nullptr);
+                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     }
     return hipGetLastError();
   }
@@ -1041,7 +1043,7 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 
 size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || N <= 0 || K % 512 != 0 || M * K < kSplitMinMK) return 0;
-  return pt_partial_bytes(split_plan(M, N, K, kSplitItems, true));
+  return pt_partial_bytes(pt_plan(M, N, K, kSplitItems, true));
 }
 
 hipError_t launch_ternary_gemm(const void* codes, int bits, const float* scales, const int32_t* rowsum,

@@ -99,7 +99,7 @@ template <int OUT, int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
 k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, const uint32_t* __restrict__ wq,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
-          int tilesM, int tilesN, int ksplit, int p16, void* __restrict__ part) {
+          int tilesM, int tilesN, int gm, int ksplit, int p16, void* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
@@ -145,7 +145,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   const int G = tilesM * tilesN * ksplit, P = gridDim.x, b = blockIdx.x;
   const int slot = (b % 8) * (P / 8) + b / 8;
   const int ntiles = slot < G ? (G - slot + P - 1) / P : 0;
-  auto tile_of = [&](int r, int64_t& m0, int64_t& n0, int& ks) { split_item<BM, BN>(r * P + slot, tilesM, tilesN, m0, n0, ks); };
+  auto tile_of = [&](int r, int64_t& m0, int64_t& n0, int& ks) { split_item<BM, BN>(r * P + slot, tilesM, tilesN, gm, m0, n0, ks); };
 
   auto mswz = [](int r, int u) { return u ^ ((r >> MSH) & (MU - 1)); };
   auto tswz = [](int r, int u) { return u ^ ((r >> TSH) & (TU - 1)); };
@@ -457,7 +457,7 @@ namespace {
 // the partials in the order k_gemm_mx wrote them.
 template <int OUT, int BN, bool P16>
 __global__ void __launch_bounds__(256)
-k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, const float* __restrict__ scales,
+k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const float* __restrict__ alpha, int64_t M, int64_t N, void* __restrict__ out, int64_t ldo) {
   constexpr int BM = 256, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int QU = P16 ? 2 : 4;                        // 16-byte units per fragment and lane
@@ -476,7 +476,7 @@ k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, c
   const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
   int64_t m0, n0;
   int ks;
-  split_item<BM, BN>(T, tilesM, tilesN, m0, n0, ks);
+  split_item<BM, BN>(T, tilesM, tilesN, gm, m0, n0, ks);
   const int64_t m = m0 + wm * WM + 32 * j + fr;
   const int64_t n = n0 + wn * WN + 32 * i + (P16 ? 16 : 8) * q + 4 * h;
   if (m >= M || n >= N) return;
@@ -537,10 +537,10 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
-  const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, p16 = p.p16 ? 1 : 0;
+  const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, gm = p.gm, p16 = p.p16 ? 1 : 0;
 #define HBL_MX(OUT, BN)                                                                                          \
   hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN>), dim3((unsigned)P), dim3(256), 0, s, c, scales, wq, alpha, M, N, K, \
-                     out, ldo, tm, tn, ksplit, p16, part)
+                     out, ldo, tm, tn, gm, ksplit, p16, part)
   if (p.bn == 256) {
     if (out_kind == 0) HBL_MX(0, 256); else if (out_kind == 1) HBL_MX(1, 256); else HBL_MX(2, 256);
   } else {
@@ -554,7 +554,7 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t units = (int64_t)tm * tn * 256 * 128 / (p16 ? 8 : 4);
   const unsigned rb = (unsigned)((units + 255) / 256);
 #define HBL_MXR(OUT, P16)                                                                                      \
-  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, scales, alpha, \
+  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, gm, scales, alpha, \
                      M, N, out, ldo)
   if (p16) {
     if (out_kind == 0) HBL_MXR(0, true); else if (out_kind == 1) HBL_MXR(1, true); else HBL_MXR(2, true);
