@@ -328,15 +328,18 @@ size_t pt_partial_bytes(const SplitPlan& p) {
   return p.ksplit > 1 ? (size_t)p.items() * 256 * 128 * sizeof(int32_t) : 0;
 }
 
-template <int BITS, int OUT, int BM, int BN>
-__global__ void __launch_bounds__(256, 1)
+template <int BITS, int OUT, int BM, int BN, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1)
 k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
           const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K,
           void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int gm, int ksplit,
           int4* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // NW waves as a (NW / 2) x 2 grid: 4 (one per SIMD), or 8 (two per SIMD)
+  // for 256 x 256 tiles
+  constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static_assert(NW == 4 || (NW == 8 && BN == 256), "8 waves only for 256 x 256 tiles");
   constexpr int BK = 128, NSTEP = BK / 32, NST = 4;  // NST stage buffers; also the unroll
   constexpr int AROW = BK * BITS / 8, BROW = BK / 4;  // bytes per row per stage
   constexpr int AU = AROW / 16, BU = BROW / 16;       // 16-byte units per row
@@ -363,7 +366,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % 2, wn = wave / 2;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int64_t arow_bytes = BITS == 4 ? K / 2 : K;  // global code row stride
   const int64_t brow_bytes = K / 4;                  // global weight row stride
   const int nks = (int)(K / BK) / ksplit;            // stages of one item (a multiple of NST)
@@ -965,8 +968,8 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
       const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
       int4* pt = static_cast<int4*>(part);
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, 4>), dim3((unsigned)P), dim3(256), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t units = (int64_t)p.tm * p.tn * (256 * 128 / 4);
@@ -1015,11 +1018,12 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
     const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
     const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
     if (p.bn == 256) {
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
+      // 256 x 256 tiles run 8 waves (two per SIMD), 256 x 128 tiles 4
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     } else {
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128>), dim3((unsigned)P), dim3(256), 0, s, codes, scales, rowsum,
-                         wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, 4>), dim3((unsigned)P), dim3(256), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     }
     return hipGetLastError();
   }

@@ -32,10 +32,11 @@
 //     2 r + (u ^ ((r >> 3) & 1)); tiles over the stages of a block, then the
 //     blocks; rows past N are zero.
 //
-// Kernel structure (k_gemm_mx): persistent, one block of 4 waves (2 x 2) per
-// CU, one wave per SIMD, block tile 256 tokens x BN features (BN = 256 when
-// the tiles fill the chip, else 128), wave tile 128 x BN/2 of 32x32x64
-// MFMAs with fp32 accumulators.  A stage is 128 codes (two MFMA steps);
+// Kernel structure (k_gemm_mx): persistent, one block per CU, block tile
+// 256 tokens x BN features (BN = 256 when the tiles fill the chip, else
+// 128).  256 x 256 tiles: 8 waves (4 x 2, two per SIMD) of 64 x 128 wave
+// tiles; 256 x 128 tiles: 4 waves (2 x 2, one per SIMD) of 128 x 64.  The
+// wave tiles are 32x32x64 MFMAs with fp32 accumulators.  A stage is 128 codes (two MFMA steps);
 // four stage buffers, each its own LDS variable, are refilled four stages
 // ahead by direct-to-LDS buffer loads; the stage sequence runs through the
 // block's tiles, so the last stages of a tile already load the next one.
@@ -95,13 +96,16 @@ __device__ __forceinline__ void store4f(void* out, int64_t idx, float a0, float 
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
-template <int OUT, int BM, int BN>
-__global__ void __launch_bounds__(256, 1)
+template <int OUT, int BM, int BN, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1)
 k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, const uint32_t* __restrict__ wq,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
           int tilesM, int tilesN, int gm, int ksplit, int p16, void* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 4, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // NW waves as a (NW / 2) x 2 grid: 4 waves (one per SIMD), or 8 (two per
+  // SIMD) for 256 x 256 tiles
+  constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static_assert(NW == 4 || (NW == 8 && BN == 256), "8 waves only for 256 x 256 tiles");
   constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
   constexpr int MROW = 64, TROW = 32, BROW = 32;    // bytes per row per stage: code mains, code tails, weights
   constexpr int MU = MROW / 16, TU = TROW / 16, BU = BROW / 16;
@@ -131,7 +135,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % 2, wn = wave / 2;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int64_t arow_bytes = K / 4 * 3;  // global code row stride (MX6)
   const int64_t brow_bytes = K / 4;      // global weight row stride (MX4)
   const int nk = (int)(K / BK);          // stages of the whole K
@@ -158,6 +162,8 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // 4 KB per 128-row block and stage.
   const uint32_t cl0 = 16u * (uint32_t)(64 * wave + lane);
   const uint32_t wblk = (uint32_t)(K / BK) * 4096u;  // bytes of one 128-row weight block
+  // weight unit 64 (w + NW j) + l lies in 128-row block (64 w + l) / 256 + j NW / 4
+  const uint32_t wb0 = (uint32_t)((64 * wave + lane) / 256) * wblk + 16u * (uint32_t)((64 * wave + lane) % 256);
   constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
 
   int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
@@ -184,16 +190,17 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     uint8_t* const Bd = bbuf(bi);
     const bool live = dr < ntiles;
     const uint32_t vm = live ? (uint32_t)dk * 24576u + cl0 : kOut;
-    const uint32_t vb = live ? (uint32_t)dk * 4096u + cl0 : kOut;
+    const uint32_t vb = live ? (uint32_t)dk * 4096u + wb0 : kOut;
 #pragma unroll
     for (int j = 0; j < MDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * 4096u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * (NW * 1024u), 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < TDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vm + 16384u + j * 4096u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vm + 16384u + j * (NW * 1024u), 0,
+                                               0, 0);
 #pragma unroll
     for (int j = 0; j < BDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * wblk, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * (NW / 4) * wblk, 0, 0, 0);
     if (++dk == nks) {
       dk = 0;
       set_tile(++dr);
@@ -538,9 +545,11 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, gm = p.gm, p16 = p.p16 ? 1 : 0;
-#define HBL_MX(OUT, BN)                                                                                          \
-  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN>), dim3((unsigned)P), dim3(256), 0, s, c, scales, wq, alpha, M, N, K, \
-                     out, ldo, tm, tn, gm, ksplit, p16, part)
+  // 256 x 256 tiles run 8 waves (two per SIMD: one wave's barrier and
+  // operand waits are covered by the other's MFMAs), 256 x 128 tiles 4
+#define HBL_MX(OUT, BN)                                                                                             \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN, BN / 32>), dim3((unsigned)P), dim3(2 * BN), 0, s, c, scales, wq, alpha, \
+                     M, N, K, out, ldo, tm, tn, gm, ksplit, p16, part)
   if (p.bn == 256) {
     if (out_kind == 0) HBL_MX(0, 256); else if (out_kind == 1) HBL_MX(1, 256); else HBL_MX(2, 256);
   } else {
