@@ -32,11 +32,12 @@
 //     2 r + (u ^ ((r >> 3) & 1)); tiles over the stages of a block, then the
 //     blocks; rows past N are zero.
 //
-// Kernel structure (k_gemm_mx): persistent, one block per CU, block tile
-// 256 tokens x BN features (BN = 256 when the tiles fill the chip, else
-// 128).  256 x 256 tiles: 8 waves (4 x 2, two per SIMD) of 64 x 128 wave
-// tiles; 256 x 128 tiles: 4 waves (2 x 2, one per SIMD) of 128 x 64.  The
-// wave tiles are 32x32x64 MFMAs with fp32 accumulators.  A stage is 128 codes (two MFMA steps);
+// Kernel structure (k_gemm_mx): persistent, one block of 8 waves (4 x 2, two
+// per SIMD) per CU, block tile 256 tokens x BN features (BN = 256 when the
+// tiles fill the chip, else 128), wave tile 64 x BN/2 of 32x32x64 MFMAs
+// with fp32 accumulators.  (The kernel also builds with 4 waves, one per
+// SIMD, 128 x BN/2 wave tiles: 5-20 % slower, since a wave's barrier and
+// operand waits then leave its matrix core idle.)  A stage is 128 codes (two MFMA steps);
 // four stage buffers, each its own LDS variable, are refilled four stages
 // ahead by direct-to-LDS buffer loads; the stage sequence runs through the
 // block's tiles, so the last stages of a tile already load the next one.
@@ -102,16 +103,20 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
           int tilesM, int tilesN, int gm, int ksplit, int p16, void* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // NW waves as a (NW / 2) x 2 grid: 4 waves (one per SIMD), or 8 (two per
-  // SIMD) for 256 x 256 tiles
+  // NW waves as a (NW / 2) x 2 grid: 4 waves (one per SIMD) or 8 (two per
+  // SIMD)
   constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  static_assert(NW == 4 || (NW == 8 && BN == 256), "8 waves only for 256 x 256 tiles");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
   constexpr int MROW = 64, TROW = 32, BROW = 32;    // bytes per row per stage: code mains, code tails, weights
   constexpr int MU = MROW / 16, TU = TROW / 16, BU = BROW / 16;
   constexpr int MSH = ilog2c(16 / MU), TSH = ilog2c(16 / TU), BSH = ilog2c(16 / BU);
-  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = BM * TROW / 1024 / NW, BDMA = BN * BROW / 1024 / NW;
-  static_assert(MDMA * NW * 1024 == BM * MROW && TDMA * NW * 1024 == BM * TROW && BDMA * NW * 1024 == BN * BROW,
+  // the weights of a 256 x 128 tile's stage (4 KB) are half a load per wave
+  // with 8 waves: each wave then loads 512 bytes with its lanes 0-31
+  constexpr bool BHALF = BN * BROW / 1024 == NW / 2;
+  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = BM * TROW / 1024 / NW, BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
+  static_assert(MDMA * NW * 1024 == BM * MROW && TDMA * NW * 1024 == BM * TROW &&
+                    (BHALF || BDMA * NW * 1024 == BN * BROW),
                 "staging must divide evenly");
   constexpr int DPS = MDMA + TDMA + BDMA;  // loads per wave per stage
   constexpr int MSZ = BM * MROW, TSZ = BM * TROW, BSZ = BN * BROW;
@@ -122,8 +127,8 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
   // bf16 outputs of 256 x 128 tiles are staged through LDS (whole-row stores)
   constexpr int OROW = (BN / 2) * 2 + 16;
-  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (MSZ + TSZ + BSZ) + 4 * 32 * OROW <= 160 * 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? 4 * 32 * OROW : 16];
+  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (MSZ + TSZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : 16];
   auto mbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return Am0; else if constexpr (I == 1) return Am1; else if constexpr (I == 2) return Am2; else return Am3;
   };
@@ -163,7 +168,9 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   const uint32_t cl0 = 16u * (uint32_t)(64 * wave + lane);
   const uint32_t wblk = (uint32_t)(K / BK) * 4096u;  // bytes of one 128-row weight block
   // weight unit 64 (w + NW j) + l lies in 128-row block (64 w + l) / 256 + j NW / 4
-  const uint32_t wb0 = (uint32_t)((64 * wave + lane) / 256) * wblk + 16u * (uint32_t)((64 * wave + lane) % 256);
+  // (half loads: unit 32 w + l of the one block, lanes l < 32)
+  const uint32_t wb0 = BHALF ? 16u * (uint32_t)(32 * wave + (lane & 31))
+                             : (uint32_t)((64 * wave + lane) / 256) * wblk + 16u * (uint32_t)((64 * wave + lane) % 256);
   constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
 
   int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
@@ -198,9 +205,14 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     for (int j = 0; j < TDMA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vm + 16384u + j * (NW * 1024u), 0,
                                                0, 0);
+    if constexpr (BHALF) {
+      if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 512 * wave, 16, vb, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < BDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * (NW / 4) * wblk, 0, 0, 0);
+      for (int j = 0; j < BDMA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * (NW / 4) * wblk, 0, 0,
+                                                 0);
+    }
     if (++dk == nks) {
       dk = 0;
       set_tile(++dr);
@@ -462,13 +474,13 @@ namespace {
 // gives the same value), then the rescale of Eq. 9.  One thread per four
 // (fp32 partials) or eight (int16) outputs of one lane's fragment, reading
 // the partials in the order k_gemm_mx wrote them.
-template <int OUT, int BN, bool P16>
+template <int OUT, int BN, bool P16, int NWV>
 __global__ void __launch_bounds__(256)
 k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const float* __restrict__ alpha, int64_t M, int64_t N, void* __restrict__ out, int64_t ldo) {
-  constexpr int BM = 256, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int QU = P16 ? 2 : 4;                        // 16-byte units per fragment and lane
-  const int64_t per_tile = (int64_t)4 * FN * FM * QU * 64;  // units of one tile
+  constexpr int NW = NWV, WGM = NW / 2, BM = 256, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int QU = P16 ? 2 : 4;                         // 16-byte units per fragment and lane
+  const int64_t per_tile = (int64_t)NW * FN * FM * QU * 64;  // units of one tile
   const int64_t units = (int64_t)tilesM * tilesN * per_tile;
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
@@ -478,9 +490,9 @@ k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, i
   t /= QU;
   const int ij = (int)(t % (FN * FM));
   t /= FN * FM;
-  const int wave = (int)(t % 4);
-  const int T = (int)(t / 4);
-  const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
+  const int wave = (int)(t % NW);
+  const int T = (int)(t / NW);
+  const int i = ij / FM, j = ij % FM, wm = wave % WGM, wn = wave / WGM, fr = lane % 32, h = lane / 32;
   int64_t m0, n0;
   int ks;
   split_item<BM, BN>(T, tilesM, tilesN, gm, m0, n0, ks);
@@ -512,6 +524,10 @@ k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, i
     store4f<OUT>(out, m * ldo + n, a.x, a.y, a.z, a.w, sc);
   }
 }
+
+// waves of the 256 x 128 tile kernel (8: 5 % faster than 4 at M = 2048,
+// N = K = 4096, 1-6 % on K-split shapes)
+constexpr int kMxWaves128 = 8;
 
 struct MxPlan : SplitPlan {
   bool p16;  // int16 partial sums
@@ -545,15 +561,17 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, gm = p.gm, p16 = p.p16 ? 1 : 0;
-  // 256 x 256 tiles run 8 waves (two per SIMD: one wave's barrier and
-  // operand waits are covered by the other's MFMAs), 256 x 128 tiles 4
-#define HBL_MX(OUT, BN)                                                                                             \
-  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN, BN / 32>), dim3((unsigned)P), dim3(2 * BN), 0, s, c, scales, wq, alpha, \
-                     M, N, K, out, ldo, tm, tn, gm, ksplit, p16, part)
+  // both tile widths run 8 waves (two per SIMD: one wave's barrier and
+  // operand waits are covered by the other's MFMAs)
+#define HBL_MX(OUT, BN, W)                                                                                       \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN, W>), dim3((unsigned)P), dim3(64 * W), 0, s, c, scales, wq, alpha, M, \
+                     N, K, out, ldo, tm, tn, gm, ksplit, p16, part)
   if (p.bn == 256) {
-    if (out_kind == 0) HBL_MX(0, 256); else if (out_kind == 1) HBL_MX(1, 256); else HBL_MX(2, 256);
+    if (out_kind == 0) HBL_MX(0, 256, 8); else if (out_kind == 1) HBL_MX(1, 256, 8); else HBL_MX(2, 256, 8);
+  } else if (kMxWaves128 == 8) {
+    if (out_kind == 0) HBL_MX(0, 128, 8); else if (out_kind == 1) HBL_MX(1, 128, 8); else HBL_MX(2, 128, 8);
   } else {
-    if (out_kind == 0) HBL_MX(0, 128); else if (out_kind == 1) HBL_MX(1, 128); else HBL_MX(2, 128);
+    if (out_kind == 0) HBL_MX(0, 128, 4); else if (out_kind == 1) HBL_MX(1, 128, 4); else HBL_MX(2, 128, 4);
   }
 #undef HBL_MX
   if (ksplit == 1) return hipGetLastError();
@@ -562,14 +580,17 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   // splits use 256 x 128 tiles only
   const int64_t units = (int64_t)tm * tn * 256 * 128 / (p16 ? 8 : 4);
   const unsigned rb = (unsigned)((units + 255) / 256);
-#define HBL_MXR(OUT, P16)                                                                                      \
-  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, gm, scales, alpha, \
-                     M, N, out, ldo)
+#define HBL_MXR(OUT, P16, W)                                                                                      \
+  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16, W>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, gm, scales, \
+                     alpha, M, N, out, ldo)
+#define HBL_MXR_W(OUT, P16) \
+  if (kMxWaves128 == 8) HBL_MXR(OUT, P16, 8); else HBL_MXR(OUT, P16, 4)
   if (p16) {
-    if (out_kind == 0) HBL_MXR(0, true); else if (out_kind == 1) HBL_MXR(1, true); else HBL_MXR(2, true);
+    if (out_kind == 0) { HBL_MXR_W(0, true); } else if (out_kind == 1) { HBL_MXR_W(1, true); } else { HBL_MXR_W(2, true); }
   } else {
-    if (out_kind == 0) HBL_MXR(0, false); else if (out_kind == 1) HBL_MXR(1, false); else HBL_MXR(2, false);
+    if (out_kind == 0) { HBL_MXR_W(0, false); } else if (out_kind == 1) { HBL_MXR_W(1, false); } else { HBL_MXR_W(2, false); }
   }
+#undef HBL_MXR_W
 #undef HBL_MXR
   return hipGetLastError();
 }
