@@ -44,24 +44,6 @@ constexpr float kSqrt7 = 2.6457513110645907f;
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Four INT4 codes (the bytes of w, two's complement, in [-8, 7]) as four
-// 6-bit E3M2 floats (1 sign, 3 exponent bits with bias 3, 2 mantissa bits:
-// 1 = 0b001100, 2 = 0b010000, 3 = 0b010010, ..., 7 = 0b010111,
-// 8 = 0b011000), code j at bits 6 j of the 24-bit result.  The low nibble of
-// a code byte indexes a 16-entry table held in four words: entries 0..7
-// (codes 0..7) and 8..15 (codes -8..-1) are picked by byte permutes and
-// merged by the index's bit 3.
-__device__ __forceinline__ uint32_t mx6_chunk(uint32_t w) {
-  const uint32_t idx = w & 0x0f0f0f0fu;
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, sel);  // 0, 12, 16, 18, 20, 21, 22, 23
-  const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, sel);  // 56, 55, 54, 53, 52, 50, 48, 44
-  const uint32_t hb = (idx >> 3) & 0x01010101u;
-  const uint32_t m = (hb << 8) - hb;  // 0xff in the bytes of negative codes
-  const uint32_t b = (pos & ~m) | (neg & m);
-  return (b & 0x3fu) | ((b >> 2) & (0x3fu << 6)) | ((b >> 4) & (0x3fu << 12)) | ((b >> 6) & (0x3fu << 18));
-}
-
 // Byte offsets of group g (32 codes) of token row m in the MX6 layout: the
 // codes of 256-row block B = m / 256 and stage s = g / 4 (128 codes) form one
 // 24 KB tile, a 16 KB main area (the first 16 bytes of each group: row r =
@@ -79,15 +61,6 @@ __device__ __forceinline__ int64_t mx6_tail_off(int64_t m, int g, int K) {
   const int64_t tile = (m >> 8) * (K / 128) + (g >> 2);
   const int r = (int)(m & 255), gi = g & 3;
   return tile * 24576 + 16384 + 16 * (2 * r + ((gi >> 1) ^ ((r >> 3) & 1))) + 8 * (gi & 1);
-}
-
-// The 192-bit field of 32 codes from its eight 24-bit chunks (chunk i at
-// bit 24 i), stored MX6-style: the first 16 bytes at main, the last 8 at
-// tail.
-__device__ __forceinline__ void mx6_store(const uint32_t (&c)[8], uint8_t* main, uint8_t* tail) {
-  *reinterpret_cast<uint4*>(main) =
-      make_uint4(c[0] | (c[1] << 24), (c[1] >> 8) | (c[2] << 16), (c[2] >> 16) | (c[3] << 8), c[4] | (c[5] << 24));
-  *reinterpret_cast<uint2*>(tail) = make_uint2((c[5] >> 8) | (c[6] << 16), (c[6] >> 16) | (c[7] << 8));
 }
 
 // Loads 8 consecutive elements starting at p (16-byte aligned) as fp32.
@@ -708,21 +681,53 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         return p01 | p23;
       };
       int qs[4] = {0, 0, 0, 0};  // four independent row-sum chains
+      // MX6 codes: the same rounding and clip, kept as fp32 integers
+      // (exact), then 32 codes at a time converted to E3M2 by the gfx950
+      // packed conversion (scale 1: exact for integers in [-8, 7]), whose
+      // 192-bit result holds element 2 i of its first operand at field 2 i and
+      // element i of its second at field 2 i + 1 (measured on the device)
+      auto qf = [&](float vv) {
+        const float r = __builtin_fmaf(vv, fc, kMagic);
+        return __builtin_amdgcn_fmed3f(r, kMagic + lo, kMagic + hi) - kMagic;
+      };
+      auto mx6_group = [&](const float* e, int g) {  // e: the group's 32 codes in order
+        v16f a, b;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          a[i] = e[2 * i];
+          b[i] = e[2 * i + 1];
+        }
+        const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
+        *reinterpret_cast<uint4*>(dst + mx6_main_off(m, g, K)) = make_uint4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<uint2*>(dst + mx6_tail_off(m, g, K)) = make_uint2(r[4], r[5]);
+      };
       if constexpr (!HAD && OUT == 2) {
         // the thread's 64 elements are contiguous: groups 2t and 2t + 1
-        uint32_t ch[2][8];
 #pragma unroll
-        for (int gi = 0; gi < 16; ++gi) {
-          const uint32_t w = quant4(v + 4 * gi);
-          qs[gi % 4] = __builtin_amdgcn_sdot4((int)w, 0x01010101, qs[gi % 4], false);
-          ch[gi / 8][gi % 8] = mx6_chunk(w);
-        }
+        for (int i = 0; i < 64; ++i) v[i] = qf(v[i]);
         if (live) {
-          uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
+          mx6_group(v, 2 * t);
+          mx6_group(v + 32, 2 * t + 1);
+        }
+      } else if constexpr (HAD && OUT == 2) {
+        // codes as fp32 to LDS in natural order, then each thread converts
+        // groups t and t + T (32 consecutive codes each)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * t + q;
-            mx6_store(ch[q], dst + mx6_main_off(m, g, K), dst + mx6_tail_off(m, g, K));
+        for (int gi = 0; gi < 16; ++gi)
+          *reinterpret_cast<float4*>(L + swz16(last_e(gi))) =
+              make_float4(qf(v[4 * gi]), qf(v[4 * gi + 1]), qf(v[4 * gi + 2]), qf(v[4 * gi + 3]));
+        __syncthreads();
+        if (live) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int g = t + T * qq;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float4 a = *reinterpret_cast<const float4*>(L + swz16(32 * g + 4 * u));
+              v[4 * u] = a.x; v[4 * u + 1] = a.y; v[4 * u + 2] = a.z; v[4 * u + 3] = a.w;
+            }
+            mx6_group(v, g);
           }
         }
       } else if constexpr (!HAD) {
@@ -753,9 +758,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           const uint32_t w = quant4(v + 4 * gi);
           qs[gi % 4] = __builtin_amdgcn_sdot4((int)w, 0x01010101, qs[gi % 4], false);
           const int e = last_e(gi);
-          if constexpr (OUT == 2) {
-            *reinterpret_cast<uint32_t*>(C8 + e) = mx6_chunk(w);  // one word per 4 codes, as for INT8
-          } else if constexpr (BITS == 8) {
+          if constexpr (BITS == 8) {
             *reinterpret_cast<uint32_t*>(C8 + e) = w;
           } else {
             *reinterpret_cast<uint32_t*>(C8 + e) = (w & 0x0f0f0f0fu) << (4 * ((e >> 2) & 1));
@@ -763,17 +766,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         }
         __syncthreads();
         if (live) {
-          if constexpr (OUT == 2) {
-            uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-              const int g = t + T * qq;  // group of 32 codes: 8 chunk words
-              const uint4 a = *reinterpret_cast<const uint4*>(C8 + 32 * g);
-              const uint4 b = *reinterpret_cast<const uint4*>(C8 + 32 * g + 16);
-              const uint32_t ch[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-              mx6_store(ch, dst + mx6_main_off(m, g, K), dst + mx6_tail_off(m, g, K));
-            }
-          } else if constexpr (BITS == 8) {
+          if constexpr (BITS == 8) {
             int8_t* dst = reinterpret_cast<int8_t*>(codes) + m * (int64_t)K;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
@@ -792,7 +785,8 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           }
         }
       }
-      const int qsum = row_reduce_int<T>((qs[0] + qs[1]) + (qs[2] + qs[3]), redi, row, t);
+      // (the FP6 x FP4 matmul needs no row sums)
+      const int qsum = OUT == 2 ? 0 : row_reduce_int<T>((qs[0] + qs[1]) + (qs[2] + qs[3]), redi, row, t);
       if (live && t == 0) {
         // the row index made opaque here, so that the store addresses are
         // formed now from the base pointers rather than kept (and spilled)
