@@ -315,6 +315,10 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 // into distinct banks.
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
+// waves of the 256 x 128 tile kernel (8: the layer 2-11 % faster than with
+// 4 at M = 2048, N = K = 4096 and on K-split shapes)
+constexpr int kPtWaves128 = 8;
+
 // smallest M K at which the int8 layer takes the split persistent matmul
 constexpr int64_t kSplitMinMK = int64_t(1) << 20;
 
@@ -336,17 +340,20 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
           void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int gm, int ksplit,
           int4* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // NW waves as a (NW / 2) x 2 grid: 4 (one per SIMD), or 8 (two per SIMD)
-  // for 256 x 256 tiles
+  // NW waves as a (NW / 2) x 2 grid: 4 (one per SIMD) or 8 (two per SIMD)
   constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  static_assert(NW == 4 || (NW == 8 && BN == 256), "8 waves only for 256 x 256 tiles");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int BK = 128, NSTEP = BK / 32, NST = 4;  // NST stage buffers; also the unroll
   constexpr int AROW = BK * BITS / 8, BROW = BK / 4;  // bytes per row per stage
   constexpr int AU = AROW / 16, BU = BROW / 16;       // 16-byte units per row
   constexpr int ASH = ilog2c(16 / AU), BSH = ilog2c(16 / BU);
   constexpr int NAU = AU / 2, NBU = BU / 2;           // units per lane half per fragment
-  constexpr int ADMA = BM * AROW / 1024 / NW, BDMA = BN * BROW / 1024 / NW;
-  static_assert(ADMA * NW * 1024 == BM * AROW && BDMA * NW * 1024 == BN * BROW, "staging must divide evenly");
+  // the weights of a 256 x 128 tile's stage (4 KB) are half a load per wave
+  // with 8 waves: each wave then loads 512 bytes with its lanes 0-31
+  constexpr bool BHALF = BN * BROW / 1024 == NW / 2;
+  constexpr int ADMA = BM * AROW / 1024 / NW, BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
+  static_assert(ADMA * NW * 1024 == BM * AROW && (BHALF || BDMA * NW * 1024 == BN * BROW),
+                "staging must divide evenly");
   static_assert(NBU == 1, "one weight unit per lane half");
   constexpr int DPS = ADMA + BDMA;  // loads per wave per stage
   constexpr int ASZ = BM * AROW, BSZ = BN * BROW;
@@ -356,8 +363,8 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   // besides the stages (INT4); the 256 x 256 tile stores fragments directly
   // (staging its 128-wide rows costs more registers than it saves)
   constexpr int OROW = (BN / 2) * 2 + 16;  // bytes per staged output row of a wave
-  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (ASZ + BSZ) + 4 * 32 * OROW <= 160 * 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? 4 * 32 * OROW : 16];
+  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (ASZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : 16];
   auto abuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return As0; else if constexpr (I == 1) return As1; else if constexpr (I == 2) return As2; else return As3;
   };
@@ -392,7 +399,8 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   // column offset per lane serves all loads.  Rows past the end of the
   // matrix lie beyond the buffer's range and read as zero.
   constexpr int AJR = 64 * NW / AU, BJR = 64 * NW / BU;  // rows between loads j and j + 1
-  const int ar0 = (64 * wave + lane) / AU, br0 = (64 * wave + lane) / BU;
+  // (half loads: unit 32 w + l of the weight stage, lanes l < 32)
+  const int ar0 = (64 * wave + lane) / AU, br0 = (BHALF ? 32 * wave + (lane & 31) : 64 * wave + lane) / BU;
   const uint32_t aoff0 = (uint32_t)ar0 * (uint32_t)arow_bytes + 16u * (uint32_t)aswz(ar0, lane % AU);
   const uint32_t boff0 = (uint32_t)br0 * (uint32_t)brow_bytes + 16u * (uint32_t)bswz(br0, lane % BU);
   const uint32_t astep = (uint32_t)AJR * (uint32_t)arow_bytes, bstep = (uint32_t)BJR * (uint32_t)brow_bytes;
@@ -427,9 +435,13 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
     for (int j = 0; j < ADMA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Ad + 1024 * (wave + NW * j), 16, va + j * astep, 0, 0, 0);
+    if constexpr (BHALF) {
+      if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 512 * wave, 16, vb, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < BDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+      for (int j = 0; j < BDMA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+    }
     if (++dk == nks) {
       dk = 0;
       set_tile(++dr);
@@ -920,12 +932,12 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
 // the epilogue of Eq. 9 (/ 16 for INT4, minus the row sum, rescale).  One
 // thread per four outputs of one lane's fragment, reading the partials in
 // the order k_gemm_pt wrote them.
-template <int BITS, int OUT>
+template <int BITS, int OUT, int NWV>
 __global__ void __launch_bounds__(256)
 k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const int32_t* __restrict__ rowsum, const float* __restrict__ alpha, int64_t M, int64_t N,
             void* __restrict__ out, int64_t ldo) {
-  constexpr int BM = 256, BN = 128, WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int NW = NWV, WGM = NW / 2, BM = 256, BN = 128, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   const int64_t units = (int64_t)tilesM * tilesN * (BM * BN / 4);
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
@@ -935,9 +947,9 @@ k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, i
   t /= 4;
   const int ij = (int)(t % (FN * FM));
   t /= FN * FM;
-  const int wave = (int)(t % 4);
-  const int T = (int)(t / 4);
-  const int i = ij / FM, j = ij % FM, wm = wave % 2, wn = wave / 2, fr = lane % 32, h = lane / 32;
+  const int wave = (int)(t % NW);
+  const int T = (int)(t / NW);
+  const int i = ij / FM, j = ij % FM, wm = wave % WGM, wn = wave / WGM, fr = lane % 32, h = lane / 32;
   int64_t m0, n0;
   int ks;
   split_item<BM, BN>(T, tilesM, tilesN, gm, m0, n0, ks);
@@ -968,12 +980,12 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
       const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
       int4* pt = static_cast<int4*>(part);
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, 4>), dim3((unsigned)P), dim3(256), 0, s, codes, scales,
-                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, kPtWaves128>), dim3((unsigned)P), dim3(64 * kPtWaves128), 0,
+                         s, codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t units = (int64_t)p.tm * p.tn * (256 * 128 / 4);
-      hipLaunchKernelGGL((k_pt_reduce<BITS, OUT>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, pt,
+      hipLaunchKernelGGL((k_pt_reduce<BITS, OUT, kPtWaves128>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, pt,
                          p.ksplit, p.tm, p.tn, p.gm, scales, rowsum, alpha, M, N, out, ldo);
       return hipGetLastError();
     }
@@ -1018,12 +1030,12 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
     const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
     const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
     if (p.bn == 256) {
-      // 256 x 256 tiles run 8 waves (two per SIMD), 256 x 128 tiles 4
+      // 256 x 256 tiles run 8 waves (two per SIMD)
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
                          rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     } else {
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, 4>), dim3((unsigned)P), dim3(256), 0, s, codes, scales,
-                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, kPtWaves128>), dim3((unsigned)P), dim3(64 * kPtWaves128), 0,
+                         s, codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     }
     return hipGetLastError();
   }
