@@ -28,10 +28,11 @@ int ternarize_partials(int64_t N, int64_t K);
 // 256 x 256 tiles when they alone fill the chip (cu_count of them), else
 // 256 x 128; below kSplitItems tiles the K range (nk stages of 128) is
 // halved while the items (tile, K slice) fit kSplitItems and each keeps at
-// least 16 stages, and once more (to 8 stages) while they fit half of them.
-// Measured on MI355X at N = 4096 (FP6 x FP4 path, every split
-// bit-identical): K = 4096, M <= 256 best at 4 slices; K = 16384, M <= 256
-// at 8, M = 512 at 4, M = 1024 at 2; from 256 tiles on, none.
+// least 16 stages (32 when the tiles alone already fill half the chip), and
+// once more (to 8 stages) while they fit half of them.  Measured on MI355X
+// at N = 4096 (both layers, every split bit-identical): K = 4096, M <= 256
+// best at 4 slices, M = 1024 unsplit; K = 16384, M <= 256 at 8, M = 512 at
+// 4, M = 1024 at 2; from 256 tiles on, none.
 struct SplitPlan {
   int bn, tm, tn, ksplit;
   // M-group of the item walk (split_item): an XCD's 32 consecutive items
@@ -54,7 +55,7 @@ inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool 
   auto ok = [&](int S, int64_t items, int64_t min_stages) {
     return may_split && p.bn == 128 && G * S <= items && (nk / 4) % S == 0 && nk / S >= min_stages;
   };
-  while (ok(p.ksplit * 2, kSplitItems, 16)) p.ksplit *= 2;
+  while (ok(p.ksplit * 2, kSplitItems, G >= kSplitItems / 2 ? 32 : 16)) p.ksplit *= 2;
   if (ok(p.ksplit * 2, kSplitItems / 2, 8)) p.ksplit *= 2;
   return p;
 }

@@ -141,10 +141,10 @@ def test_gemm_mx_full_tile_grid_exact(hbl):
 
 
 # (M, N, K) -> slices: (1, 4096, 16384) 8, (100, 272, 4096) 4, (256, 4096,
-# 16384) 8, (300, 528, 8192) 8, (1024, 4096, 4096) 2 (int16 partial sums);
+# 16384) 8, (300, 528, 8192) 8, (768, 4096, 4096) 2 (int16 partial sums);
 # (200, 4224, 16384) 4 (slices of 4096: fp32 partial sums)
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 16384), (100, 272, 4096), (256, 4096, 16384), (300, 528, 8192),
-                                   (1024, 4096, 4096), (200, 4224, 16384)])
+                                   (768, 4096, 4096), (200, 4224, 16384)])
 def test_forward_mx_k_split(hbl, M, N, K):
     # fewer than 256 tiles: the layer splits K over the workspace's partial
     # sums; exact integer partials give the unsplit matmul's bits

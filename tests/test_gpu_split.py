@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 # (M, N, K) -> slices of the 256 x 128 tiles: (64, 4096, 16384) 8,
 # (100, 272, 16384) 16, (256, 4096, 4096) 4, (200, 4224, 16384) 4 (a ragged
-# last tile column), (1024, 4096, 4096) 2
-SHAPES = [(64, 4096, 16384), (100, 272, 16384), (256, 4096, 4096), (200, 4224, 16384), (1024, 4096, 4096)]
+# last tile column), (768, 4096, 4096) 2
+SHAPES = [(64, 4096, 16384), (100, 272, 16384), (256, 4096, 4096), (200, 4224, 16384), (768, 4096, 4096)]
 
 
 def _split_active(hbl, M, N, K, bits):
