@@ -33,7 +33,7 @@ MAX_K = 16384
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built; run `python bit_quantization_amd/build.py` "
-        "(or __graft_entry__.build()) first")
+        "first")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
