@@ -18,8 +18,9 @@
 // bos_scales [B][H].
 //
 // One lane per 32 consecutive elements, D / 32 consecutive lanes per head
-// (D a power of two, 32 .. 2048); the head's maximum is reduced across its
-// lanes with xor shuffles.  Memory-bound: 2 (bf16) or 4 (fp32) bytes read
+// (D a power of two, 32 .. 2048), a grid of up to 128 blocks per CU that
+// strides over larger inputs; the head's maximum is reduced across its lanes
+// with xor shuffles.  Memory-bound: 2 (bf16) or 4 (fp32) bytes read
 // and b / 8 written per element.
 #include "hbl_internal.h"
 
@@ -162,7 +163,10 @@ hipError_t launch_kv_l(const void* x, int64_t groups, int64_t S, int64_t H, int 
   const int L = D / 32;
   const int64_t lanes = groups * L;
   const int64_t want = (lanes + 255) / 256;
-  const int64_t cap = 16 * (int64_t)(cu > 0 ? cu : 256);
+  // up to 128 blocks per CU: at one 7B layer's K states (2^23 lanes) every
+  // lane then quantises one group (122 us), against 135 us when 16 blocks
+  // per CU stride over the groups
+  const int64_t cap = 128 * (int64_t)(cu > 0 ? cu : 256);
   const unsigned blocks = (unsigned)(want < cap ? want : cap);
 #define HBL_KV(LL)                                                                                               \
   case LL:                                                                                                       \
