@@ -413,11 +413,11 @@ k_fwht_quant(const void* __restrict__ x, int64_t M, int64_t ldx,
 // go back through LDS in natural order, and each thread stores contiguous
 // 16-byte units.  The next row group's input is loaded while the current
 // one is transformed.
-template <int LOG2K>
+template <int LOG2K, int BS = 256>
 struct G64 {
   static constexpr int K = 1 << LOG2K;
   static constexpr int T = K / 64;             // threads per row
-  static constexpr int RPB = 256 / T;          // rows per block
+  static constexpr int RPB = BS / T;           // rows per block (BS threads)
   static constexpr int A3 = LOG2K - 10;        // active bits of pass 3
   static constexpr int EX = 4 - A3;            // low bits of 2-5 kept in registers in pass 3
 };
@@ -440,13 +440,13 @@ __device__ __forceinline__ int swz16(int e) {  // float index -> swizzled float 
 // MX6 operands of the FP6 x FP4 matmul (BITS 4): groups of 32 codes as
 // 192-bit fields (code e at bit 6 e), placed in 24 KB tiles of 256 rows x 128
 // codes (mx6_main_off, mx6_tail_off).
-template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
-__global__ void __launch_bounds__(256, 2)
+template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM, int BS>
+__global__ void __launch_bounds__(BS, 2)
 k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
                void* __restrict__ codes, float* __restrict__ scales,
                int32_t* __restrict__ rowsum, float* __restrict__ yout,
                const float* __restrict__ gain) {
-  using G = G64<LOG2K>;
+  using G = G64<LOG2K, BS>;
   constexpr int K = G::K, T = G::T, RPB = G::RPB, A3 = G::A3, EX = G::EX;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int NL = BF16 ? 8 : 16;  // 16-byte loads per thread
@@ -884,14 +884,23 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
   }
 }
 
+// Block size: rows of K <= 4096 (a wave or less per row) run in blocks of
+// 64 threads (codes; up to 8 blocks per CU) or 128 (MX6 codes; up to 4 per
+// CU), which need no barrier across rows; measured at K = 4096 against 256
+// threads and 2 blocks per CU: codes 7-15 % faster at M = 1 ... 65536, MX6
+// codes 2-11 %.  Longer rows, and the fp32 output, keep 256 threads.
 template <int LOG2K, bool BF16, int BITS, bool HAD, int OUT, bool NORM>
 hipError_t launch_fq64(const void* x, int64_t M, int64_t ldx, void* codes, float* scales, int32_t* rowsum,
                        float* y, const float* gain, int cu_count, hipStream_t s) {
-  using G = G64<LOG2K>;
+  constexpr int BS = (LOG2K <= 12 && OUT != 1) ? (OUT == 2 ? 128 : 64) : 256;
+  using G = G64<LOG2K, BS>;
+  // persistent: as many blocks per CU as 128 KB of row buffers hold (two of
+  // 256 threads)
+  constexpr int PER_CU = BS == 256 ? 2 : 128 * 1024 / (4 * G::RPB * G::K);
   const int64_t groups = (M + G::RPB - 1) / G::RPB;
-  const int64_t cap = 2 * (int64_t)(cu_count > 0 ? cu_count : 256);  // two blocks fit per CU
+  const int64_t cap = (int64_t)PER_CU * (cu_count > 0 ? cu_count : 256);
   const int64_t blocks = groups < cap ? groups : cap;
-  hipLaunchKernelGGL((k_fwht_quant64<LOG2K, BF16, BITS, HAD, OUT, NORM>), dim3((unsigned)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_fwht_quant64<LOG2K, BF16, BITS, HAD, OUT, NORM, BS>), dim3((unsigned)blocks), dim3(BS), 0, s,
                      x, M, ldx, codes, scales, rowsum, y, gain);
   return hipGetLastError();
 }
