@@ -32,10 +32,11 @@
 //     2 r + (u ^ ((r >> 3) & 1)); tiles over the stages of a block, then the
 //     blocks; rows past N are zero.
 //
-// Kernel structure (k_gemm_mx): persistent, one block of 8 waves (4 x 2, two
-// per SIMD) per CU, block tile 256 tokens x BN features (BN = 256 when the
-// tiles fill the chip, else 128), wave tile 64 x BN/2 of 32x32x64 MFMAs
-// with fp32 accumulators.  (The kernel also builds with 4 waves, one per
+// Kernel structure (k_gemm_mx): persistent, one block of 8 waves (two per
+// SIMD) per CU, block tile 256 x 256 (4 x 2 waves) when those tiles fill the
+// chip, else 128 tokens x 256 features (2 x 4 waves), or 256 x 128 (4 x 2)
+// for the items of a K split; wave tile 64 x 128 or 64 x 64 of 32x32x64
+// MFMAs with fp32 accumulators.  (The kernel also builds with 4 waves, one per
 // SIMD, 128 x BN/2 wave tiles: 5-20 % slower, since a wave's barrier and
 // operand waits then leave its matrix core idle.)  A stage is 128 codes (two MFMA steps);
 // four stage buffers, each its own LDS variable, are refilled four stages
@@ -103,31 +104,37 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
           int tilesM, int tilesN, int gm, int ksplit, int p16, void* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // NW waves as a (NW / 2) x 2 grid: 4 waves (one per SIMD) or 8 (two per
-  // SIMD)
-  constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // NW waves as a (NW / 2) x 2 grid of 256-row tiles (4 waves, one per
+  // SIMD, or 8, two per SIMD), or 2 x 4 for 128 x 256 tiles: 64 x 64 wave
+  // tiles with 8 waves
+  constexpr int NW = NWV, WGM = BM == 128 ? 2 : NW / 2, WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int BK = 128, NST = 4;                  // codes per stage; stage buffers (also the unroll)
   constexpr int MROW = 64, TROW = 32, BROW = 32;    // bytes per row per stage: code mains, code tails, weights
   constexpr int MU = MROW / 16, TU = TROW / 16, BU = BROW / 16;
   constexpr int MSH = ilog2c(16 / MU), TSH = ilog2c(16 / TU), BSH = ilog2c(16 / BU);
-  // the weights of a 256 x 128 tile's stage (4 KB) are half a load per wave
-  // with 8 waves: each wave then loads 512 bytes with its lanes 0-31
+  // the weights of a 256 x 128 tile's stage (4 KB), and the code tails of a
+  // 128 x 256 tile's (4 KB), are half a load per wave with 8 waves: each
+  // wave then loads 512 bytes with its lanes 0-31
   constexpr bool BHALF = BN * BROW / 1024 == NW / 2;
-  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = BM * TROW / 1024 / NW, BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
-  static_assert(MDMA * NW * 1024 == BM * MROW && TDMA * NW * 1024 == BM * TROW &&
+  constexpr bool THALF = BM * TROW / 1024 == NW / 2;
+  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = THALF ? 1 : BM * TROW / 1024 / NW,
+                BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
+  static_assert(MDMA * NW * 1024 == BM * MROW && (THALF || TDMA * NW * 1024 == BM * TROW) &&
                     (BHALF || BDMA * NW * 1024 == BN * BROW),
                 "staging must divide evenly");
   constexpr int DPS = MDMA + TDMA + BDMA;  // loads per wave per stage
   constexpr int MSZ = BM * MROW, TSZ = BM * TROW, BSZ = BN * BROW;
-  static_assert(BM == 256 && MSZ == 16384 && TSZ == 8192 && BN % 128 == 0,
-                "the MX6 tile is 256 rows x 128 codes, the MX4 tile 128 rows x 128 weights");
+  static_assert((BM == 256 || (BM == 128 && BN == 256 && NW == 8)) && BN % 128 == 0,
+                "the MX6 tile is 256 rows x 128 codes (a block takes all of it or one half), the MX4 tile "
+                "128 rows x 128 weights");
   __shared__ __attribute__((aligned(1024))) uint8_t Am0[MSZ], Am1[MSZ], Am2[MSZ], Am3[MSZ];
   __shared__ __attribute__((aligned(1024))) uint8_t At0[TSZ], At1[TSZ], At2[TSZ], At3[TSZ];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
   // bf16 outputs of 256 x 128 tiles are staged through LDS (whole-row stores)
-  constexpr int OROW = (BN / 2) * 2 + 16;
-  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (MSZ + TSZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
+  constexpr int OROW = WN * 2 + 16;
+  constexpr bool STAGE_OUT = OUT == 0 && WN == 64 && NST * (MSZ + TSZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : 16];
   auto mbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return Am0; else if constexpr (I == 1) return Am1; else if constexpr (I == 2) return Am2; else return Am3;
@@ -163,9 +170,12 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // 16-byte units, XOR-swizzled by row), so lane l of load j of wave w copies
   // the 16 contiguous bytes of physical unit 64 (w + NW j) + l: every load
   // instruction moves 1 KB of consecutive addresses.  Codes: 24 KB per
-  // 256-row block and stage (16 KB main area, then 8 KB tail area); weights:
-  // 4 KB per 128-row block and stage.
+  // 256-row block and stage (16 KB main area, then 8 KB tail area); a
+  // 128-row half takes the half of each area that holds its rows (the
+  // swizzles depend on r % 16 only, so each half is itself the image of its
+  // rows); weights: 4 KB per 128-row block and stage.
   const uint32_t cl0 = 16u * (uint32_t)(64 * wave + lane);
+  const uint32_t tl0 = THALF ? 16u * (uint32_t)(32 * wave + (lane & 31)) : cl0;
   const uint32_t wblk = (uint32_t)(K / BK) * 4096u;  // bytes of one 128-row weight block
   // weight unit 64 (w + NW j) + l lies in 128-row block (64 w + l) / 256 + j NW / 4
   // (half loads: unit 32 w + l of the one block, lanes l < 32)
@@ -174,6 +184,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
 
   int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
+  uint32_t amo = 0, ato = 16384;  // offsets of the tile's main and tail areas in a stage image
   __amdgpu_buffer_rsrc_t rA, rB;
   auto set_tile = [&](int r) {
     int64_t m0 = 0, n0 = 0;
@@ -185,8 +196,12 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     const int64_t wrows = (N + 127) / 128 * 128;
     const int brows = r < ntiles ? (int)min<int64_t>(BN, wrows - n0) : 0;
     const int64_t ka = (int64_t)ks * nks * 24576, kb = (int64_t)ks * nks * 4096;
-    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + m0 * arow_bytes + ka), (short)0,
-                                           r < ntiles ? (int)(BM * arow_bytes - ka) : 0, 0x00020000);
+    const int64_t mb = m0 & ~(int64_t)255;  // the 256-row block holding the tile
+    const uint32_t half = (uint32_t)((m0 >> 7) & 1);
+    amo = half * 8192u;
+    ato = 16384u + half * 4096u;
+    rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + mb * arow_bytes + ka), (short)0,
+                                           r < ntiles ? (int)(256 * arow_bytes - ka) : 0, 0x00020000);
     rB = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes + kb), (short)0,
         r < ntiles ? (int)(brows * brow_bytes - kb) : 0, 0x00020000);
@@ -196,15 +211,20 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     uint8_t* const Td = tbuf(bi);
     uint8_t* const Bd = bbuf(bi);
     const bool live = dr < ntiles;
-    const uint32_t vm = live ? (uint32_t)dk * 24576u + cl0 : kOut;
+    const uint32_t vm = live ? (uint32_t)dk * 24576u + amo + cl0 : kOut;
+    const uint32_t vt = live ? (uint32_t)dk * 24576u + ato + tl0 : kOut;
     const uint32_t vb = live ? (uint32_t)dk * 4096u + wb0 : kOut;
 #pragma unroll
     for (int j = 0; j < MDMA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * (NW * 1024u), 0, 0, 0);
+    if constexpr (THALF) {
+      if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 512 * wave, 16, vt, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < TDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vm + 16384u + j * (NW * 1024u), 0,
-                                               0, 0);
+      for (int j = 0; j < TDMA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vt + j * (NW * 1024u), 0, 0,
+                                                 0);
+    }
     if constexpr (BHALF) {
       if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 512 * wave, 16, vb, 0, 0, 0);
     } else {
@@ -288,7 +308,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     asm volatile("" : "+s"(r));
     int fr = lane % 32, h = lane / 32;
     asm volatile("" : "+v"(fr), "+v"(h));
-    if (BN == 128 && ksplit > 1) {
+    if (BM == 256 && BN == 128 && ksplit > 1) {
       // exact partial sums, in fragment order: each store is 1 KB contiguous
       // (splits use 256 x 128 tiles only)
       const int64_t item = r * P + slot;
@@ -561,12 +581,25 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, gm = p.gm, p16 = p.p16 ? 1 : 0;
-  // both tile widths run 8 waves (two per SIMD: one wave's barrier and
+  // every tile shape runs 8 waves (two per SIMD: one wave's barrier and
   // operand waits are covered by the other's MFMAs)
-#define HBL_MX(OUT, BN, W)                                                                                       \
-  hipLaunchKernelGGL((k_gemm_mx<OUT, 256, BN, W>), dim3((unsigned)P), dim3(64 * W), 0, s, c, scales, wq, alpha, M, \
-                     N, K, out, ldo, tm, tn, gm, ksplit, p16, part)
-  if (p.bn == 256) {
+#define HBL_MXT(OUT, BM, BN, W, TM, TN, GM)                                                                      \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, BM, BN, W>), dim3((unsigned)P), dim3(64 * W), 0, s, c, scales, wq, alpha, M,  \
+                     N, K, out, ldo, TM, TN, GM, ksplit, p16, part)
+#define HBL_MX(OUT, BN, W) HBL_MXT(OUT, 256, BN, W, tm, tn, gm)
+  if (p.bn == 128 && ksplit == 1) {
+    // unsplit narrow tiles as 128 x 256: the same outputs per tile from 20
+    // instead of 28 KB of operands per stage (6-bit codes cost more bytes
+    // per row than 2-bit weights).  Measured on MI355X against 256 x 128
+    // (bit-identical): layer at M = 2048, N = K = 4096 35.1 -> 32.9 us,
+    // M = 1024 28.8 -> 27.2, M = 3072 55.1 -> 53.4; M = 2048, K = 16384
+    // 102 -> 99.
+    const int tm2 = (int)((M + 127) / 128), tn2 = (int)((N + 255) / 256);
+    const int64_t P = std::min<int64_t>(((int64_t)tm2 * tn2 + 7) / 8 * 8, cap);
+    if (out_kind == 0) HBL_MXT(0, 128, 256, 8, tm2, tn2, gm);
+    else if (out_kind == 1) HBL_MXT(1, 128, 256, 8, tm2, tn2, gm);
+    else HBL_MXT(2, 128, 256, 8, tm2, tn2, gm);
+  } else if (p.bn == 256) {
     if (out_kind == 0) HBL_MX(0, 256, 8); else if (out_kind == 1) HBL_MX(1, 256, 8); else HBL_MX(2, 256, 8);
   } else if (kMxWaves128 == 8) {
     if (out_kind == 0) HBL_MX(0, 128, 8); else if (out_kind == 1) HBL_MX(1, 128, 8); else HBL_MX(2, 128, 8);
@@ -574,6 +607,7 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
     if (out_kind == 0) HBL_MX(0, 128, 4); else if (out_kind == 1) HBL_MX(1, 128, 4); else HBL_MX(2, 128, 4);
   }
 #undef HBL_MX
+#undef HBL_MXT
   if (ksplit == 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

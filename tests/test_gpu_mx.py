@@ -50,7 +50,10 @@ def test_quant_mx_codes(hbl, log2k, had, dtype):
     check_scales(sm.cpu().numpy(), os_, "mx scales")
 
 
-@pytest.mark.parametrize("M", [1, 5, 100, 256, 300])
+# (unsplit: 128 x 256 tiles, whose rows are one half of a 256-row MX6 block;
+# M = 129 and 383 end in the second half of a block and the first half of the
+# next one, N = 16 and 272 leave part of a 256-column tile empty)
+@pytest.mark.parametrize("M", [1, 5, 100, 129, 256, 300, 383])
 @pytest.mark.parametrize("N,K", [(16, 512), (48, 1024), (272, 2048)])
 def test_gemm_mx_exact_on_oracle_codes(hbl, M, N, K):
     x = workloads.random_rows(M + N + K, M, K, "t3", as_bf16=True)
