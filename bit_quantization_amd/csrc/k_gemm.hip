@@ -340,9 +340,12 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
           void* __restrict__ out, int64_t ldo, int tilesM, int tilesN, int gm, int ksplit,
           int4* __restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // NW waves as a (NW / 2) x 2 grid: 4 (one per SIMD) or 8 (two per SIMD)
-  constexpr int NW = NWV, WGM = NW / 2, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // NW waves as a (NW / 2) x 2 grid of 256-row tiles, 4 (one per SIMD) or
+  // 8 (two per SIMD), or 2 x 4 for 128 x 256 tiles (64 x 64 wave tiles)
+  constexpr int NW = NWV, WGM = BM == 128 ? 2 : NW / 2, WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(BM == 256 || (BM == 128 && BN == 256 && NW == 8), "tile shapes 256 x BN and 128 x 256");
   constexpr int BK = 128, NSTEP = BK / 32, NST = 4;  // NST stage buffers; also the unroll
   constexpr int AROW = BK * BITS / 8, BROW = BK / 4;  // bytes per row per stage
   constexpr int AU = AROW / 16, BU = BROW / 16;       // 16-byte units per row
@@ -359,11 +362,11 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   constexpr int ASZ = BM * AROW, BSZ = BN * BROW;
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASZ], As1[ASZ], As2[ASZ], As3[ASZ];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BSZ], Bs1[BSZ], Bs2[BSZ], Bs3[BSZ];
-  // bf16 outputs of 256 x 128 tiles are staged through LDS when it has room
-  // besides the stages (INT4); the 256 x 256 tile stores fragments directly
+  // bf16 outputs of 64 x 64 wave tiles are staged through LDS when it has
+  // room besides the stages; the 256 x 256 tile stores fragments directly
   // (staging its 128-wide rows costs more registers than it saves)
-  constexpr int OROW = (BN / 2) * 2 + 16;  // bytes per staged output row of a wave
-  constexpr bool STAGE_OUT = OUT == 0 && BN == 128 && NST * (ASZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
+  constexpr int OROW = WN * 2 + 16;  // bytes per staged output row of a wave
+  constexpr bool STAGE_OUT = OUT == 0 && WN == 64 && NST * (ASZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : 16];
   auto abuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return As0; else if constexpr (I == 1) return As1; else if constexpr (I == 2) return As2; else return As3;
@@ -538,7 +541,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     // r made opaque here: nothing of the epilogue is computed early and kept
     // live through the stage loop
     asm volatile("" : "+s"(r));
-    if (BN == 128 && ksplit > 1) {
+    if (BM == 256 && BN == 128 && ksplit > 1) {
       // raw int32 partial sums in fragment order: each store is 1 KB
       // contiguous (splits use 256 x 128 tiles only)
       int4* dst = part + ((int64_t)(r * P + slot) * NW + wave) * (FN * FM * 4 * 64) + lane;
@@ -1034,8 +1037,13 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
                          rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     } else {
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, kPtWaves128>), dim3((unsigned)P), dim3(64 * kPtWaves128), 0,
-                         s, codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
+      // narrower tiles as 128 x 256 (the 256 x 128 shape is kept for the
+      // items of a K split): the same outputs per tile from 24 instead of 36
+      // KB (INT8 codes) or 16 instead of 20 KB (INT4) of operands per stage
+      const int tm2 = (int)((M + 127) / 128), tn2 = (int)((N + 255) / 256);
+      const int64_t P2 = std::min<int64_t>(((int64_t)tm2 * tn2 + 7) / 8 * 8, cap);
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 128, 256, 8>), dim3((unsigned)P2), dim3(512), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, tm2, tn2, p.gm, 1, nullptr);
     }
     return hipGetLastError();
   }
