@@ -784,7 +784,8 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
 }
 
 // ---------------------------------------------------------------------------
-// Decode with very few tokens (M <= 4), K % 1024 == 0: dot-product kernel.
+// Decode with very few tokens (M <= 2, or M <= 4 at K >= 16384), K % 1024 == 0:
+// dot-product kernel.
 // A block of 512 threads owns NB output features.  Thread t covers the 64
 // codes k = 64*(t % TK) .. +63 (TK = min(256, K/64) threads per feature row)
 // of RPT = NB / (512 / TK) of those features; it loads the tokens' codes for
@@ -993,7 +994,12 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       return hipGetLastError();
     }
   }
-  if (M <= 4 && K % 1024 == 0) {
+  // the dot-product kernel for 1-2 tokens, and up to 4 from K = 16384; its
+  // per-token code loads grow with M, and at K = 4096 the matrix-core GEMV
+  // is faster from 3 tokens on (measured at N = 4096, 10 or more matrices
+  // cycled: M = 4 INT8 6.3 against 4.1 us, INT4 4.6 against 4.1; M = 2
+  // INT4 3.7 against 4.0; at K = 16384, M = 4 10.1 against 10.4)
+  if ((M <= 2 || (M <= 4 && K >= 16384)) && K % 1024 == 0) {
     const int64_t tk = K / 64 < 256 ? K / 64 : 256;
 #define HBL_DOT(MT, TK)                                                                                      \
   if (N % DotGeom<BITS, OUT, MT, TK>::NB == 0) {                                                           \
