@@ -701,6 +701,11 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   const int64_t KW = K / 16;
   const int64_t steps = (KW + 15) / 16;  // a step is 16 words (256 k) per row
   const uint32_t* wrow = wp + (n0 + fr) * KW;
+  // every block reads every token's codes: each starts its walk over K at
+  // its own step, so that the blocks do not all read the same code lines of
+  // the L2 at once (the integer sums do not depend on the order; measured at
+  // N = 4096, K = 16384: M = 16 13.4 -> 12.9 us, M = 8 10.7 -> 10.2)
+  const int64_t rot = ((int64_t)blockIdx.x * 13) % steps;
 
   v4i acc[MG];
 #pragma unroll
@@ -709,13 +714,14 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
     uint4 w[kGemvBatch];
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
-      const int64_t kw = (s0 + 4 * b) * 16 + 4 * g;
-      w[b] = (s0 + 4 * b < steps && kw < KW) ? load_stream(wrow + kw)
-                                             : make_uint4(0, 0, 0, 0);
+      const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+      const int64_t kw = ps * 16 + 4 * g;
+      w[b] = (st < steps && kw < KW) ? load_stream(wrow + kw) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
-      const int64_t kw = (s0 + 4 * b) * 16 + 4 * g;
+      const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+      const int64_t kw = ps * 16 + 4 * g;
       // Skip only whole steps (a wave-uniform test): an MFMA always runs on
       // all 64 lanes, so lanes past the end of K feed zeros instead.
       if (s0 + 4 * b >= steps) continue;
