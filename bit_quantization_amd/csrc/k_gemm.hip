@@ -24,6 +24,8 @@
 // output features of one token: one 8-byte bf16 store.
 #include "hbl_internal.h"
 
+#include <climits>
+
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -695,6 +697,15 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
        const float* __restrict__ alpha, int M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo) {
   __shared__ v4i red[MG][3][64];
+  // One group of INT8 tokens: each step's codes (16 tokens x 256 bytes) are
+  // copied into the wave's LDS area by direct-to-LDS loads in which 16
+  // consecutive lanes read one token's 256 bytes, then read back as MFMA
+  // operands.  (Read straight into registers, each 16-byte load of a wave
+  // touches 16 token rows at a 64-byte lane stride.)  Unit u of token t is
+  // stored at slot u ^ t of its 256-byte row, so that the 16 rows read at
+  // once fall into distinct banks.
+  constexpr bool XLDS = BITS == 8 && MG == 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XLDS ? 4 * kGemvBatch * 4096 : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int fr = lane % 16, g = lane / 16;
@@ -710,6 +721,9 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   v4i acc[MG];
 #pragma unroll
   for (int tg = 0; tg < MG; ++tg) acc[tg] = v4i{0, 0, 0, 0};
+  __amdgpu_buffer_rsrc_t rX;
+  if constexpr (XLDS)
+    rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(codes), (short)0, (int)(M * K), 0x00020000);
   for (int64_t s0 = wave; s0 < steps; s0 += 4 * kGemvBatch) {
     uint4 w[kGemvBatch];
 #pragma unroll
@@ -717,6 +731,28 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
       const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
       const int64_t kw = ps * 16 + 4 * g;
       w[b] = (st < steps && kw < KW) ? load_stream(wrow + kw) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (XLDS) {
+      // the previous batch's operand reads are done before its area is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int t0 = lane / 16, q = lane % 16;
+#pragma unroll
+      for (int b = 0; b < kGemvBatch; ++b) {
+        const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+        if (st >= steps) break;  // wave-uniform
+        uint8_t* dst = xs + (wave * kGemvBatch + b) * 4096;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // four tokens per load; groups wholly past M are not loaded (their
+          // output columns are not stored), tokens past M in a partly
+          // filled group lie beyond the range and read as zero
+          if (4 * j >= M) break;  // wave-uniform
+          const int t = 4 * j + t0;
+          const uint32_t off = (uint32_t)(t * K + ps * 256 + 16 * (q ^ t));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, dst + 1024 * j, 16, off, 0, 0, 0);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the batch's weights and codes
     }
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
@@ -737,7 +773,14 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
         if (MG > 1 && 16 * tg >= M) break;  // wave-uniform: no token of this group
         // activation codes for k = 16*kw .. 16*kw + 63 of token tok
         uint32_t x[16];
-        if (tok < M && kw < KW) {
+        if constexpr (XLDS) {
+          const uint8_t* row = xs + (wave * kGemvBatch + b) * 4096 + fr * 256;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * ((4 * g + i) ^ fr));
+            x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+          }
+        } else if (tok < M && kw < KW) {
           if constexpr (BITS == 8) {
             const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + tok * K + 16 * kw);
 #pragma unroll
@@ -790,8 +833,8 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
 }
 
 // ---------------------------------------------------------------------------
-// Decode with very few tokens (M <= 2, or M <= 4 at K >= 16384), K % 1024 == 0:
-// dot-product kernel.
+// Decode with very few tokens (M <= 2, or INT4 M <= 4 at K >= 16384),
+// K % 1024 == 0: dot-product kernel.
 // A block of 512 threads owns NB output features.  Thread t covers the 64
 // codes k = 64*(t % TK) .. +63 (TK = min(256, K/64) threads per feature row)
 // of RPT = NB / (512 / TK) of those features; it loads the tokens' codes for
@@ -1000,12 +1043,13 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       return hipGetLastError();
     }
   }
-  // the dot-product kernel for 1-2 tokens, and up to 4 from K = 16384; its
-  // per-token code loads grow with M, and at K = 4096 the matrix-core GEMV
-  // is faster from 3 tokens on (measured at N = 4096, 10 or more matrices
-  // cycled: M = 4 INT8 6.3 against 4.1 us, INT4 4.6 against 4.1; M = 2
-  // INT4 3.7 against 4.0; at K = 16384, M = 4 10.1 against 10.4)
-  if ((M <= 2 || (M <= 4 && K >= 16384)) && K % 1024 == 0) {
+  // the dot-product kernel for 1-2 tokens, and for 3-4 INT4 tokens from
+  // K = 16384; its per-token code loads grow with M, and the matrix-core
+  // GEMV is faster from 3 tokens on otherwise (measured at N = 4096, 10 or
+  // more matrices cycled, us dot against MFMA: K = 4096, M = 4 INT8 6.3 /
+  // 3.8, INT4 4.6 / 4.4; M = 2 INT4 3.7 / 4.0; K = 16384, M = 4 INT8 9.9 /
+  // 8.5 (INT8 codes staged through LDS), INT4 10.2 / 10.7)
+  if ((M <= 2 || (BITS == 4 && M <= 4 && K >= 16384)) && K % 1024 == 0) {
     const int64_t tk = K / 64 < 256 ? K / 64 : 256;
 #define HBL_DOT(MT, TK)                                                                                      \
   if (N % DotGeom<BITS, OUT, MT, TK>::NB == 0) {                                                           \
@@ -1032,7 +1076,9 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 #define HBL_GV(MG)                                                                                              \
   hipLaunchKernelGGL((k_gemv<BITS, OUT, MG>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales, rowsum, wp, \
                      alpha, (int)M, N, K, out, ldo)
-    if (M <= 16) HBL_GV(1);
+    // (one INT8 group stages its codes by buffer loads, whose range is
+    // 16 K bytes < 2^31; longer rows take the two-group kernel)
+    if (M <= 16 && (BITS == 4 || 16 * K <= (int64_t)INT_MAX)) HBL_GV(1);
     else if (M <= 32) HBL_GV(2);
     else if (M <= 64) HBL_GV(4);
     else HBL_GV(8);
