@@ -833,14 +833,16 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
 }
 
 // ---------------------------------------------------------------------------
-// Decode with very few tokens (M <= 2, or INT4 M <= 4 at K >= 16384),
-// K % 1024 == 0: dot-product kernel.
-// A block of 512 threads owns NB output features.  Thread t covers the 64
-// codes k = 64*(t % TK) .. +63 (TK = min(256, K/64) threads per feature row)
-// of RPT = NB / (512 / TK) of those features; it loads the tokens' codes for
-// its k-range once (registers) and streams the rows' packed weights with one
-// 16-byte load per row (consecutive threads read consecutive 16 bytes of a
-// row).  Each weight word gives 4 dwords of bytes c = q_w + 1, multiplied
+// Decode with very few tokens (M <= 2, or INT4 M <= 4 at K = 16384), K a
+// power of two from 1024 to 16384: dot-product kernel.
+// A block of 512 threads owns NB output features.  Thread t covers 64 codes
+// of RPT = NB / (512 / TK) of those features (TK = K / 64 threads per
+// feature row; kt = t % TK): k = 64 kt .. + 63 (one 16-byte weight load
+// per row, consecutive threads reading consecutive 16 bytes of a row), or,
+// for INT8 codes up to K = 8192, the four 16-code groups kt + TK j (j =
+// 0..3, so that consecutive threads also read consecutive 16-byte pieces
+// of the codes); it loads the tokens' codes once (registers) and streams
+// the rows' packed weights, every load issued first.  Each weight word gives 4 dwords of bytes c = q_w + 1, multiplied
 // into the codes with v_dot4_i32_i8; INT4 codes are widened to 16 q_x (the
 // sums are divided by 16 at the end, exactly).  Partial sums are reduced
 // over the TK threads of a row (xor-butterflies within a wave, then a fixed
@@ -870,10 +872,24 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
   const int64_t n0 = (int64_t)blockIdx.x * NB;
   const int64_t KW = K / 16;
 
-  // the weights: rows n0 + rg + RP*i, words 4*kt .. 4*kt+3; issue every load first
+  // IL: the thread's codes are the four 16-code groups kt + TK j (j =
+  // 0..3), so that the lanes of a wave read consecutive 16-byte pieces of
+  // codes and consecutive weight words (INT8 codes up to K = 8192: M = 1,
+  // K = 4096 3.5 -> 3.1 us, M = 2 4.4 -> 3.7; at K = 16384 and with INT4
+  // codes, read as 8-byte pieces, 3-11 % slower); else the 64 consecutive
+  // codes 64 kt .. + 63 and one 16-byte weight load per row.  Weights: rows
+  // n0 + rg + RP i; every load is issued first.
+  constexpr bool IL = BITS == 8 && TK <= 128;
   uint4 w[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) w[i] = load_stream(wp + (n0 + rg + (int64_t)RP * i) * KW + 4 * kt);
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t* row = wp + (n0 + rg + (int64_t)RP * i) * KW;
+    if constexpr (IL)
+      w[i] = make_uint4(__builtin_nontemporal_load(row + kt), __builtin_nontemporal_load(row + kt + TK),
+                        __builtin_nontemporal_load(row + kt + 2 * TK), __builtin_nontemporal_load(row + kt + 3 * TK));
+    else
+      w[i] = load_stream(row + 4 * kt);
+  }
 
   // the tokens' codes for k = 64*kt .. +63, as 16 dwords of signed bytes
   uint32_t x[MT][16];
@@ -881,10 +897,11 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
   for (int m = 0; m < MT; ++m) {
     if (m < M) {
       if constexpr (BITS == 8) {
-        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (int64_t)m * K + 64 * kt);
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (int64_t)m * K) +
+                         (IL ? kt : 4 * kt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 u = p[q];
+          const uint4 u = p[IL ? TK * q : q];
           x[m][4 * q] = u.x; x[m][4 * q + 1] = u.y; x[m][4 * q + 2] = u.z; x[m][4 * q + 3] = u.w;
         }
       } else {
@@ -1049,8 +1066,10 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
   // more matrices cycled, us dot against MFMA: K = 4096, M = 4 INT8 6.3 /
   // 3.8, INT4 4.6 / 4.4; M = 2 INT4 3.7 / 4.0; K = 16384, M = 4 INT8 9.9 /
   // 8.5 (INT8 codes staged through LDS), INT4 10.2 / 10.7)
-  if ((M <= 2 || (BITS == 4 && M <= 4 && K >= 16384)) && K % 1024 == 0) {
-    const int64_t tk = K / 64 < 256 ? K / 64 : 256;
+  // (a thread covers 64 codes of each of its rows, TK = K / 64 a power of
+  // two from 16 to 256: K = 1024 ... 16384)
+  if ((M <= 2 || (BITS == 4 && M <= 4 && K >= 16384)) && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0) {
+    const int64_t tk = K / 64;
 #define HBL_DOT(MT, TK)                                                                                      \
   if (N % DotGeom<BITS, OUT, MT, TK>::NB == 0) {                                                           \
     hipLaunchKernelGGL((k_gemv_dot<BITS, OUT, MT, TK>), dim3((unsigned)(N / DotGeom<BITS, OUT, MT, TK>::NB)), \

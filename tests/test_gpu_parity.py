@@ -146,6 +146,20 @@ def test_gemm_exact_on_oracle_codes(hbl, M, N, K, bits):
     assert np.array_equal(acc.cpu().numpy(), ref)
 
 
+# decode token counts with K past the dot-product kernel's range (a power
+# of two up to 16384): K = 3072 and 5120 (multiples of 1024, not powers of
+# two) and 32768 take the matrix-core weight streaming
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
+@pytest.mark.parametrize("N,K", [(32, 3072), (16, 5120), (16, 32768)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_decode_widths_outside_dot_kernel(hbl, M, N, K, bits):
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 2000 + M + N + K)
+    acc = hbl.ternary_gemm(_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(),
+                           torch.from_numpy(rowsum).cuda(), torch.from_numpy(packed.view(np.int32)).cuda(),
+                           torch.tensor([alpha], dtype=torch.float32).cuda(), K, out_dtype=hbl.OUT_I32)
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(codes, bits, packed, K))
+
+
 @pytest.mark.parametrize("M", [5, 130])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_gemm_rescaled_outputs(hbl, M, bits):
