@@ -34,7 +34,7 @@ int ternarize_partials(int64_t N, int64_t K);
 // best at 4 slices, M = 1024 unsplit; K = 16384, M <= 256 at 8, M = 512 at
 // 4, M = 1024 at 2; from 256 tiles on, none.
 struct SplitPlan {
-  int bn, tm, tn, ksplit;
+  int bm = 256, bn, tm, tn, ksplit;
   // M-group of the item walk (split_item): an XCD's 32 consecutive items
   // cover 2 row blocks x 16 column blocks, whose codes and weights it then
   // fetches once into its L2 (measured on MI355X at M = 2048, N = K =
@@ -44,16 +44,21 @@ struct SplitPlan {
   int64_t items() const { return (int64_t)tm * tn * ksplit; }
 };
 constexpr int kSplitItems = 256;
-inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
+// wide_narrow: the narrow tiles are 128 x 256 instead of 256 x 128 (the
+// FP6 x FP4 matmul, split or not)
+inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split,
+                            bool wide_narrow = false) {
   SplitPlan p;
   const int64_t g256 = ((M + 255) / 256) * ((N + 255) / 256);
-  p.bn = g256 >= cu_count ? 256 : 128;
-  p.tm = (int)((M + 255) / 256);
+  const bool narrow = g256 < cu_count;
+  p.bm = narrow && wide_narrow ? 128 : 256;
+  p.bn = narrow && !wide_narrow ? 128 : 256;
+  p.tm = (int)((M + p.bm - 1) / p.bm);
   p.tn = (int)((N + p.bn - 1) / p.bn);
   p.ksplit = 1;
   const int64_t G = (int64_t)p.tm * p.tn, nk = K / 128;
   auto ok = [&](int S, int64_t items, int64_t min_stages) {
-    return may_split && p.bn == 128 && G * S <= items && (nk / 4) % S == 0 && nk / S >= min_stages;
+    return may_split && narrow && G * S <= items && (nk / 4) % S == 0 && nk / S >= min_stages;
   };
   while (ok(p.ksplit * 2, kSplitItems, G >= kSplitItems / 2 ? 32 : 16)) p.ksplit *= 2;
   if (ok(p.ksplit * 2, kSplitItems / 2, 8)) p.ksplit *= 2;

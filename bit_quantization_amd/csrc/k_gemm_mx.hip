@@ -34,9 +34,9 @@
 //
 // Kernel structure (k_gemm_mx): persistent, one block of 8 waves (two per
 // SIMD) per CU, block tile 256 x 256 (4 x 2 waves) when those tiles fill the
-// chip, else 128 tokens x 256 features (2 x 4 waves), or 256 x 128 (4 x 2)
-// for the items of a K split; wave tile 64 x 128 or 64 x 64 of 32x32x64
-// MFMAs with fp32 accumulators.  (The kernel also builds with 4 waves, one per
+// chip, else 128 tokens x 256 features (2 x 4 waves), also for the items of
+// a K split; wave tile 64 x 128 or 64 x 64 of 32x32x64 MFMAs with fp32
+// accumulators.  (The kernel also builds with 4 waves, one per
 // SIMD, 128 x BN/2 wave tiles: 5-20 % slower, since a wave's barrier and
 // operand waits then leave its matrix core idle.)  A stage is 128 codes (two MFMA steps);
 // four stage buffers, each its own LDS variable, are refilled four stages
@@ -308,9 +308,9 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     asm volatile("" : "+s"(r));
     int fr = lane % 32, h = lane / 32;
     asm volatile("" : "+v"(fr), "+v"(h));
-    if (BM == 256 && BN == 128 && ksplit > 1) {
+    if ((BM == 128 || BN == 128) && ksplit > 1) {
       // exact partial sums, in fragment order: each store is 1 KB contiguous
-      // (splits use 256 x 128 tiles only)
+      // (splits use the narrow tiles only)
       const int64_t item = r * P + slot;
       if (p16) {
         uint4* dst = static_cast<uint4*>(part) + (item * NW + wave) * (FN * FM * 2 * 64) + lane;
@@ -494,11 +494,13 @@ namespace {
 // gives the same value), then the rescale of Eq. 9.  One thread per four
 // (fp32 partials) or eight (int16) outputs of one lane's fragment, reading
 // the partials in the order k_gemm_mx wrote them.
-template <int OUT, int BN, bool P16, int NWV>
+template <int OUT, int BM, int BN, bool P16, int NWV>
 __global__ void __launch_bounds__(256)
 k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const float* __restrict__ alpha, int64_t M, int64_t N, void* __restrict__ out, int64_t ldo) {
-  constexpr int NW = NWV, WGM = NW / 2, BM = 256, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // the wave grid of k_gemm_mx for the tile shape
+  constexpr int NW = NWV, WGM = BM == 128 ? 2 : NW / 2, WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   constexpr int QU = P16 ? 2 : 4;                         // 16-byte units per fragment and lane
   const int64_t per_tile = (int64_t)NW * FN * FM * QU * 64;  // units of one tile
   const int64_t units = (int64_t)tilesM * tilesN * per_tile;
@@ -545,18 +547,15 @@ k_mx_reduce(const void* __restrict__ part, int ksplit, int tilesM, int tilesN, i
   }
 }
 
-// waves of the 256 x 128 tile kernel (8: 5 % faster than 4 at M = 2048,
-// N = K = 4096, 1-6 % on K-split shapes)
-constexpr int kMxWaves128 = 8;
-
 struct MxPlan : SplitPlan {
   bool p16;  // int16 partial sums
-  size_t part_bytes() const { return ksplit > 1 ? (size_t)ksplit * tm * tn * 256 * bn * (p16 ? 2 : 4) : 0; }
+  size_t part_bytes() const { return ksplit > 1 ? (size_t)ksplit * tm * tn * bm * bn * (p16 ? 2 : 4) : 0; }
 };
 
+// narrow tiles (fewer 256 x 256 tiles than CUs) are 128 x 256, split or not
 MxPlan mx_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
   MxPlan p;
-  static_cast<SplitPlan&>(p) = split_plan(M, N, K, cu_count, may_split);
+  static_cast<SplitPlan&>(p) = split_plan(M, N, K, cu_count, may_split, true);
   p.p16 = 8 * (K / p.ksplit) <= 32767;  // |partial sum| <= 8 K / ksplit
   return p;
 }
@@ -581,50 +580,36 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   const int64_t P = std::min<int64_t>(((G + 7) / 8) * 8, cap);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const int ksplit = p.ksplit, tm = p.tm, tn = p.tn, gm = p.gm, p16 = p.p16 ? 1 : 0;
-  // every tile shape runs 8 waves (two per SIMD: one wave's barrier and
-  // operand waits are covered by the other's MFMAs)
-#define HBL_MXT(OUT, BM, BN, W, TM, TN, GM)                                                                      \
-  hipLaunchKernelGGL((k_gemm_mx<OUT, BM, BN, W>), dim3((unsigned)P), dim3(64 * W), 0, s, c, scales, wq, alpha, M,  \
-                     N, K, out, ldo, TM, TN, GM, ksplit, p16, part)
-#define HBL_MX(OUT, BN, W) HBL_MXT(OUT, 256, BN, W, tm, tn, gm)
-  if (p.bn == 128 && ksplit == 1) {
-    // unsplit narrow tiles as 128 x 256: the same outputs per tile from 20
-    // instead of 28 KB of operands per stage (6-bit codes cost more bytes
-    // per row than 2-bit weights).  Measured on MI355X against 256 x 128
-    // (bit-identical): layer at M = 2048, N = K = 4096 35.1 -> 32.9 us,
-    // M = 1024 28.8 -> 27.2, M = 3072 55.1 -> 53.4; M = 2048, K = 16384
-    // 102 -> 99.
-    const int tm2 = (int)((M + 127) / 128), tn2 = (int)((N + 255) / 256);
-    const int64_t P = std::min<int64_t>(((int64_t)tm2 * tn2 + 7) / 8 * 8, cap);
-    if (out_kind == 0) HBL_MXT(0, 128, 256, 8, tm2, tn2, gm);
-    else if (out_kind == 1) HBL_MXT(1, 128, 256, 8, tm2, tn2, gm);
-    else HBL_MXT(2, 128, 256, 8, tm2, tn2, gm);
-  } else if (p.bn == 256) {
-    if (out_kind == 0) HBL_MX(0, 256, 8); else if (out_kind == 1) HBL_MX(1, 256, 8); else HBL_MX(2, 256, 8);
-  } else if (kMxWaves128 == 8) {
-    if (out_kind == 0) HBL_MX(0, 128, 8); else if (out_kind == 1) HBL_MX(1, 128, 8); else HBL_MX(2, 128, 8);
+  // 8 waves (two per SIMD: one wave's barrier and operand waits are covered
+  // by the other's MFMAs).  Narrow tiles are 128 x 256: the same outputs per
+  // tile as 256 x 128 from 20 instead of 28 KB of operands per stage (6-bit
+  // codes cost more bytes per row than 2-bit weights).  Measured on MI355X
+  // against 256 x 128 (bit-identical), unsplit: layer at M = 2048, N = K =
+  // 4096 35.1 -> 32.9 us, M = 1024 28.8 -> 27.2, M = 3072 55.1 -> 53.4;
+  // M = 2048, K = 16384 102 -> 99.
+#define HBL_MXT(OUT, BM, BN)                                                                                     \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, BM, BN, 8>), dim3((unsigned)P), dim3(512), 0, s, c, scales, wq, alpha, M, N, K, \
+                     out, ldo, tm, tn, gm, ksplit, p16, part)
+  if (p.bm == 128) {
+    if (out_kind == 0) HBL_MXT(0, 128, 256); else if (out_kind == 1) HBL_MXT(1, 128, 256); else HBL_MXT(2, 128, 256);
   } else {
-    if (out_kind == 0) HBL_MX(0, 128, 4); else if (out_kind == 1) HBL_MX(1, 128, 4); else HBL_MX(2, 128, 4);
+    if (out_kind == 0) HBL_MXT(0, 256, 256); else if (out_kind == 1) HBL_MXT(1, 256, 256); else HBL_MXT(2, 256, 256);
   }
-#undef HBL_MX
 #undef HBL_MXT
   if (ksplit == 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // splits use 256 x 128 tiles only
-  const int64_t units = (int64_t)tm * tn * 256 * 128 / (p16 ? 8 : 4);
+  // (splits use the 128 x 256 tiles only)
+  const int64_t units = (int64_t)tm * tn * 128 * 256 / (p16 ? 8 : 4);
   const unsigned rb = (unsigned)((units + 255) / 256);
-#define HBL_MXR(OUT, P16, W)                                                                                      \
-  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, P16, W>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, gm, scales, \
+#define HBL_MXR(OUT, P16)                                                                                          \
+  hipLaunchKernelGGL((k_mx_reduce<OUT, 128, 256, P16, 8>), dim3(rb), dim3(256), 0, s, part, ksplit, tm, tn, gm, scales, \
                      alpha, M, N, out, ldo)
-#define HBL_MXR_W(OUT, P16) \
-  if (kMxWaves128 == 8) HBL_MXR(OUT, P16, 8); else HBL_MXR(OUT, P16, 4)
   if (p16) {
-    if (out_kind == 0) { HBL_MXR_W(0, true); } else if (out_kind == 1) { HBL_MXR_W(1, true); } else { HBL_MXR_W(2, true); }
+    if (out_kind == 0) { HBL_MXR(0, true); } else if (out_kind == 1) { HBL_MXR(1, true); } else { HBL_MXR(2, true); }
   } else {
-    if (out_kind == 0) { HBL_MXR_W(0, false); } else if (out_kind == 1) { HBL_MXR_W(1, false); } else { HBL_MXR_W(2, false); }
+    if (out_kind == 0) { HBL_MXR(0, false); } else if (out_kind == 1) { HBL_MXR(1, false); } else { HBL_MXR(2, false); }
   }
-#undef HBL_MXR_W
 #undef HBL_MXR
   return hipGetLastError();
 }
