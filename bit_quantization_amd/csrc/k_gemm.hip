@@ -317,21 +317,18 @@ k_gemm(const void* __restrict__ codes, const float* __restrict__ scales,
 // into distinct banks.
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
-// waves of the 256 x 128 tile kernel (8: the layer 2-11 % faster than with
-// 4 at M = 2048, N = K = 4096 and on K-split shapes)
-constexpr int kPtWaves128 = 8;
-
 // smallest M K at which the int8 layer takes the split persistent matmul
 constexpr int64_t kSplitMinMK = int64_t(1) << 20;
 
 // the plan of k_gemm_pt
+// narrow tiles (fewer 256 x 256 tiles than CUs) are 128 x 256, split or not
 SplitPlan pt_plan(int64_t M, int64_t N, int64_t K, int cu_count, bool may_split) {
-  return split_plan(M, N, K, cu_count, may_split);
+  return split_plan(M, N, K, cu_count, may_split, true);
 }
 
-// int32 partial sums of a split plan's 256 x 128 items (0: no split)
+// int32 partial sums of a split plan's items (0: no split)
 size_t pt_partial_bytes(const SplitPlan& p) {
-  return p.ksplit > 1 ? (size_t)p.items() * 256 * 128 * sizeof(int32_t) : 0;
+  return p.ksplit > 1 ? (size_t)p.items() * p.bm * p.bn * sizeof(int32_t) : 0;
 }
 
 template <int BITS, int OUT, int BM, int BN, int NWV>
@@ -543,9 +540,9 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     // r made opaque here: nothing of the epilogue is computed early and kept
     // live through the stage loop
     asm volatile("" : "+s"(r));
-    if (BM == 256 && BN == 128 && ksplit > 1) {
+    if ((BM == 128 || BN == 128) && ksplit > 1) {
       // raw int32 partial sums in fragment order: each store is 1 KB
-      // contiguous (splits use 256 x 128 tiles only)
+      // contiguous (splits use the narrow tiles only)
       int4* dst = part + ((int64_t)(r * P + slot) * NW + wave) * (FN * FM * 4 * 64) + lane;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -998,16 +995,18 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
   }
 }
 
-// Sum of the ksplit int32 partial sums of k_gemm_pt's 256 x 128 tiles, then
+// Sum of the ksplit int32 partial sums of k_gemm_pt's 128 x 256 split items, then
 // the epilogue of Eq. 9 (/ 16 for INT4, minus the row sum, rescale).  One
 // thread per four outputs of one lane's fragment, reading the partials in
 // the order k_gemm_pt wrote them.
-template <int BITS, int OUT, int NWV>
+template <int BITS, int OUT, int BM, int BN, int NWV>
 __global__ void __launch_bounds__(256)
 k_pt_reduce(const int4* __restrict__ part, int ksplit, int tilesM, int tilesN, int gm, const float* __restrict__ scales,
             const int32_t* __restrict__ rowsum, const float* __restrict__ alpha, int64_t M, int64_t N,
             void* __restrict__ out, int64_t ldo) {
-  constexpr int NW = NWV, WGM = NW / 2, BM = 256, BN = 128, WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  // the wave grid of k_gemm_pt for the tile shape
+  constexpr int NW = NWV, WGM = BM == 128 ? 2 : NW / 2, WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   const int64_t units = (int64_t)tilesM * tilesN * (BM * BN / 4);
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
@@ -1050,13 +1049,14 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
       const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
       int4* pt = static_cast<int4*>(part);
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 128, kPtWaves128>), dim3((unsigned)P), dim3(64 * kPtWaves128), 0,
-                         s, codes, scales, rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
+      // (splits use the narrow tiles, 128 x 256)
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 128, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, p.ksplit, pt);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      const int64_t units = (int64_t)p.tm * p.tn * (256 * 128 / 4);
-      hipLaunchKernelGGL((k_pt_reduce<BITS, OUT, kPtWaves128>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, pt,
-                         p.ksplit, p.tm, p.tn, p.gm, scales, rowsum, alpha, M, N, out, ldo);
+      const int64_t units = (int64_t)p.tm * p.tn * (128 * 256 / 4);
+      hipLaunchKernelGGL((k_pt_reduce<BITS, OUT, 128, 256, 8>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
+                         pt, p.ksplit, p.tm, p.tn, p.gm, scales, rowsum, alpha, M, N, out, ldo);
       return hipGetLastError();
     }
   }
@@ -1109,18 +1109,16 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
     const SplitPlan p = pt_plan(M, N, K, cu_count, false);
     const int64_t cap = cu_count >= 8 ? (cu_count / 8) * 8 : 8;
     const int64_t P = std::min<int64_t>(((p.items() + 7) / 8) * 8, cap);
-    if (p.bn == 256) {
+    if (p.bm == 256) {
       // 256 x 256 tiles run 8 waves (two per SIMD)
       hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 256, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
                          rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     } else {
-      // narrower tiles as 128 x 256 (the 256 x 128 shape is kept for the
-      // items of a K split): the same outputs per tile from 24 instead of 36
-      // KB (INT8 codes) or 16 instead of 20 KB (INT4) of operands per stage
-      const int tm2 = (int)((M + 127) / 128), tn2 = (int)((N + 255) / 256);
-      const int64_t P2 = std::min<int64_t>(((int64_t)tm2 * tn2 + 7) / 8 * 8, cap);
-      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 128, 256, 8>), dim3((unsigned)P2), dim3(512), 0, s, codes, scales,
-                         rowsum, wp, alpha, M, N, K, out, ldo, tm2, tn2, p.gm, 1, nullptr);
+      // narrower tiles as 128 x 256: the same outputs per tile as 256 x 128
+      // from 24 instead of 36 KB (INT8 codes) or 16 instead of 20 KB (INT4)
+      // of operands per stage
+      hipLaunchKernelGGL((k_gemm_pt<BITS, OUT, 128, 256, 8>), dim3((unsigned)P), dim3(512), 0, s, codes, scales,
+                         rowsum, wp, alpha, M, N, K, out, ldo, p.tm, p.tn, p.gm, 1, nullptr);
     }
     return hipGetLastError();
   }

@@ -114,10 +114,10 @@ def test_forward_workspace(hbl):
     assert need >= 10 * 128 + 2 * 40
     assert need % 256 == 0
     # room for int32 partial sums of a K split of the persistent matmul when
-    # its 256 x 128 tiles leave most CUs idle and M K >= 2^20: M = 64,
-    # N = 4096, K = 16384 -> 32 tiles, 8 slices; M = 32 streams the weights
+    # its tiles leave most CUs idle and M K >= 2^20: M = 64, N = 4096,
+    # K = 16384 -> 16 tiles of 128 x 256, 8 slices; M = 32 streams the weights
     assert lib.hbl_forward_workspace_size(32, 4096, 16384, 8) == 32 * 16384 + 2 * 256
-    assert lib.hbl_forward_workspace_size(64, 4096, 16384, 8) == 64 * 16384 + 2 * 256 + 8 * 32 * 256 * 128 * 4
+    assert lib.hbl_forward_workspace_size(64, 4096, 16384, 8) == 64 * 16384 + 2 * 256 + 8 * 16 * 128 * 256 * 4
     # 16 tokens stream the weights; 256 tiles need no split
     assert lib.hbl_forward_workspace_size(16, 4096, 16384, 8) == 16 * 16384 + 2 * 256
     assert lib.hbl_forward_workspace_size(2048, 4096, 4096, 4) == 2048 * 2048 + 2 * 8192

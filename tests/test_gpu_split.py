@@ -14,7 +14,7 @@ from parity_util import bf16_to_f64, check_output, to_device
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K) -> slices of the 256 x 128 tiles: (64, 4096, 16384) 8,
+# (M, N, K) -> slices of the 128 x 256 tiles: (64, 4096, 16384) 8,
 # (100, 272, 16384) 16, (256, 4096, 4096) 4, (200, 4224, 16384) 4 (a ragged
 # last tile column), (768, 4096, 4096) 2
 SHAPES = [(64, 4096, 16384), (100, 272, 16384), (256, 4096, 4096), (200, 4224, 16384), (768, 4096, 4096)]
