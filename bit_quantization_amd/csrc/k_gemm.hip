@@ -694,15 +694,18 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
        const float* __restrict__ alpha, int M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo) {
   __shared__ v4i red[MG][3][64];
-  // One group of INT8 tokens: each step's codes (16 tokens x 256 bytes) are
-  // copied into the wave's LDS area by direct-to-LDS loads in which 16
-  // consecutive lanes read one token's 256 bytes, then read back as MFMA
-  // operands.  (Read straight into registers, each 16-byte load of a wave
-  // touches 16 token rows at a 64-byte lane stride.)  Unit u of token t is
-  // stored at slot u ^ t of its 256-byte row, so that the 16 rows read at
-  // once fall into distinct banks.
-  constexpr bool XLDS = BITS == 8 && MG == 1;
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[XLDS ? 4 * kGemvBatch * 4096 : 16];
+  // One group of tokens: each step's codes (16 tokens x RB bytes: 256 for
+  // INT8, 128 for INT4) are copied into the wave's LDS area by direct-to-LDS
+  // loads in which RB / 16 consecutive lanes read one token's RB bytes, then
+  // read back as MFMA operands.  (Read straight into registers, each 16-byte
+  // load of a wave touches 16 token rows at a 64- or 32-byte lane stride.)
+  // Unit u of token t is stored at slot u ^ t (INT8) or u ^ (t / 2 mod 8)
+  // (INT4) of its row, so that the 16 rows read at once fall into distinct
+  // banks.
+  constexpr bool XLDS = MG == 1;
+  constexpr int RB = BITS == 8 ? 256 : 128, XU = RB / 16, TPL = 1024 / RB;
+  auto xswz = [](int t) { return BITS == 8 ? t : (t >> 1) & 7; };
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XLDS ? 4 * kGemvBatch * 16 * RB : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int fr = lane % 16, g = lane / 16;
@@ -720,7 +723,7 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   for (int tg = 0; tg < MG; ++tg) acc[tg] = v4i{0, 0, 0, 0};
   __amdgpu_buffer_rsrc_t rX;
   if constexpr (XLDS)
-    rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(codes), (short)0, (int)(M * K), 0x00020000);
+    rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(codes), (short)0, (int)(M * K * BITS / 8), 0x00020000);
   for (int64_t s0 = wave; s0 < steps; s0 += 4 * kGemvBatch) {
     uint4 w[kGemvBatch];
 #pragma unroll
@@ -732,20 +735,20 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
     if constexpr (XLDS) {
       // the previous batch's operand reads are done before its area is refilled
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int t0 = lane / 16, q = lane % 16;
+      const int t0 = lane / XU, q = lane % XU;
 #pragma unroll
       for (int b = 0; b < kGemvBatch; ++b) {
         const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
         if (st >= steps) break;  // wave-uniform
-        uint8_t* dst = xs + (wave * kGemvBatch + b) * 4096;
+        uint8_t* dst = xs + (wave * kGemvBatch + b) * 16 * RB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // four tokens per load; groups wholly past M are not loaded (their
+        for (int j = 0; j < 16 / TPL; ++j) {
+          // TPL tokens per load; groups wholly past M are not loaded (their
           // output columns are not stored), tokens past M in a partly
           // filled group lie beyond the range and read as zero
-          if (4 * j >= M) break;  // wave-uniform
-          const int t = 4 * j + t0;
-          const uint32_t off = (uint32_t)(t * K + ps * 256 + 16 * (q ^ t));
+          if (TPL * j >= M) break;  // wave-uniform
+          const int t = TPL * j + t0;
+          const uint32_t off = (uint32_t)(t * (K * BITS / 8) + ps * RB + 16 * (q ^ xswz(t)));
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, dst + 1024 * j, 16, off, 0, 0, 0);
         }
       }
@@ -771,11 +774,24 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
         // activation codes for k = 16*kw .. 16*kw + 63 of token tok
         uint32_t x[16];
         if constexpr (XLDS) {
-          const uint8_t* row = xs + (wave * kGemvBatch + b) * 4096 + fr * 256;
+          const uint8_t* row = xs + (wave * kGemvBatch + b) * 16 * RB + fr * RB;
+          if constexpr (BITS == 8) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * ((4 * g + i) ^ fr));
-            x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+            for (int i = 0; i < 4; ++i) {
+              const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * ((4 * g + i) ^ fr));
+              x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * ((2 * g + i) ^ xswz(fr)));
+              const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                x[8 * i + 2 * qq] = sext_nibbles(ww[qq] & 0x0f0f0f0fu);
+                x[8 * i + 2 * qq + 1] = sext_nibbles((ww[qq] >> 4) & 0x0f0f0f0fu);
+              }
+            }
           }
         } else if (tok < M && kw < KW) {
           if constexpr (BITS == 8) {
@@ -1095,9 +1111,9 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
 #define HBL_GV(MG)                                                                                              \
   hipLaunchKernelGGL((k_gemv<BITS, OUT, MG>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales, rowsum, wp, \
                      alpha, (int)M, N, K, out, ldo)
-    // (one INT8 group stages its codes by buffer loads, whose range is
-    // 16 K bytes < 2^31; longer rows take the two-group kernel)
-    if (M <= 16 && (BITS == 4 || 16 * K <= (int64_t)INT_MAX)) HBL_GV(1);
+    // (one group stages its codes by buffer loads, whose range is 16 K BITS / 8
+    // bytes < 2^31; longer rows take the two-group kernel)
+    if (M <= 16 && 16 * K * BITS / 8 <= (int64_t)INT_MAX) HBL_GV(1);
     else if (M <= 32) HBL_GV(2);
     else if (M <= 64) HBL_GV(4);
     else HBL_GV(8);
