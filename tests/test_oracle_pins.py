@@ -7,9 +7,12 @@ Sources of truth used here, per function of the oracle:
               in tests/golden/hadamard_h2.txt; closed forms (H e0, H 1, spikes);
               invariants (H H = I, norm preservation, linearity); the page's own
               op count (tests/golden/fwht_opcount.txt).
-  quantizer - hand-worked cases (tests/golden/quant_cases.txt); range and error
+  quantizer - hand-worked cases (tests/golden/quant_cases.txt); exact
+              rounding ties (tests/golden/quant_ties.txt, round half to even,
+              also for the ternariser and the KV quantiser); range and error
               invariants; code frequencies on Gaussian rows against the normal
               CDF (closed form).
+  bf16      - torch's fp32 -> bf16 conversion and hand-worked ties.
   ternarizer- hand-worked case; idempotence on already-ternary matrices;
               alpha, zero and +-1 fractions on Gaussian weights against closed
               forms.
@@ -340,12 +343,20 @@ def test_forward_zero_rows_give_zero():
 
 
 def test_dequant_output_bf16_rounding():
-    acc = np.array([[1, -3, 1000, 0]], np.int32)
+    # the bf16 output is torch's round-to-nearest-even conversion of the
+    # fp32 value (torch is an implementation independent of the oracle)
+    import torch
+    acc = np.array([[1, -3, 1000, 0, 257, -257, 771]], np.int32)
     s = np.array([0.1], np.float32)
     y64, yb = oracle.dequant_output(acc, s, np.float32(0.5))
-    np.testing.assert_allclose(y64[0], [0.05, -0.15, 50.0, 0.0], rtol=1e-7)
-    np.testing.assert_array_equal(workloads.bf16_to_f32(yb)[0],
-                                  workloads.bf16_to_f32(workloads.bf16_bits(y64.astype(np.float32)))[0])
+    np.testing.assert_allclose(y64[0], [0.05, -0.15, 50.0, 0.0, 12.85, -12.85, 38.55], rtol=1e-7)
+    want = torch.from_numpy(y64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(yb, want)
+    # acc = 257 and 771 at scale 1 land exactly halfway between bf16 values
+    # (257 = 256 + 1, 771 = 768 + 3 with 8 significant bits): ties to even
+    _, yt = oracle.dequant_output(np.array([[257, 771, -257]], np.int32), np.array([1.0], np.float32),
+                                  np.float32(1.0))
+    assert workloads.bf16_to_f32(yt)[0].tolist() == [256.0, 772.0, -256.0]
 
 
 # ------------------------------------------- normalisation layer (Eq. 9 LN)
@@ -610,3 +621,122 @@ def test_kv_quant_bos_kept_at_8_bits():
     # the low-bit slot of position 0 is written too
     c3, _, _, _ = oracle.kv_quant(np.ascontiguousarray(x[:, :1]), 3, keep_bos8=False)
     assert np.array_equal(codes[:, :1], c3)
+
+
+# ------------------------------------------------ exact rounding ties (Eq. 2)
+# Reading: RoundClip rounds an exact half to the even neighbour.  The cases
+# in golden/quant_ties.txt make the fp32 product the quantiser rounds exactly
+# k + 1/2 (the row statistic makes the per-row factor a power of two); the
+# expected codes are worked out by hand there.  Each test first checks that
+# premise in fp32, so a case cannot silently stop being a tie.
+
+def _hexes(vals):
+    return np.array([float.fromhex(v) for v in vals], np.float32)
+
+
+def _tie_row(kv, key):
+    x = _hexes(kv[f"{key}.x"])
+    K = int(kv[f"{key}.K"][0])
+    row = np.zeros((1, K), np.float32)
+    row[0, :x.size] = x
+    return row, x.size
+
+
+def _assert_exact_halves(prod, n_min):
+    """The products are exact in fp32 (checked in fp64) and at least n_min of
+    them sit exactly halfway between two integers."""
+    frac = np.abs(prod.astype(np.float64)) % 1.0
+    assert np.sum(frac == 0.5) >= n_min
+
+
+def test_golden_ties_int8():
+    _, kv = read_golden("quant_ties.txt")
+    row, n = _tie_row(kv, "int8")
+    eps = np.float32(1e-5)
+    gamma = np.abs(row).max()
+    assert np.float32(gamma + eps) == np.float32(1.984375)
+    f = np.float32(127.0) / np.float32(gamma + eps)
+    assert f == np.float32(64.0)
+    prod = row[0, :n] * f
+    assert np.array_equal(prod.astype(np.float64), row[0, :n].astype(np.float64) * 64.0)
+    _assert_exact_halves(prod, 5)
+    codes, scales, rowsum = oracle.quantize(row, 8, hadamard=False)
+    want = [int(v) for v in kv["int8.codes"]]
+    assert codes[0, :n].tolist() == want and not codes[0, n:].any()
+    assert rowsum[0] == int(kv["int8.rowsum"][0])
+
+
+def test_golden_ties_int4():
+    _, kv = read_golden("quant_ties.txt")
+    row, n = _tie_row(kv, "int4")
+    eps = np.float32(1e-5)
+    beta = np.float32(np.abs(row.astype(np.float64)).sum() / row.shape[1])
+    assert beta == np.float32(float.fromhex(kv["int4.beta"][0]))
+    # the fp32 sum of |x| is exact too (every partial sum is a multiple of
+    # 2^-17 below 128), so an fp32 statistic gives the same beta
+    assert np.float32(np.abs(row).sum(dtype=np.float32)) == np.float32(beta * row.shape[1])
+    f = np.float32(math.sqrt(7.0)) / np.float32(beta + eps)
+    assert f == np.float32(2.0)
+    _assert_exact_halves(row[0, :n] * f, 8)
+    codes, scales, rowsum = oracle.quantize(row, 4, hadamard=False)
+    q = oracle.unpack_int4(codes, row.shape[1])
+    assert q[0, :n].tolist() == [int(v) for v in kv["int4.codes"]] and not q[0, n:].any()
+    assert rowsum[0] == int(kv["int4.rowsum"][0])
+
+
+def test_golden_ties_ternary():
+    _, kv = read_golden("quant_ties.txt")
+    row, n = _tie_row(kv, "ternary")
+    alpha_want = np.float32(float.fromhex(kv["ternary.alpha"][0]))
+    assert np.float32(np.abs(row.astype(np.float64)).sum() / row.size) == alpha_want
+    d = np.float32(alpha_want + np.float32(1e-5))
+    assert d == np.float32(0.25)
+    _assert_exact_halves(row[0, :n] / d, 2)
+    _, alpha, q = oracle.ternarize(row)
+    assert alpha == alpha_want
+    assert q[0, :n].tolist() == [int(v) for v in kv["ternary.codes"]] and not q[0, n:].any()
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_golden_ties_kv_quant(bits):
+    _, kv = read_golden("quant_ties.txt")
+    x = _hexes(kv[f"kv{bits}.x"])
+    eps = np.float32(1e-5)
+    gamma = np.abs(x).max()
+    Q = np.float32((1 << (bits - 1)) - 1)
+    f = Q / np.float32(gamma + eps)
+    assert f == np.float32({3: 2.0, 4: 4.0}[bits])
+    _assert_exact_halves(x * f, 4)
+    codes, scales, _, _ = oracle.kv_quant(x.reshape(1, 1, 1, 8), bits, keep_bos8=False)
+    # unpack the bytes by the packing contract (3-bit: bits 3j of a 24-bit
+    # little-endian value; 4-bit: low nibble first)
+    b = codes.ravel().astype(np.int64)
+    if bits == 3:
+        v = int(b[0]) | int(b[1]) << 8 | int(b[2]) << 16
+        u = [(v >> (3 * j)) & 7 for j in range(8)]
+    else:
+        u = [int(b[j // 2] >> (4 * (j % 2))) & 15 for j in range(8)]
+    assert u == [int(v) for v in kv[f"kv{bits}.codes"]]
+
+
+def test_golden_bf16_ties():
+    import torch
+    _, kv = read_golden("quant_ties.txt")
+    f = np.array([int(v, 16) for v in kv["bf16.f32"]], np.uint32).view(np.float32)
+    want = [int(v, 16) for v in kv["bf16.bits"]]
+    assert oracle.f32_to_bf16(f).tolist() == want
+    assert torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).tolist() == want
+
+
+def test_bf16_conversion_equals_torch():
+    # finite fp32 patterns, a third of them forced to exact ties (low half
+    # 0x8000), against torch's fp32 -> bf16 conversion
+    import torch
+    rng = np.random.default_rng(17)
+    u = rng.integers(0, 1 << 32, size=12000, dtype=np.uint64).astype(np.uint32)
+    u[::3] = (u[::3] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    u = u[(u & np.uint32(0x7F800000)) != np.uint32(0x7F800000)]          # no Inf / NaN
+    u = u[(u & np.uint32(0x7FFFFFFF)) < np.uint32(0x7F7F8000)]           # no overflow to Inf
+    f = u.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16(f), want)
