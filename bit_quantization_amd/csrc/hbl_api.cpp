@@ -74,7 +74,8 @@ int check_flags(int flags) {
 int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t ldo) {
   if (M < 0) return fail(HBL_ERR_SHAPE, "M = %lld is negative", (long long)M);
   if (N < 16 || N % 16 != 0) return fail(HBL_ERR_SHAPE, "N = %lld must be a positive multiple of 16", (long long)N);
-  if (K < 64 || K % 64 != 0) return fail(HBL_ERR_SHAPE, "K = %lld must be a positive multiple of 64", (long long)K);
+  if (K < 64 || K % 64 != 0 || K > HBL_MAX_GEMM_K)
+    return fail(HBL_ERR_SHAPE, "K = %lld must be a multiple of 64 in [64, %d]", (long long)K, HBL_MAX_GEMM_K);
   if (ldo < N) return fail(HBL_ERR_SHAPE, "ldo = %lld < N = %lld", (long long)ldo, (long long)N);
   if (ldo % 4 != 0) return fail(HBL_ERR_ALIGN, "ldo = %lld is not a multiple of 4", (long long)ldo);
   // token rows are addressed with 64-bit offsets; the grid size is the limit
@@ -351,8 +352,6 @@ int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales, const uint32_
     return fail(HBL_ERR_NULL, "codes_mx, scales, w_mx, alpha and out must be non-NULL");
   if (!aligned16(codes_mx) || !aligned16(w_mx) || !aligned16(out) || !aligned4(scales) || !aligned4(alpha))
     return fail(HBL_ERR_ALIGN, "codes_mx, w_mx and out must be 16-byte aligned");
-  if ((K / 4 * 3) * 256 > (int64_t)INT_MAX)  // a 256-row tile is addressed with 32-bit offsets
-    return fail(HBL_ERR_SHAPE, "K = %lld is too large for the FP6 x FP4 path", (long long)K);
   hipError_t e = hbl::launch_gemm_mx(codes_mx, scales, w_mx, alpha, M, N, K, out_dtype, out, ldo, nullptr, 0,
                                      cu_count_cached(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");

@@ -83,6 +83,13 @@ extern "C" {
  * 7B model, Table 8). */
 #define HBL_MAX_K 16384
 
+/* Largest K of the matmul entry points (hbl_ternary_gemm, hbl_forward and
+ * their FP6 x FP4 forms): 2^21.  Up to it every partial sum of the FP6 x
+ * FP4 matmul is an integer of magnitude <= 8 K <= 2^24, exact in its fp32
+ * accumulators; the int8 path's int32 sums (|sum| <= 256 K) and the 32-bit
+ * byte offsets of its 256-row tiles stay in range as well. */
+#define HBL_MAX_GEMM_K 2097152
+
 /* Library version, major*10000 + minor*100 + patch. */
 int hbl_version(void);
 
@@ -152,8 +159,20 @@ int hbl_hadamard_backward_f32(const void* dy, int dy_dtype, int64_t M, int64_t K
  *              -128, 127);  scale = gamma/127.
  *   bits == 4: beta = mean_j |x_r|;  q = RoundClip(sqrt(7)/(beta+eps) x_r,
  *              -8, 7);      scale = beta/sqrt(7).
- * The factor Qmax/(stat+eps) is formed once per row with an IEEE divide and
- * each code is rint(x_r * factor) clipped, all in fp32.
+ * The factor Qmax/(stat+eps) is formed once per row in fp32 with an IEEE
+ * divide, and each code is the round-to-nearest-even of x_r * factor,
+ * clipped.  How that product is rounded:
+ *   - K < 1024 (and every row without HBL_HADAMARD below 1024): the fp32
+ *     product fl(x_r * factor) is formed, then rounded to an integer (rint);
+ *   - K >= 1024: one fused multiply-add rounds the exact product
+ *     v * fl(c * factor) to an integer, v being the un-normalised transform
+ *     of the row (fp32) and c = 2^(-k/2) the normalisation (c = 1 without
+ *     HBL_HADAMARD; for odd k, c = fl(1/sqrt(K))).  For even k this is the
+ *     exact real product x_r * factor rounded once.
+ * The two forms give the same code except where x_r * factor lies within
+ * half an fp32 ulp of a half-integer (then fl() may land on the half).
+ * The statistic: gamma is the exact maximum; beta is a fixed-order fp32
+ * tree sum of |x_r| divided by K (the transform's scale applied to the sum).
  *
  * codes:  out, int8 [M][K] (bits 8) or uint32 [M][K/8] (bits 4).
  * scales: out, float [M].
@@ -189,12 +208,16 @@ int hbl_norm_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
  *   acc[m][n] = sum_k q_x[m][k] * q_w[n][k]            (exact, int32)
  *   out[m][n] = (scales[m] * alpha) * acc[m][n]        (fp32, then rounded
  *                                                       to nearest-even bf16)
- * codes/scales/rowsum: as written by hbl_hadamard_quant (rowsum required).
+ * codes/scales/rowsum: as written by hbl_hadamard_quant.  rowsum is
+ *     required: the kernels multiply the codes with the stored weight
+ *     bytes c = q + 1 and subtract sum_k q_x, which the quantiser produces
+ *     as it writes the codes.  (A caller holding codes from elsewhere
+ *     passes their row sums.)
  * w_packed, alpha:     as written by hbl_ternarize_weights.
  * out_dtype: HBL_OUT_BF16 or HBL_OUT_F32 write the rescaled value;
  *            HBL_OUT_I32 writes acc itself (for exact checks).
  * out: [M][ldo] of out_dtype; ldo >= N, ldo % 4 == 0.
- * Shapes: N >= 16, N % 16 == 0, K >= 64, K % 64 == 0.
+ * Shapes: N >= 16, N % 16 == 0, K >= 64, K % 64 == 0, K <= HBL_MAX_GEMM_K.
  * Token counts M <= 128 take a kernel that streams the weights once (one
  * block per 16 output features, the tokens in groups of 16); larger M take
  * the matrix-core tile kernel.
@@ -343,7 +366,8 @@ int hbl_hadamard_quant_mx(const void* x, int x_dtype, int64_t M, int64_t K,
 /* hbl_ternary_gemm_mx -- hbl_ternary_gemm for MX6 codes and MX4 weights:
  *   out[m][n] = (scales[m] * alpha) * sum_k q_x[m][k] q_w[n][k]
  * (HBL_OUT_I32: the exact sum).  No row sums are needed.
- * Shapes: N >= 16, N % 16 == 0; K >= 512, K % 512 == 0; ldo as there. */
+ * Shapes: N >= 16, N % 16 == 0; K >= 512, K % 512 == 0, K <= HBL_MAX_GEMM_K;
+ * ldo as there. */
 int hbl_ternary_gemm_mx(const void* codes_mx, const float* scales,
                         const uint32_t* w_mx, const float* alpha, int64_t M,
                         int64_t N, int64_t K, int out_dtype, void* out,

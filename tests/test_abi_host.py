@@ -108,6 +108,18 @@ def test_gemm_errors(hbl):
     assert g(A, 8, B, C, D, E, 0, 64, 256, 0, F, 64, None) == hbl.OK         # M = 0
 
 
+@pytest.mark.parametrize("K,expect", [((1 << 21), 0), ((1 << 21) + 64, 2), ((1 << 23), 2)])
+def test_gemm_k_bound(hbl, K, expect):
+    # K <= 2^21 (HBL_MAX_GEMM_K): the int32 sums and 32-bit tile offsets of
+    # the int8 path and the fp32 sums of the FP6 x FP4 path stay exact;
+    # checked with M = 0 so nothing is enqueued when the call is accepted
+    lib = hbl.lib()
+    assert lib.hbl_ternary_gemm(A, 8, B, C, D, E, 0, 64, K, 0, F, 64, None) == expect
+    assert lib.hbl_ternary_gemm_mx(A, B, D, E, 0, 64, K, 0, F, 64, None) == expect
+    if expect:
+        assert "K =" in last(hbl)
+
+
 def test_forward_workspace(hbl):
     lib = hbl.lib()
     need = lib.hbl_forward_workspace_size(10, 64, 256, 4)
