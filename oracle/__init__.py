@@ -205,6 +205,26 @@ def gemm_i32(codes: np.ndarray, bits: int, packed: np.ndarray, K: int) -> np.nda
     return acc
 
 
+def gemm_exact(codes: np.ndarray, bits: int, packed: np.ndarray, K: int) -> np.ndarray:
+    """acc[m][n] = sum_k q_x[m][k] q_w[n][k], the same integers as
+    gemm_i32, with a library matmul as the step (numpy/BLAS in fp64) for
+    the large parity cases the triple loop cannot finish in seconds.
+
+    The codes and weights are unpacked by the oracle's own unpackers; every
+    product and every partial sum is an integer of magnitude at most
+    128 K <= 2^21 < 2^53, so the fp64 matmul is exact whatever its blocking
+    and summation order.  Pinned against gemm_i32 and numpy's int64 matmul
+    in tests/test_oracle_pins.py."""
+    if K > (1 << 23):
+        raise ValueError("gemm_exact: K too large for the exactness argument")
+    q = codes_int8(np.ascontiguousarray(codes), bits, K).astype(np.float64)
+    t, bad = unpack_ternary(packed, K)
+    if bad:
+        raise ValueError(f"gemm_exact: {bad} invalid 2-bit weight fields")
+    acc = q @ t.astype(np.float64).T
+    return acc.astype(np.int32)
+
+
 def dequant_output(acc: np.ndarray, scales: np.ndarray, alpha) -> tuple[np.ndarray, np.ndarray]:
     """(y64 fp64, y as bf16 bits) from the int32 accumulator."""
     acc = np.ascontiguousarray(acc, dtype=np.int32)

@@ -27,3 +27,18 @@ def hbl():
         pytest.skip("no GPU visible")
     import bit_quantization_amd as hbl_pkg
     return hbl_pkg
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With HBL_PARITY_REPORT set to a path, write the worst parity figures
+    met by the GPU tests of this session (tolerances are in parity_util)."""
+    path = os.environ.get("HBL_PARITY_REPORT")
+    if not path or "parity_util" not in sys.modules:
+        return
+    import json
+    import parity_util
+    with open(path, "w") as fh:
+        json.dump(dict(parity_util.WORST, tolerances={"hadamard_rel": parity_util.HAD_TOL,
+                                                      "scale_rel": parity_util.SCALE_TOL,
+                                                      "output_rel_l2": parity_util.OUT_TOL,
+                                                      "code_fraction": parity_util.CODE_FRAC}), fh, indent=1)

@@ -6,7 +6,9 @@ Tolerances (the arithmetic behind them is in the design notes):
   codes            identical, except at most ceil(1e-4 * n) elements per
                    tensor that differ by exactly 1 and sit at a rounding tie
                    of the oracle's value (|frac(|x_r * factor|) - 1/2| < 1e-3)
-  scales           relative difference <= 1e-5
+  scales           relative difference <= 1e-6 (about 8 ulp: the fp32
+                   statistic of rotated values that agree with the oracle's
+                   to a few ulp, or an fp32 tree sum against an fp64 sum)
   integer matmul   bit-exact on the oracle's codes
   layer output     per row ||y_gpu - y_ref||_2 <= 1e-2 ||y_ref||_2; rows with
                    y_ref == 0 must be exactly 0
@@ -20,8 +22,13 @@ import torch
 
 HAD_TOL = 1e-5
 CODE_FRAC = 1e-4
-SCALE_TOL = 1e-5
+SCALE_TOL = 1e-6
 OUT_TOL = 1e-2
+
+# worst cases met in this process, written out by the test session when
+# HBL_PARITY_REPORT names a file (tests/conftest.py)
+WORST = {"hadamard_rel": 0.0, "scale_rel": 0.0, "output_rel_l2": 0.0, "code_tie_mismatches": 0,
+         "code_tie_fraction": 0.0}
 
 
 def to_device(x: np.ndarray) -> torch.Tensor:
@@ -62,6 +69,8 @@ def check_codes(gpu_q: np.ndarray, ora_q: np.ndarray, xr: np.ndarray, bits: int,
     v = np.abs(xr[idx] * f[idx[0]]).astype(np.float64)
     frac = v - np.floor(v)
     assert np.all(np.abs(frac - 0.5) < 1e-3), f"{what}: a mismatch is not at a rounding tie: {frac}"
+    WORST["code_tie_mismatches"] += nbad
+    WORST["code_tie_fraction"] = max(WORST["code_tie_fraction"], nbad / d.size)
     return nbad
 
 
@@ -70,6 +79,8 @@ def check_scales(gpu_s: np.ndarray, ora_s: np.ndarray, what: str) -> None:
     rel = np.abs(gpu_s.astype(np.float64) - ora_s) / den
     zero = ora_s == 0
     assert np.all(gpu_s[zero] == 0), f"{what}: zero rows must have zero scale"
+    if np.any(~zero):
+        WORST["scale_rel"] = max(WORST["scale_rel"], float(rel[~zero].max()))
     assert np.all(rel[~zero] <= SCALE_TOL), f"{what}: scale rel err {rel[~zero].max():.3e}"
 
 
@@ -80,6 +91,7 @@ def check_hadamard(gpu_y: np.ndarray, ref: np.ndarray, what: str) -> float:
     assert np.all(err[zero] == 0), f"{what}: zero rows must map to zero"
     rel = err[~zero] / den[~zero]
     worst = float(rel.max()) if rel.size else 0.0
+    WORST["hadamard_rel"] = max(WORST["hadamard_rel"], worst)
     assert worst <= HAD_TOL, f"{what}: Hadamard max rel err {worst:.3e}"
     return worst
 
@@ -92,6 +104,7 @@ def check_output(gpu_y: np.ndarray, y64: np.ndarray, what: str) -> float:
     assert np.all(np.abs(g[zero]) == 0), f"{what}: rows with zero reference must be exactly zero"
     rel = err[~zero] / ref[~zero]
     worst = float(rel.max()) if rel.size else 0.0
+    WORST["output_rel_l2"] = max(WORST["output_rel_l2"], worst)
     assert worst <= OUT_TOL, f"{what}: output rel L2 {worst:.3e}"
     return worst
 

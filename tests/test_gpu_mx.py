@@ -109,24 +109,6 @@ def test_forward_mx_zero_tokens(hbl):
     assert hbl.forward_mx(x, wq, alpha, N=32).shape == (0, 32)
 
 
-@pytest.mark.parametrize("name", ["wo_7b", "wdown_7b"])
-def test_forward_mx_full_size(hbl, name):
-    c = getattr(workloads, name)()
-    x_np, w_np = c["x"], c["w"]
-    M, K = x_np.shape
-    packed, alpha = hbl.ternarize_weights(to_device(w_np))
-    wq = hbl.prepare_weights_mx(packed, K)
-    x = to_device(x_np)
-    y = hbl.forward_mx(x, wq, alpha)
-    y_int = hbl.forward(x, packed, alpha, 4)
-    assert torch.equal(y.view(torch.int16), y_int.view(torch.int16)), f"{name}: FP6 x FP4 and int8 paths differ"
-    del y_int
-    o_packed, o_alpha, _ = oracle.ternarize(w_np)
-    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).choice(M, 6, replace=False)]))
-    y64 = oracle.forward(np.ascontiguousarray(x_np[rows]), o_packed, o_alpha, 4, hadamard=True)
-    check_output(bf16_to_f64(y[torch.from_numpy(rows).cuda()]), y64, f"{name} forward_mx")
-
-
 def test_gemm_mx_full_tile_grid_exact(hbl):
     # 256 x 256 tiles (the grid fills the chip): int32 sums on sampled rows
     M, N, K = 4096, 4096, 4096

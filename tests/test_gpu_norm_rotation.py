@@ -5,7 +5,7 @@ activation rotation variant (Table 5), each against the CPU oracle.
 
 Tolerances as for the core path: rotated values 1e-5 of the row maximum;
 codes identical except at most 1e-4 of them, off by one at rounding ties;
-scales 1e-5 relative; bf16 layer outputs 1e-2 per-row L2.  Ternary codes of
+scales 1e-6 relative; bf16 layer outputs 1e-2 per-row L2.  Ternary codes of
 the rotated weights follow the code rule (the GPU rotates in fp32, the
 oracle in fp64), and alpha agrees to 1e-5 relative.
 """

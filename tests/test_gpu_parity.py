@@ -1,8 +1,7 @@
 """GPU parity of every entry point against the CPU oracle, through the C ABI.
 
-Small cases span several tiles and ragged tails; the five workloads run at
-their full sizes in the launch configuration the benchmark times, compared
-on sampled token rows that the oracle recomputes one by one.
+Small cases span several tiles and ragged tails (the five workloads at their
+full sizes are in test_gpu_full_size.py).
 """
 from __future__ import annotations
 
@@ -18,17 +17,6 @@ from parity_util import (bf16_to_f64, check_codes, check_hadamard, check_output,
 pytestmark = pytest.mark.gpu
 
 ALL_LOG2K = list(range(4, 15))
-
-
-def rows_of(x: np.ndarray, rows) -> np.ndarray:
-    return np.ascontiguousarray(x[rows])
-
-
-def sample_rows(M: int, n: int = 24, seed: int = 0) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    r = set(rng.choice(M, min(n, M), replace=False).tolist())
-    r.update({0, M - 1})
-    return np.array(sorted(r))
 
 
 # ---------------------------------------------------------------- rotation
@@ -160,6 +148,21 @@ def test_gemm_decode_widths_outside_dot_kernel(hbl, M, N, K, bits):
     assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(codes, bits, packed, K))
 
 
+# every decode dispatch branch at the 7B widths: the dot-product kernel (M <=
+# 2, and INT4 M = 3-4 at K = 16384), its interleaved INT8 code loads (K <=
+# 8192) and the matrix-core weight streaming (M = 3-4 otherwise)
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("K", [4096, 8192, 16384])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_decode_dispatch_exact(hbl, M, K, bits):
+    N = 4096
+    codes, scales, rowsum, packed, alpha = _gemm_inputs(M, N, K, bits, 3000 + M + K // 1024 + bits)
+    acc = hbl.ternary_gemm(_dev_codes(codes, bits), bits, torch.from_numpy(scales).cuda(),
+                           torch.from_numpy(rowsum).cuda(), torch.from_numpy(packed.view(np.int32)).cuda(),
+                           torch.tensor([alpha], dtype=torch.float32).cuda(), K, out_dtype=hbl.OUT_I32)
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_exact(codes, bits, packed, K))
+
+
 @pytest.mark.parametrize("M", [5, 130])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_gemm_rescaled_outputs(hbl, M, bits):
@@ -240,66 +243,3 @@ def test_zero_tokens(hbl):
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(1, 1, 32, 256)))
     assert hbl.forward(x, packed, alpha, 4).shape == (0, 32)
-
-
-# ------------------------------------------------- full-size workloads
-
-def _full_size_layer(hbl, x_np, w_np, bits, had, what, gemm_rows=8):
-    """GPU at full size; oracle on sampled rows.  Checks codes and scales on
-    the sampled rows, the integer matmul bit-exactly on the oracle's codes of
-    all rows (sampled outputs), and the bf16 layer output."""
-    M, K = x_np.shape
-    x = to_device(x_np)
-    packed, alpha = hbl.ternarize_weights(to_device(w_np))
-    o_packed, o_alpha, _ = oracle.ternarize(w_np)
-    assert float(alpha.cpu()[0]) == float(o_alpha), f"{what}: alpha"
-    assert np.array_equal(packed.cpu().numpy().view(np.uint32), o_packed), f"{what}: ternary codes"
-
-    rows = sample_rows(M)
-    xs = rows_of(x_np, rows)
-    q, s, rs = hbl.hadamard_quant(x, bits, hadamard=had)
-    oq, os_, ors, xr = oracle.quantize(xs, bits, hadamard=had, want_xr=True)
-    gq = oracle.codes_int8(codes_to_numpy(q, bits)[rows], bits, K)
-    check_codes(gq, oracle.codes_int8(oq, bits, K), xr, bits, what)
-    check_scales(s.cpu().numpy()[rows], os_, what)
-
-    # integer matmul on the oracle's codes of every row (the bench's launch shape)
-    all_q, all_s, all_rs = oracle.quantize(x_np, bits, hadamard=had)
-    acc = hbl.ternary_gemm(_dev_codes(all_q, bits), bits, torch.from_numpy(all_s).cuda(),
-                           torch.from_numpy(all_rs).cuda(), packed, alpha, K, out_dtype=hbl.OUT_I32)
-    gr = rows[np.linspace(0, len(rows) - 1, min(gemm_rows, len(rows))).astype(int)]
-    ref = oracle.gemm_i32(np.ascontiguousarray(all_q[gr]), bits, o_packed, K)
-    assert np.array_equal(acc.cpu().numpy()[gr], ref), f"{what}: integer matmul"
-    del acc
-
-    y = hbl.forward(x, packed, alpha, bits, hadamard=had)
-    y64 = oracle.forward(rows_of(x_np, gr), o_packed, o_alpha, bits, hadamard=had)
-    check_output(bf16_to_f64(y[torch.from_numpy(gr).cuda()]), y64, what)
-
-
-def test_full_wo_7b(hbl):
-    c = workloads.wo_7b()
-    _full_size_layer(hbl, c["x"], c["w"], c["bits"], True, "wo_7b")
-
-
-def test_full_wdown_7b(hbl):
-    c = workloads.wdown_7b()
-    _full_size_layer(hbl, c["x"], c["w"], c["bits"], True, "wdown_7b")
-
-
-@pytest.mark.parametrize("K,N", [(4096, 4096), (16384, 4096)])
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_full_decode(hbl, K, N, M):
-    x = workloads.decode_inputs(K, M)
-    w = workloads.decode_weights(K, N, 0)
-    _full_size_layer(hbl, x, w, 8, True, f"decode M={M} K={K}")
-
-
-@pytest.mark.parametrize("layer", ["q", "o", "up", "down"])
-@pytest.mark.parametrize("bits", [8, 4])
-def test_full_block_7b(hbl, layer, bits):
-    names = [n for n, *_ in workloads.BLOCK_7B_LAYERS]
-    _, K, N, had = workloads.BLOCK_7B_LAYERS[names.index(layer)]
-    x = workloads.block_input(workloads.BLOCK_7B_INPUT_OF[layer])
-    w = workloads.block_weights(layer)
-    _full_size_layer(hbl, x, w, bits, had, f"block_7b {layer} INT{bits}")

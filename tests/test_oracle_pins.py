@@ -18,7 +18,9 @@ Sources of truth used here, per function of the oracle:
               forms.
   packing   - hand-worked words (tests/golden/packing_cases.txt); round trips.
   int GEMM  - numpy int64 matmul; all-(+1) weights give the row sums; identity
-              weights give the codes back.
+              weights give the codes back; the library-matmul form
+              (gemm_exact, fp64 BLAS, used by the large GPU parity cases)
+              equals the triple loop.
   forward   - closed form: for x = H z with integer z the layer returns
               alpha * T z exactly (INT8) or alpha * T (3c/sqrt7) sign(z) (INT4).
 All formulas: architecture write-up of "BitNet v2: Native 4-bit Activations
@@ -283,6 +285,28 @@ def test_gemm_equals_numpy_matmul(bits):
     codes = q if bits == 8 else oracle.pack_int4(q)
     acc = oracle.gemm_i32(codes, bits, oracle.pack_ternary(t), K)
     assert np.array_equal(acc, q.astype(np.int64) @ t.astype(np.int64).T)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,N,K", [(7, 32, 64), (33, 48, 1024), (5, 16, 16384)])
+def test_gemm_exact_equals_triple_loop(bits, M, N, K):
+    # the library-matmul form of the oracle's matmul gives the triple loop's
+    # integers, including the extreme sums (codes at the range ends against
+    # all-+1 / all--1 weight rows)
+    rng = np.random.default_rng(M + N + K + bits)
+    lo, hi = (-128, 128) if bits == 8 else (-8, 8)
+    q = rng.integers(lo, hi, size=(M, K)).astype(np.int8)
+    q[0] = lo
+    q[1] = hi - 1
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    t[0] = 1
+    t[1] = -1
+    codes = q if bits == 8 else oracle.pack_int4(q)
+    packed = oracle.pack_ternary(t)
+    acc = oracle.gemm_exact(codes, bits, packed, K)
+    assert np.array_equal(acc, oracle.gemm_i32(codes, bits, packed, K))
+    assert np.array_equal(acc, q.astype(np.int64) @ t.astype(np.int64).T)
+    assert acc[0, 0] == lo * K and acc[0, 1] == -lo * K
 
 
 def test_gemm_special_weights():
