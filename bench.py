@@ -1,17 +1,21 @@
 """Throughput of the H-BitLinear forward on one MI355X.
 
-Default workload: the attention output projection of a 7B-shaped BitNet v2
-block with the rotation, M=2048 tokens, K=N=4096, INT4 activations (bf16
-Student-t(3) input, 1 % of channels x20; N(0, 0.02^2) weights, ternarised).
-One step = one whole layer (rotation + quantisation, then the ternary
-matmul with its rescale) over the batch, inputs already resident in HBM.
+Default workload: the seven linear layers of one 7B-shaped BitNet v2 block
+at M = 65536 tokens (64 sequences x 1024): Q, K, V (4096 -> 4096) and up,
+gate (4096 -> 16384) as plain BitLinear, Wo (4096 -> 4096) and Wdown
+(16384 -> 4096) as H-BitLinear with the rotation.  Activations bf16
+Student-t(3) with 1 % of channels x20, weights N(0, 0.02^2) ternarised.  One
+step = the block's 4 quantisations (Q/K/V and up/gate share theirs) and 7
+matmuls, inputs resident in HBM.  The headline is INT4 activations on the
+FP6 x FP4 matrix cores; INT8 activations are timed beside it.
 
 Prints one JSON line.  ``roofline`` is for the dominant kernel (the
-matrix-core matmul), its average duration measured with HIP events over
-back-to-back launches on the stream it runs on; ``cpu_baseline`` is the CPU
-oracle timed on a bounded sample of rows of the same workload.
+matrix-core matmul): algorithmic ops per launch over its average duration,
+from HIP events around every launch of the timed steps on the stream the
+library launches on.  ``cpu_baseline`` is the CPU oracle timed on a bounded
+sample of rows of the same workload, at all cores and at one thread.
 
-Other workloads (--workload): tiny, wo_7b, wdown_7b, decode, block_7b,
+Other workloads (--workload): tiny, wo_7b, wdown_7b (single layers), decode,
 msweep (layer time over token counts 1-4096 for BitLinear INT8 against
 H-BitLinear INT8/INT4, and the break-even batch where the rotated INT4 layer
 catches up), kvcache (the post-RoPE K/V quantiser on one 7B layer's cache
@@ -76,7 +80,7 @@ def parse():
     # of a process run 3-5 % slower)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="wo_7b",
+    ap.add_argument("--workload", default="block_7b",
                     choices=["tiny", "wo_7b", "wdown_7b", "decode", "block_7b", "msweep", "kvcache", "copy"])
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="copy: bytes moved per launch (calibrates the HBM traffic counters)")
@@ -500,31 +504,98 @@ def run_kvcache(args, hbl, torch):
             "launch": launch}
 
 
-def run_block(args, hbl, torch):
-    """The seven linears of one 7B block at M = 65536 tokens: Q/K/V share one
-    quantisation of their input, up/gate another; Wo and Wdown rotate their
-    inputs.  One step = 4 quantisations + 7 matmuls, per activation mode."""
+BLOCK_GROUPS = [("attn_in", False, ["q", "k", "v"]), ("o_in", True, ["o"]),
+                ("ffn_in", False, ["up", "gate"]), ("down_in", True, ["down"])]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def block_cpu_baseline(bits, rows_all_cores=256, rows_one_core=16):
+    """The CPU oracle on the 7B block, as it stands: per activation input the
+    quantiser (fp64 rotation for Wo and Wdown), then for each linear its
+    triple-loop integer matmul and the rescale, on the first R token rows of
+    each input; tokens/s = R / (time of the whole block on those rows).  The
+    oracle's work is linear in the token count, so the rate applies to M
+    (extrapolated).  Timed at all cores and at one thread."""
+    import oracle
     import workloads
-    M = workloads.CONFIGS["block_7b"]["M"]
-    xs = {name: dev_x(workloads.block_input(name)) for name, _ in workloads.BLOCK_7B_INPUTS}
     ws = {}
     for name, K, N, had in workloads.BLOCK_7B_LAYERS:
-        ws[name] = hbl.ternarize_weights(torch.from_numpy(workloads.block_weights(name)).cuda())
-    groups = [("attn_in", False, ["q", "k", "v"]), ("o_in", True, ["o"]),
-              ("ffn_in", False, ["up", "gate"]), ("down_in", True, ["down"])]
-    out = {}
-    for name, K, N, had in workloads.BLOCK_7B_LAYERS:
-        out[name] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    results = []
-    for bits in ([8, 4] if args.bits == 0 else [args.bits]):
-        mx = use_mx(args, bits, M, 4096)  # every input width here (4096, 16384) qualifies
+        packed, alpha, _ = oracle.ternarize(workloads.block_weights(name))
+        ws[name] = (packed, alpha, K)
+    R = max(rows_all_cores, rows_one_core)
+    xs = {name: workloads.block_input(name, M=R) for name, _ in workloads.BLOCK_7B_INPUTS}
+
+    def run(rows):
+        t = 0.0
+        for inp, had, layers in BLOCK_GROUPS:
+            x = np.ascontiguousarray(xs[inp][:rows])
+            t0 = time.perf_counter()
+            codes, scales, _ = oracle.quantize(x, bits, hadamard=had)
+            for layer in layers:
+                packed, alpha, K = ws[layer]
+                acc = oracle.gemm_i32(codes, bits, packed, K)
+                oracle.dequant_output(acc, scales, alpha)
+            t += time.perf_counter() - t0
+        return rows / t, t
+
+    all_cores = oracle.num_threads()
+    v_all, t_all = run(rows_all_cores)
+    oracle.set_num_threads(1)
+    try:
+        v_one, t_one = run(rows_one_core)
+    finally:
+        oracle.set_num_threads(all_cores)
+    what = ("the 7 linears of the block (4 quantisations with the fp64 rotation on Wo/Wdown inputs, 7 triple-loop "
+            f"integer matmuls and rescales), INT{bits}")
+    return {"value": v_all, "unit": "tokens/s", "cores": all_cores, "kind": "oracle",
+            "sample": f"first {rows_all_cores} token rows of each of the 4 block inputs, {what}; {t_all:.1f} s; "
+                      f"rate extrapolated to M = 65536 (the work is linear in M)",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "single_thread": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {rows_one_core} token rows of each input, same work; {t_one:.1f} s; "
+                                        "extrapolated"}}
+
+
+def run_block(args, hbl, torch):
+    """The seven linears of one 7B block at M = 65536 tokens, the pages'
+    largest shape (hidden 4096, FFN 16384).  Q/K/V share one quantisation of
+    their input, up/gate another (plain BitLinear); Wo and Wdown rotate
+    their inputs (H-BitLinear).  One step = the block's 4 quantisations and 7
+    matmuls, inputs resident in HBM.  The headline mode is INT4 on the FP6 x
+    FP4 matrix cores (--path int8: the int8 matrix cores); INT8 activations
+    are timed beside it.  Every launch of the timed steps is bracketed by HIP
+    events on the stream the library launches on (torch's current stream),
+    which gives the per-kernel averages of the roofline."""
+    import workloads
+    M = workloads.CONFIGS["block_7b"]["M"]
+    print(f"[bench] block_7b: drawing inputs (M = {M})", file=sys.stderr, flush=True)
+    xs = {name: dev_x(workloads.block_input(name)) for name, _ in workloads.BLOCK_7B_INPUTS}
+    dims = {name: (K, N, had) for name, K, N, had in workloads.BLOCK_7B_LAYERS}
+    ws = {name: hbl.ternarize_weights(torch.from_numpy(workloads.block_weights(name)).cuda())
+          for name, *_ in workloads.BLOCK_7B_LAYERS}
+    out = {name: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for name, K, N, _ in workloads.BLOCK_7B_LAYERS}
+    in_k = dict(workloads.BLOCK_7B_INPUTS)
+    peaks = measured().get("peaks", {})
+
+    def mode(bits):
+        mx = use_mx(args, bits, M, 4096)  # both input widths (4096, 16384) qualify
         qbuf = {}
-        for inp, had, layers in groups:
-            K = dict(workloads.BLOCK_7B_INPUTS)[inp]
+        for inp, had, layers in BLOCK_GROUPS:
+            K = in_k[inp]
             shape, dt = (((M + 255) // 256 * 256, K // 4 * 3), torch.uint8) if mx else hbl.codes_shape(M, K, bits)
             qbuf[inp] = (torch.empty(shape, dtype=dt, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda"),
                          torch.empty(M, dtype=torch.int32, device="cuda"))
-        wmx = {name: hbl.prepare_weights_mx(ws[name][0], K) for name, K, N, had in workloads.BLOCK_7B_LAYERS} if mx else {}
+        wmx = {name: hbl.prepare_weights_mx(ws[name][0], dims[name][0]) for name in dims} if mx else {}
 
         def quant(inp, had):
             q, sc, rs = qbuf[inp]
@@ -533,45 +604,118 @@ def run_block(args, hbl, torch):
                 hbl._check(hbl.lib().hbl_hadamard_quant_mx(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
                                                            hbl.HADAMARD if had else 0, q.data_ptr(), sc.data_ptr(),
                                                            hbl._stream()), "hbl_hadamard_quant_mx")
-                return
-            hbl._check(hbl.lib().hbl_hadamard_quant(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
-                                                    hbl.HADAMARD if had else 0, bits, q.data_ptr(), sc.data_ptr(),
-                                                    rs.data_ptr(), hbl._stream()), "hbl_hadamard_quant")
+            else:
+                hbl._check(hbl.lib().hbl_hadamard_quant(x.data_ptr(), hbl.DTYPE_BF16, M, x.shape[1], x.shape[1],
+                                                        hbl.HADAMARD if had else 0, bits, q.data_ptr(), sc.data_ptr(),
+                                                        rs.data_ptr(), hbl._stream()), "hbl_hadamard_quant")
 
         def gemm(inp, layer):
             q, sc, rs = qbuf[inp]
             p, a = ws[layer]
-            K = dict(workloads.BLOCK_7B_INPUTS)[inp]
             if mx:
-                hbl.ternary_gemm_mx(q, sc, wmx[layer], a, K, out=out[layer])
+                hbl.ternary_gemm_mx(q, sc, wmx[layer], a, in_k[inp], out=out[layer])
             else:
-                hbl.ternary_gemm(q, bits, sc, rs, p, a, K, out=out[layer])
+                hbl.ternary_gemm(q, bits, sc, rs, p, a, in_k[inp], out=out[layer])
 
-        def step():
-            for inp, had, layers in groups:
+        def step(ev=None):
+            for inp, had, layers in BLOCK_GROUPS:
+                if ev is not None:
+                    ev.append(("quant", inp, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
                 quant(inp, had)
+                if ev is not None:
+                    ev[-1][3].record()
                 for layer in layers:
+                    if ev is not None:
+                        ev.append(("gemm", layer, torch.cuda.Event(enable_timing=True),
+                                   torch.cuda.Event(enable_timing=True)))
+                        ev[-1][2].record()
                     gemm(inp, layer)
+                    if ev is not None:
+                        ev[-1][3].record()
 
+        print(f"[bench] block_7b INT{bits}: {args.warmup} warm-up and {args.steps} timed steps",
+              file=sys.stderr, flush=True)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        ev = []
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step()
+            step(ev)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-        per = {}
-        for inp, had, layers in groups:
-            per["quant " + inp] = time_stream(lambda: quant(inp, had), args.kernel_reps) * 1e6
-            for layer in layers:
-                per["gemm " + layer] = time_stream(lambda: gemm(inp, layer), args.kernel_reps) * 1e6
-        ops = sum(2.0 * M * K * N for _, K, N, _ in workloads.BLOCK_7B_LAYERS)
-        gemm_us = sum(v for k, v in per.items() if k.startswith("gemm"))
-        results.append({"bits": bits, "path": "FP6 x FP4 matrix cores" if mx else "int8 matrix cores",
-                        "tokens_per_s": M / dt, "ms_per_step": dt * 1e3, "effective_tops": ops / dt / 1e12,
-                        "gemm_only_tops": ops / (gemm_us * 1e-6) / 1e12, "kernel_us": per})
-    return {"metric": METRIC, "workload": "block_7b: the 7 linears of a 7B block, M=65536", "results": results}
+        kern = {}
+        for kind, name, a, b in ev:
+            kern.setdefault((kind, name), []).append(a.elapsed_time(b) * 1e-3)
+        k_us = {f"{kind} {name}": float(np.mean(v)) * 1e6 for (kind, name), v in kern.items()}
+        gemm_s = sum(float(np.mean(v)) for (kind, _), v in kern.items() if kind == "gemm")
+        quant_s = sum(float(np.mean(v)) for (kind, _), v in kern.items() if kind == "quant")
+        ops = sum(2.0 * M * K * N for K, N, _ in dims.values())
+        code_b = {inp: (M * in_k[inp] * 3 // 4 if mx else M * in_k[inp] // (2 if bits == 4 else 1))
+                  for inp, _, _ in BLOCK_GROUPS}
+        q_bytes = sum(M * in_k[inp] * 2 + code_b[inp] + (4 if mx else 8) * M for inp, _, _ in BLOCK_GROUPS)
+        g_min = sum(code_b[inp] + dims[l][1] * dims[l][0] // 4 + 2 * M * dims[l][1]
+                    for inp, _, layers in BLOCK_GROUPS for l in layers)
+        return {"bits": bits, "mx": mx, "dt": dt, "k_us": k_us, "gemm_s": gemm_s, "quant_s": quant_s, "ops": ops,
+                "q_bytes": q_bytes, "gemm_bytes_min": g_min, "n_gemm": len(dims), "n_quant": len(BLOCK_GROUPS)}
+
+    modes = [4, 8] if args.bits == 0 else [args.bits]
+    res_modes = {b: mode(b) for b in modes}
+    head = res_modes[modes[0]]
+    bits, mx, dt = head["bits"], head["mx"], head["dt"]
+    ops = head["ops"]
+    n_g, n_q = head["n_gemm"], head["n_quant"]
+    gemm_tops = ops / head["gemm_s"] / 1e12
+    best = peaks.get("i8_mfma_tops_best")
+    if mx:
+        peak, kernel = MX_PEAK_TOPS, "k_gemm_mx (FP6 x FP4 ternary matmul)"
+        meas = peaks.get("fp6fp4_mfma_tops_best")
+    else:
+        peak, kernel = I8_PEAK_TOPS, "k_gemm_pt (int8 ternary matmul)"
+        meas = best
+    hbm_meas = peaks.get("hbm_read_gbs")
+    roofline = {"bound": "mfma", "kernel": kernel, "achieved": gemm_tops, "peak": peak, "unit": "TOP/s",
+                "frac": gemm_tops / peak, "traffic": counter_traffic("block_7b", "gemm_mx" if mx else "gemm"),
+                "avg_kernel_us": head["gemm_s"] / n_g * 1e6, "algorithmic_ops_per_launch": ops / n_g,
+                "launches_per_step": n_g,
+                "measured_peak": {"tops": meas, "frac": gemm_tops / meas if meas else None,
+                                  "i8_mfma_tops": best, "frac_of_i8": gemm_tops / best if best else None,
+                                  "source": "profiles/peaks.md"}}
+    q_gbs = head["q_bytes"] / head["quant_s"] / 1e9
+    res = {
+        "metric": METRIC, "value": M / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp6xfp4" if mx else "i8", "data": "synthetic",
+        "config": {"workload": "block_7b: the 7 linears of one 7B block (Q/K/V 4096->4096 and up/gate "
+                               "4096->16384 plain BitLinear; Wo 4096->4096 and Wdown 16384->4096 H-BitLinear), "
+                               f"M = {M} tokens (64 x 1024), INT{bits} activations",
+                   "M": M, "bits": bits, "x_dtype": "bf16",
+                   "path": "FP6 x FP4 matrix cores (exact)" if mx else "int8 matrix cores"},
+        "effective_tops": ops / dt / 1e12,
+        "roofline": roofline,
+        "fused": {"effective_tops": ops / dt / 1e12,
+                  "frac_of_measured_i8_peak": ops / dt / 1e12 / best if best else None,
+                  "frac_of_published_i8_peak": ops / dt / 1e12 / I8_PEAK_TOPS},
+        "quant_kernel": {"bound": "hbm", "kernel": "k_fwht_quant64 (rotation + quantisation)",
+                         "avg_kernel_us": head["quant_s"] / n_q * 1e6,
+                         "algorithmic_bytes_per_launch": head["q_bytes"] / n_q, "achieved_gbs": q_gbs,
+                         "frac": q_gbs / HBM_PEAK_GBS,
+                         "frac_of_measured_read_peak": q_gbs / hbm_meas if hbm_meas else None,
+                         "traffic": counter_traffic("block_7b", "quant_mx" if mx else "quant")},
+        "gemm_bytes_min_per_step": head["gemm_bytes_min"],
+        "kernel_us": head["k_us"],
+        "launch": "eager launches on one stream, HIP events around each launch",
+    }
+    for b, r in res_modes.items():
+        if r is head:
+            continue
+        res[f"int{b}_mode"] = {"tokens_per_s": M / r["dt"], "ms_per_step": r["dt"] * 1e3,
+                               "effective_tops": r["ops"] / r["dt"] / 1e12,
+                               "frac_of_measured_i8_peak": r["ops"] / r["dt"] / 1e12 / best if best else None,
+                               "path": "FP6 x FP4 matrix cores" if r["mx"] else "int8 matrix cores",
+                               "gemm_tops": r["ops"] / r["gemm_s"] / 1e12, "kernel_us": r["k_us"]}
+    return res
 
 
 def main():
@@ -606,7 +750,11 @@ def main():
         return
 
     if args.workload == "block_7b":
-        print(json.dumps(run_block(args, hbl, torch)), flush=True)
+        res = run_block(args, hbl, torch)
+        if not args.no_cpu_baseline:
+            print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = block_cpu_baseline(res["config"]["bits"])
+        print(json.dumps(res), flush=True)
         return
 
     if args.workload == "msweep":

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         _lib.hbo_f32_to_bf16.argtypes = [ctypes.c_float]
         _lib.hbo_f32_to_bf16.restype = ctypes.c_uint16
         _lib.hbo_num_threads.restype = I
+        _lib.hbo_set_num_threads.argtypes = [I]
+        _lib.hbo_set_num_threads.restype = None
     return _lib
 
 
@@ -97,6 +99,11 @@ def _check(rc: int, what: str) -> None:
 
 def num_threads() -> int:
     return int(lib().hbo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops (OpenMP)."""
+    lib().hbo_set_num_threads(int(n))
 
 
 def fwht_unnormalized(v: np.ndarray) -> tuple[np.ndarray, int]:

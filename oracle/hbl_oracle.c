@@ -584,3 +584,13 @@ int hbo_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads of the calling thread's later parallel
+ * loops (used to time the oracle at one thread and at all cores). */
+void hbo_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
