@@ -53,6 +53,7 @@ _SIGS = {
     "hbl_ternary_gemm": ([_P, _I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
     "hbl_forward_workspace_size": ([_I64, _I64, _I64, _I], _SZ),
     "hbl_forward": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
+    "hbl_forward_noalloc": ([_P, _I, _I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _I64, _P], _I),
     "hbl_hadamard_backward_f32": ([_P, _I, _I64, _I64, _I64, _P, _P], _I),
     "hbl_norm_hadamard_quant": ([_P, _I, _I64, _I64, _I64, _P, _I, _I, _P, _P, _P, _P], _I),
     "hbl_norm_forward": ([_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _P, _P, _P, _I64, _P, _SZ, _P], _I),
@@ -246,6 +247,23 @@ def forward(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: in
     _check(_lib.hbl_forward(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, bits,
                             _ptr(packed), _ptr(alpha), _ptr(out), out.stride(0), _ptr(workspace),
                             workspace.numel(), _stream()), "hbl_forward")
+    return out
+
+
+NOALLOC_WORKSPACE_BYTES = 64 * 1024 * 1024
+
+
+def forward_noalloc(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, bits: int, hadamard: bool = True,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """forward() with the library's static workspace (hbl_forward_noalloc):
+    the library allocates nothing; calls that overlap on one GPU race."""
+    M, K, ldx = _rows(x)
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(_lib.hbl_forward_noalloc(_ptr(x), _x_dtype(x), M, K, ldx, N, HADAMARD if hadamard else 0, bits,
+                                    _ptr(packed), _ptr(alpha), _ptr(out), out.stride(0), _stream()),
+           "hbl_forward_noalloc")
     return out
 
 

@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libhbl.so")
 PROBE = os.path.join(HERE, "peak_probe")  # stand-alone program: measured device peaks
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["k_quant.hip", "k_ternarize.hip", "k_gemm.hip", "k_gemm_mx.hip", "k_kvquant.hip", "hbl_api.cpp"]
+SOURCES = ["k_quant.hip", "k_ternarize.hip", "k_gemm.hip", "k_gemm_mx.hip", "k_kvquant.hip", "hbl_noalloc.hip",
+           "hbl_api.cpp"]
 HEADERS = [os.path.join(CSRC, "hbl_internal.h"), os.path.join(ROOT, "include", "hbl.h")]
 
 # -ffp-contract=off: no fused multiply-adds, so every product and sum is

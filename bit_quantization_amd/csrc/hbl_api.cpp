@@ -176,6 +176,8 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, 
 
 }  // namespace
 
+int hbl::set_error(int status, const char* text) { return fail(status, "%s", text); }
+
 extern "C" {
 
 int hbl_version(void) { return 100; }

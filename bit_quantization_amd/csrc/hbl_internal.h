@@ -118,4 +118,8 @@ hipError_t launch_kv_quant(const void* x, bool x_bf16, int64_t B, int64_t S, int
 // Token counts up to this take the weight-streaming kernel.
 constexpr int kGemvMaxM = 128;
 
+// Records the detail text hbl_last_error() returns on the calling thread and
+// returns status (for entry points defined outside hbl_api.cpp).
+int set_error(int status, const char* text);
+
 }  // namespace hbl

@@ -248,6 +248,30 @@ int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                 size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
+ * hbl_forward_noalloc -- hbl_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, arguments and result
+ * as hbl_forward, without the workspace: the library's own static device
+ * array of HBL_NOALLOC_WORKSPACE_BYTES (64 MiB) serves as the workspace.
+ * Each GPU the library runs on holds its own copy of that array until the
+ * process ends; its device address is looked up on the first call made with
+ * the device current (hipGetSymbolAddress; no allocation, no
+ * synchronisation).  The call itself allocates nothing.
+ * Limit: hbl_forward_workspace_size(M, N, K, bits) <= 64 MiB, else
+ * HBL_ERR_WORKSPACE (e.g. M = 2048 at K = 16384 in INT8 needs more).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or threads) race and must be serialised by the
+ * caller.  Calls on one stream are ordered and safe.  Nothing in the array
+ * needs to start at zero: every byte a call reads was written by the same
+ * call.
+ * ------------------------------------------------------------------- */
+#define HBL_NOALLOC_WORKSPACE_BYTES (64 * 1024 * 1024)
+int hbl_forward_noalloc(const void* x, int x_dtype, int64_t M, int64_t K,
+                        int64_t ldx, int64_t N, int flags, int bits,
+                        const uint32_t* w_packed, const float* alpha, void* y,
+                        int64_t ldy, void* stream);
+
+/* ---------------------------------------------------------------------
  * hbl_norm_forward -- the whole layer of Eq. 9 with its normalisation:
  * hbl_norm_hadamard_quant(x, gain, flags, bits) then hbl_ternary_gemm.
  * Arguments as hbl_forward plus gain (as hbl_norm_hadamard_quant); the
