@@ -428,7 +428,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
         brows > 0 ? (int)(brows * brow_bytes - kb) : 0, 0x00020000);
   };
   // loads of stage (dr, dk) into buffer I; advances the cursor
-  auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
+  auto stage_load = [&]<int I, bool SW = true>(std::integral_constant<int, I> bi, std::bool_constant<SW> = {}) {
     uint8_t* const Ad = abuf(bi);
     uint8_t* const Bd = bbuf(bi);
     const bool live = dr < ntiles;
@@ -444,9 +444,12 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
       for (int j = 0; j < BDMA; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
     }
-    if (++dk == nks) {
-      dk = 0;
-      set_tile(++dr);
+    ++dk;
+    if constexpr (SW) {
+      if (dk == nks) {
+        dk = 0;
+        set_tile(++dr);
+      }
     }
   };
 
@@ -661,11 +664,14 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     mfmas(d1);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
     bar();
-    stage_load(std::integral_constant<int, Q>{});
+    // nks is a multiple of NST and the loads run NST stages ahead, so the
+    // load cursor reaches the end of a tile only in the group's last body
+    stage_load(std::integral_constant<int, Q>{}, std::bool_constant<Q == NST - 1>{});
     read_head(nxt, std::integral_constant<int, (Q + 1) % NST>{});
     decode(d1, cur.b, tl.a, 3);
     mfmas(d0);
     mfmas(d1);
+    __builtin_amdgcn_iglp_opt(0);
   };
   const int groups_per_tile = nks / NST;
   for (int r = 0; r < ntiles; ++r) {

@@ -206,7 +206,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
         const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + n0 * brow_bytes + kb), (short)0,
         r < ntiles ? (int)(brows * brow_bytes - kb) : 0, 0x00020000);
   };
-  auto stage_load = [&]<int I>(std::integral_constant<int, I> bi) {
+  auto stage_load = [&]<int I, bool SW = true>(std::integral_constant<int, I> bi, std::bool_constant<SW> = {}) {
     uint8_t* const Md = mbuf(bi);
     uint8_t* const Td = tbuf(bi);
     uint8_t* const Bd = bbuf(bi);
@@ -233,9 +233,12 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * (NW / 4) * wblk, 0, 0,
                                                  0);
     }
-    if (++dk == nks) {
-      dk = 0;
-      set_tile(++dr);
+    ++dk;
+    if constexpr (SW) {
+      if (dk == nks) {
+        dk = 0;
+        set_tile(++dr);
+      }
     }
   };
 
@@ -431,10 +434,22 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     decw(wf1, cur.w, 1);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
     bar();
-    stage_load(std::integral_constant<int, Q>{});
+    // nks is a multiple of NST and the loads run NST stages ahead, so the
+    // load cursor reaches the end of a tile only in the group's last body
+    stage_load(std::integral_constant<int, Q>{}, std::bool_constant<Q == NST - 1>{});
     read_frag(nxt, std::integral_constant<int, (Q + 1) % NST>{});
     step(wf1, cur.c1);
     decw(wf0, nxt.w, 0);
+    if constexpr (Q != NST - 1) {
+      // the next stage's fragment reads spread over this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, DPS, 0);
+#pragma unroll
+      for (int g = 0; g < (FM * 4 + FN + 1) / 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * FM * FN - (FM * 4 + FN + 1) / 2, 0);
+    }
   };
   const int groups_per_tile = nks / NST;
   for (int r = 0; r < ntiles; ++r) {
