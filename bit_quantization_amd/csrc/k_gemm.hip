@@ -693,13 +693,13 @@ constexpr int kGemvBatch = 8;  // 16-byte weight loads in flight per lane
 // MG groups of 16 tokens (M <= 16 MG): every block streams its 16 features'
 // weights once and applies each decoded weight fragment to all token groups,
 // whose codes are read from the L2 (every block reads all of them).
-template <int BITS, int OUT, int MG>
-__global__ void __launch_bounds__(256)
+template <int BITS, int OUT, int MG, int NWV = 8, int BATCH = 4>
+__global__ void __launch_bounds__(64 * NWV)
 k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
        const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
        const float* __restrict__ alpha, int M, int64_t N, int64_t K,
        void* __restrict__ out, int64_t ldo) {
-  __shared__ v4i red[MG][3][64];
+  __shared__ v4i red[MG][NWV - 1][64];
   // One group of tokens: each step's codes (16 tokens x RB bytes: 256 for
   // INT8, 128 for INT4) are copied into the wave's LDS area by direct-to-LDS
   // loads in which RB / 16 consecutive lanes read one token's RB bytes, then
@@ -711,7 +711,7 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   constexpr bool XLDS = MG == 1;
   constexpr int RB = BITS == 8 ? 256 : 128, XU = RB / 16, TPL = 1024 / RB;
   auto xswz = [](int t) { return BITS == 8 ? t : (t >> 1) & 7; };
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[XLDS ? 4 * kGemvBatch * 16 * RB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XLDS ? NWV * BATCH * 16 * RB : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int fr = lane % 16, g = lane / 16;
@@ -730,11 +730,11 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   __amdgpu_buffer_rsrc_t rX;
   if constexpr (XLDS)
     rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(codes), (short)0, (int)(M * K * BITS / 8), 0x00020000);
-  for (int64_t s0 = wave; s0 < steps; s0 += 4 * kGemvBatch) {
-    uint4 w[kGemvBatch];
+  for (int64_t s0 = wave; s0 < steps; s0 += NWV * BATCH) {
+    uint4 w[BATCH];
 #pragma unroll
-    for (int b = 0; b < kGemvBatch; ++b) {
-      const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+    for (int b = 0; b < BATCH; ++b) {
+      const int64_t st = s0 + NWV * b, ps = st + rot < steps ? st + rot : st + rot - steps;
       const int64_t kw = ps * 16 + 4 * g;
       w[b] = (st < steps && kw < KW) ? load_stream(wrow + kw) : make_uint4(0, 0, 0, 0);
     }
@@ -743,10 +743,10 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int t0 = lane / XU, q = lane % XU;
 #pragma unroll
-      for (int b = 0; b < kGemvBatch; ++b) {
-        const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+      for (int b = 0; b < BATCH; ++b) {
+        const int64_t st = s0 + NWV * b, ps = st + rot < steps ? st + rot : st + rot - steps;
         if (st >= steps) break;  // wave-uniform
-        uint8_t* dst = xs + (wave * kGemvBatch + b) * 16 * RB;
+        uint8_t* dst = xs + (wave * BATCH + b) * 16 * RB;
 #pragma unroll
         for (int j = 0; j < 16 / TPL; ++j) {
           // TPL tokens per load; groups wholly past M are not loaded (their
@@ -761,12 +761,12 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the batch's weights and codes
     }
 #pragma unroll
-    for (int b = 0; b < kGemvBatch; ++b) {
-      const int64_t st = s0 + 4 * b, ps = st + rot < steps ? st + rot : st + rot - steps;
+    for (int b = 0; b < BATCH; ++b) {
+      const int64_t st = s0 + NWV * b, ps = st + rot < steps ? st + rot : st + rot - steps;
       const int64_t kw = ps * 16 + 4 * g;
       // Skip only whole steps (a wave-uniform test): an MFMA always runs on
       // all 64 lanes, so lanes past the end of K feed zeros instead.
-      if (s0 + 4 * b >= steps) continue;
+      if (s0 + NWV * b >= steps) continue;
       const uint32_t ws[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
       v4i a[4];
 #pragma unroll
@@ -780,7 +780,7 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
         // activation codes for k = 16*kw .. 16*kw + 63 of token tok
         uint32_t x[16];
         if constexpr (XLDS) {
-          const uint8_t* row = xs + (wave * kGemvBatch + b) * 16 * RB + fr * RB;
+          const uint8_t* row = xs + (wave * BATCH + b) * 16 * RB + fr * RB;
           if constexpr (BITS == 8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -841,13 +841,30 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
     for (int tg = 0; tg < MG; ++tg) {
       v4i t = acc[tg];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) t += red[tg][i][lane];
+      for (int i = 0; i < NWV - 1; ++i) t += red[tg][i][lane];
       const int tok = 16 * tg + fr;
       if (tok < M) {
         const float sc = scales[tok] * *alpha;
         store4<OUT>(out, tok * ldo + n0 + 4 * g, t, rowsum[tok], sc);
       }
     }
+  }
+}
+
+// Value of the partner lane in an xor-butterfly sum over lane distances o =
+// 1, 2, 4, ... taken in that order: 1 and 2 are quad permutations; 4 and 8
+// the half-row and row mirrors (lane i <-> 7 - i, 15 - i), which pair each
+// lane with the other half of its group, the same sum as l ^ o once the
+// earlier steps have made every 4- (8-) lane group hold one value; 16 and 32
+// through the LDS crossbar.  Integer sums: any pairing order gives the same
+// result.
+__device__ __forceinline__ int lane_sum_partner(int v, int o) {
+  switch (o) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    case 8: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    default: return __shfl_xor(v, o);
   }
 }
 
@@ -974,7 +991,7 @@ k_gemv_dot(const void* __restrict__ codes, const float* __restrict__ scales,
     for (int m = 0; m < MT; ++m) {
       int v = acc[i][m];
 #pragma unroll
-      for (int o = 1; o < lanes_per_row; o <<= 1) v += __shfl_xor(v, o);
+      for (int o = 1; o < lanes_per_row; o <<= 1) v += lane_sum_partner(v, o);
       acc[i][m] = v;
     }
   }
@@ -1115,7 +1132,7 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
     // block per 16 features) where the matrix-core tiles would leave most
     // of them idle
 #define HBL_GV(MG)                                                                                              \
-  hipLaunchKernelGGL((k_gemv<BITS, OUT, MG>), dim3((unsigned)(N / 16)), dim3(256), 0, s, codes, scales, rowsum, wp, \
+  hipLaunchKernelGGL((k_gemv<BITS, OUT, MG>), dim3((unsigned)(N / 16)), dim3(512), 0, s, codes, scales, rowsum, wp, \
                      alpha, (int)M, N, K, out, ldo)
     // (one group stages its codes by buffer loads, whose range is 16 K BITS / 8
     // bytes < 2^31; longer rows take the two-group kernel)
