@@ -805,6 +805,128 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
   for (; grp < ngroups; grp += S) row_group(raw0, grp, grp + S);
 }
 
+// Few-token form of the rotation + INT8 quantisation (decode): one token row
+// per block of K / 16 threads (16 waves at K = 16384), 16 elements per
+// thread, so that the row's latency chain is spread over 4 waves per SIMD
+// instead of one.  K = 2^k, k = 10 ... 14; bf16 input.
+//   pass 1: wave w holds elements 1024 w .. + 1023, 16 chunks of 64; the
+//           64-point transforms of its chunks run on the matrix cores as
+//           Y = H_64 X with v_mfma_f32_16x16x32_bf16 (X: 64 elements x 16
+//           chunks, two k-steps of 32; the bf16 inputs and +-1 entries are
+//           exact, the sums fp32).  Lane l then holds elements 16 rb +
+//           4 (l / 16) + j of chunk l % 16 (rb, j = 0..3): bits 0-5 done.
+//   pass 2: through LDS (16-byte unit u of a wave's 1024-element area at
+//           16 (u / 16) + ((u % 16) ^ (u / 16))), lane l takes element bits
+//           0-5 = l and the 16 chunks: bits 6-9 in registers.
+//   pass 3: back through LDS, thread t takes bits 10 .. k-1 (the waves)
+//           and 16 / 2^(k-10) consecutive passengers: the last k - 10 stages.
+// Then the row maximum, the codes by one fma against 1.5 * 2^23 (as the
+// row-group kernel), and the codes through LDS in natural order for
+// contiguous 16-byte stores.
+template <int LOG2K>
+__global__ void __launch_bounds__((1 << LOG2K) / 16)
+k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ codes, float* __restrict__ scales,
+                 int32_t* __restrict__ rowsum) {
+  constexpr int K = 1 << LOG2K, TR = K / 16, WB = LOG2K - 10, NWV = 1 << WB;
+  constexpr int PB = 4 - WB, P = 1 << PB;  // passengers of pass 3
+  __shared__ __attribute__((aligned(16))) float L[K];
+  __shared__ float redf[NWV];
+  __shared__ int redi[NWV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m = blockIdx.x;
+  const __bf16* xr = reinterpret_cast<const __bf16*>(x) + m * ldx;
+  const int cc = lane & 15, g = lane >> 4;
+
+  // pass 1: B operand of k-step ks = 8 consecutive inputs of chunk cc
+  v8bf bx[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    bx[ks] = *reinterpret_cast<const v8bf*>(xr + 1024 * wave + 64 * cc + 32 * ks + 8 * g);
+  // A operand (rb, ks): rows 16 rb + i of H_64 (i = l % 16), columns 32 ks +
+  // kk (kk = 8 (l / 16) + e, e = 0..7).  The row and column bits split into
+  // disjoint parts, so H_64[16 rb + i][32 ks + kk] = (-1)^popcount(i & kk) *
+  // (-1)^((rb & 1) (kk >> 4)) * (-1)^((rb >> 1) ks), and kk >> 4 = (l / 16) / 2
+  // is the lane's: one base operand per lane, the others its sign flips.
+  uint32_t hb[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    uint32_t h2 = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int kk = 8 * g + 2 * pp + half;
+      h2 |= ((__popc(cc & kk) & 1) ? 0xbf80u : 0x3f80u) << (16 * half);
+    }
+    hb[pp] = h2;
+  }
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f c[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    c[rb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t neg = ((((rb & 1) & (g >> 1)) ^ ((rb >> 1) & ks)) != 0) ? 0x80008000u : 0u;
+      const v8bf ha = __builtin_bit_cast(v8bf, make_uint4(hb[0] ^ neg, hb[1] ^ neg, hb[2] ^ neg, hb[3] ^ neg));
+      c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, bx[ks], c[rb], 0, 0, 0);
+    }
+  }
+  float* Lw = L + 1024 * wave;
+  auto unit = [](int u) { return 16 * (u >> 4) + ((u & 15) ^ (u >> 4)); };
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    *reinterpret_cast<float4*>(Lw + 4 * unit(16 * cc + 4 * rb + g)) = make_float4(c[rb][0], c[rb][1], c[rb][2], c[rb][3]);
+  __syncthreads();
+  // pass 2: element bits 0-5 = lane, bits 6-9 = register index
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = Lw[4 * unit(16 * q + (lane >> 2)) + (lane & 3)];
+  butterflies<16, 0, 4>(v);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) Lw[4 * unit(16 * q + (lane >> 2)) + (lane & 3)] = v[q];
+  __syncthreads();
+  // pass 3: register i = p + P w', element 1024 w' + P t + p
+#pragma unroll
+  for (int wv = 0; wv < NWV; ++wv)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int f = P * tid + p;
+      v[p + P * wv] = L[1024 * wv + 4 * unit(f >> 2) + (f & 3)];
+    }
+  butterflies<16, PB, 4>(v);
+
+  // INT8 absmax (Eq. 7) of the rotated row x_r = c v
+  constexpr float scale = (LOG2K % 2 == 0) ? (float)(1.0 / (double)(1 << (LOG2K / 2))) : 0.0f;
+  const float cn = (LOG2K % 2 == 0) ? scale : (float)(1.0 / __builtin_sqrt((double)K));
+  float st = abs_tree<16, true>(v);
+  st = row_reduce<TR, true>(st, redf, 0, tid);
+  const float gamma = st * cn;
+  const float f = 127.0f / (gamma + kEps);
+  const float fc = cn * f;
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  constexpr int kMagicBits = 0x4b400000;
+  __syncthreads();  // every thread's pass-3 reads are done: L takes the codes
+  int8_t* C8 = reinterpret_cast<int8_t*>(L);
+#pragma unroll
+  for (int wv = 0; wv < NWV; ++wv)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int bits = __float_as_int(__builtin_fmaf(v[p + P * wv], fc, kMagic));
+      C8[1024 * wv + P * tid + p] = (int8_t)(min(max(bits, kMagicBits - 128), kMagicBits + 127) - kMagicBits);
+    }
+  __syncthreads();
+  const uint4 q4 = *reinterpret_cast<const uint4*>(C8 + 16 * tid);
+  *reinterpret_cast<uint4*>(codes + m * (int64_t)K + 16 * tid) = q4;
+  int qs = __builtin_amdgcn_sdot4((int)q4.x, 0x01010101, 0, false);
+  qs = __builtin_amdgcn_sdot4((int)q4.y, 0x01010101, qs, false);
+  qs = __builtin_amdgcn_sdot4((int)q4.z, 0x01010101, qs, false);
+  qs = __builtin_amdgcn_sdot4((int)q4.w, 0x01010101, qs, false);
+  qs = row_reduce_int<TR>(qs, redi, 0, tid);
+  if (tid == 0) {
+    scales[m] = gamma / 127.0f;
+    if (rowsum) rowsum[m] = qs;
+  }
+}
+
 // Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
 // per block of 256 threads, each holding up to 8 chunks of 8 elements.
 template <bool BF16, int BITS, bool NORM>
@@ -884,6 +1006,14 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
   }
 }
 
+// Token counts up to this take k_fwht_quant_row (INT8 codes with the
+// rotation, bf16 input): measured on MI355X against the row-group kernel
+// (us per call, graph replay): K = 16384 M = 1 5.37 -> 4.98, M = 256 8.10 ->
+// 7.63, M = 512 10.63 -> 10.89 (slower); K = 4096 M = 1 4.03 -> 2.90, M =
+// 1024 7.47 -> 6.81; K = 8192 M = 256 6.71 -> 4.91.
+template <int LOG2K>
+constexpr int64_t kRowKernelMaxM = LOG2K >= 14 ? 256 : 1024;
+
 // Block size: rows of K <= 4096 (a wave or less per row) run in blocks of
 // 64 threads (codes; up to 8 blocks per CU) or 128 (MX6 codes; up to 4 per
 // CU), which need no barrier across rows; measured at K = 4096 against 256
@@ -935,6 +1065,14 @@ hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool
                           hipStream_t s) {
   if constexpr (!NORM)  // MX6 codes are written without the normalisation layer
     if (bits == 6) return dispatch_quant_mx<LOG2K, NORM>(x, bf16, M, ldx, had, codes, scales, rowsum, gain, cu, s);
+  if constexpr (!NORM && LOG2K >= 10) {
+    // few rows of INT8 codes: one row per block of K / 16 threads
+    if (bits == 8 && bf16 && had && M <= kRowKernelMaxM<LOG2K>) {
+      hipLaunchKernelGGL((k_fwht_quant_row<LOG2K>), dim3((unsigned)M), dim3((1 << LOG2K) / 16), 0, s, x, ldx,
+                         static_cast<int8_t*>(codes), scales, rowsum);
+      return hipGetLastError();
+    }
+  }
 #define HBL_FQ(B16, BITS, HAD)                                                                              \
   if constexpr (LOG2K >= 10)                                                                                \
     return launch_fq64<LOG2K, B16, BITS, HAD, 0, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, cu, \
