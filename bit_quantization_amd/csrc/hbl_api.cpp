@@ -78,6 +78,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t ldo) {
     return fail(HBL_ERR_SHAPE, "K = %lld must be a multiple of 64 in [64, %d]", (long long)K, HBL_MAX_GEMM_K);
   if (ldo < N) return fail(HBL_ERR_SHAPE, "ldo = %lld < N = %lld", (long long)ldo, (long long)N);
   if (ldo % 4 != 0) return fail(HBL_ERR_ALIGN, "ldo = %lld is not a multiple of 4", (long long)ldo);
+  if (ldo > HBL_MAX_LDO) return fail(HBL_ERR_SHAPE, "ldo = %lld exceeds %d", (long long)ldo, HBL_MAX_LDO);
   // token rows are addressed with 64-bit offsets; the grid size is the limit
   if ((M + 127) / 128 * ((N + 127) / 128) > (int64_t)INT_MAX)
     return fail(HBL_ERR_SHAPE, "M x N is too large for one launch");

@@ -48,6 +48,15 @@
 // (a fence would also wait for the prefetch in flight); each wave has waited
 // for its own loads of the next stage first.
 //
+// Output of bf16 tiles: every block finishes its tiles at about the same
+// time, so the stores come in bursts.  Each wave writes its fragments to
+// its own LDS area and stores whole 128-byte row pieces from there (16
+// bytes per lane; rows or features outside the matrix take an offset past
+// the buffer range and are dropped, so the number of stores is fixed), and
+// the next tile's first stages do not wait for those stores: their load
+// waits count them (vmcnt retires in issue order), so only the fourth
+// stage of the next tile waits for them.
+//
 // Fragment layout (32x32x64, measured on the device): lane l of an operand
 // holds row l % 32 and the 32 k's 32 (l / 32) .. + 31 of the MFMA step,
 // as consecutive 6-bit (codes) or 4-bit (weights) fields; in the
@@ -74,12 +83,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest even (the same rounding as the int8 path)
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values to packed bf16 (first in the low half), round to nearest
+// even: gfx950's v_cvt_pk_bf16_f32, one instruction for both.  For the
+// finite values the epilogues produce this is the same rounding as adding
+// 0x7fff plus the lowest kept bit and truncating.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
 }
 
 // four consecutive features of one token: acc holds exact integers
@@ -90,13 +104,15 @@ __device__ __forceinline__ void store4f(void* out, int64_t idx, float a0, float 
   } else if constexpr (OUT == 1) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = make_float4(sc * a0, sc * a1, sc * a2, sc * a3);
   } else {
-    const uint32_t lo = bf16_rne(sc * a0) | (bf16_rne(sc * a1) << 16);
-    const uint32_t hi = bf16_rne(sc * a2) | (bf16_rne(sc * a3) << 16);
+    const uint32_t lo = pk_bf16(sc * a0, sc * a1);
+    const uint32_t hi = pk_bf16(sc * a2, sc * a3);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = make_uint2(lo, hi);
   }
 }
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+
 
 template <int OUT, int BM, int BN, int NWV>
 __global__ void __launch_bounds__(64 * NWV, 1)
@@ -135,7 +151,11 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // bf16 outputs of 256 x 128 tiles are staged through LDS (whole-row stores)
   constexpr int OROW = WN * 2 + 16;
   constexpr bool STAGE_OUT = OUT == 0 && WN == 64 && NST * (MSZ + TSZ + BSZ) + NW * 32 * OROW <= 160 * 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : 16];
+  // 256 x 256 tiles stage them by halves of the wave's 128 features: 32 rows
+  // x 64 features (128 bytes, 16-byte units XOR-swizzled by row) per wave,
+  // the 32 KB of LDS the four stage buffers leave
+  constexpr bool STAGE_HALF = OUT == 0 && WN == 128 && NST * (MSZ + TSZ + BSZ) + NW * 32 * 128 <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t Os[STAGE_OUT ? NW * 32 * OROW : (STAGE_HALF ? NW * 32 * 128 : 16)];
   auto mbuf = [&]<int I>(std::integral_constant<int, I>) -> uint8_t* {
     if constexpr (I == 0) return Am0; else if constexpr (I == 1) return Am1; else if constexpr (I == 2) return Am2; else return Am3;
   };
@@ -364,8 +384,8 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const v16f& a = acc[i][j];
-            const uint32_t lo = bf16_rne(sc * a[4 * q]) | (bf16_rne(sc * a[4 * q + 1]) << 16);
-            const uint32_t hi = bf16_rne(sc * a[4 * q + 2]) | (bf16_rne(sc * a[4 * q + 3]) << 16);
+            const uint32_t lo = pk_bf16(sc * a[4 * q], sc * a[4 * q + 1]);
+            const uint32_t hi = pk_bf16(sc * a[4 * q + 2], sc * a[4 * q + 3]);
             *reinterpret_cast<uint2*>(Ow + fr * OROW + 2 * (32 * i + 8 * q + 4 * h)) = make_uint2(lo, hi);
           }
           __builtin_amdgcn_sched_barrier(0);  // one fragment's values live at a time
@@ -388,6 +408,52 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next row's writes
         __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (STAGE_HALF) {
+      // per fragment row and half of the wave's features: the fragments'
+      // 8-byte pieces go to the wave's own [32][64] bf16 area (unit u of
+      // row r at u ^ (r % 8)), then each lane stores 16 bytes: a store
+      // instruction writes 8 whole 128-byte rows
+      uint8_t* const Ow = Os + wave * 32 * 128;
+      const bool wide = (ldo & 7) == 0;
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * WM + 32 * j + fr;
+        const float sc = m < M ? scales[m] * al : 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const v16f& a = acc[2 * half + ii][j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t lo = pk_bf16(sc * a[4 * q], sc * a[4 * q + 1]);
+              const uint32_t hi = pk_bf16(sc * a[4 * q + 2], sc * a[4 * q + 3]);
+              *reinterpret_cast<uint2*>(Ow + fr * 128 + 16 * ((4 * ii + q) ^ (fr & 7)) + 8 * h) = make_uint2(lo, hi);
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the area is the wave's own: no barrier
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            // 8 rows per store; lanes outside the matrix take an offset
+            // past the range (dropped), so every store is issued
+            const int rl = (fr >> 3) + 4 * h, u = fr & 7, row = rl + 8 * pp;
+            const int64_t mr = m0 + wm * WM + 32 * j + 8 * pp, nc = n0 + wn * WN + 64 * half;
+            const uint4 v = *reinterpret_cast<const uint4*>(Ow + row * 128 + 16 * (u ^ (row & 7)));
+            const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<uint16_t*>(out) + mr * ldo + nc, (short)0, 0x7fffffff, 0x00020000);
+            const bool ok = mr + rl < M && nc + 8 * u < N;
+            const uint32_t off = ok ? (uint32_t)(rl * ldo + 8 * u) * 2u : kOut;
+            if (wide) {
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, rO, (int)off, 0, 0);
+            } else {  // rows 8-byte aligned: two stores (more in flight than EPI_STORES: waits only lengthen)
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, rO, (int)off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.z, v.w}, rO, (int)(off + 8u), 0, 0);
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half's writes
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else {
 #pragma unroll
@@ -427,12 +493,19 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // Stage Q of a group of NST: buffer Q, fragments f0 / f1 by parity.  The
   // weight operands of the next step are formed while a step's MFMAs run
   // (an MFMA whose operand was just written by the VALU waits for it).
-  auto body = [&]<int Q>(std::integral_constant<int, Q>) {
+  // A staged epilogue leaves EPI_STORES stores per wave in flight.  In
+  // the next tile's first group, the stage loads a body waits for were
+  // issued before them in its first NST - 1 bodies: those bodies let them
+  // run on while the tile's MFMAs start (counts retire in issue order).
+  constexpr int EPI_STORES = STAGE_HALF ? FM * 2 * 4 : 0;
+  auto body = [&]<int Q, bool AFTER = false>(std::integral_constant<int, Q>, std::bool_constant<AFTER> = {}) {
     Frag& cur = (Q % 2 == 0) ? f0 : f1;
     Frag& nxt = (Q % 2 == 0) ? f1 : f0;
     step(wf0, cur.c0);
     decw(wf1, cur.w, 1);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * DPS) : "memory");
+    constexpr int inflight = (NST - 2) * DPS + (AFTER && Q < NST - 1 ? EPI_STORES : 0);
+    static_assert(inflight <= 63, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(inflight) : "memory");
     bar();
     // nks is a multiple of NST and the loads run NST stages ahead, so the
     // load cursor reaches the end of a tile only in the group's last body
@@ -452,8 +525,24 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     }
   };
   const int groups_per_tile = nks / NST;
+  if constexpr (EPI_STORES > 0) {
+    // the first tile starts as every later one: EPI_STORES stores issued
+    // after its first stages' loads (an empty range: all dropped)
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, 0, 0x00020000);
+#pragma unroll
+    for (int e = 0; e < EPI_STORES; ++e) __builtin_amdgcn_raw_buffer_store_b128(v4u{0u, 0u, 0u, 0u}, rz, 16 * e, 0, 0);
+  }
   for (int r = 0; r < ntiles; ++r) {
-    for (int gq = 0; gq < groups_per_tile; ++gq) {
+    int gq = 0;
+    if constexpr (EPI_STORES > 0) {
+      if (r > 0) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (body(std::integral_constant<int, I>{}, std::true_type{}), ...);
+        }(std::make_integer_sequence<int, NST>{});
+        gq = 1;
+      }
+    }
+    for (; gq < groups_per_tile; ++gq) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (body(std::integral_constant<int, I>{}), ...);
       }(std::make_integer_sequence<int, NST>{});

@@ -90,6 +90,11 @@ extern "C" {
  * byte offsets of its 256-row tiles stay in range as well. */
 #define HBL_MAX_GEMM_K 2097152
 
+/* Largest output row stride (elements) of the matmul entry points: 2^27.
+ * The tile kernels address the rows of one store (up to 8 rows) with
+ * 32-bit byte offsets. */
+#define HBL_MAX_LDO 134217728
+
 /* Library version, major*10000 + minor*100 + patch. */
 int hbl_version(void);
 
@@ -216,7 +221,7 @@ int hbl_norm_hadamard_quant(const void* x, int x_dtype, int64_t M, int64_t K,
  * w_packed, alpha:     as written by hbl_ternarize_weights.
  * out_dtype: HBL_OUT_BF16 or HBL_OUT_F32 write the rescaled value;
  *            HBL_OUT_I32 writes acc itself (for exact checks).
- * out: [M][ldo] of out_dtype; ldo >= N, ldo % 4 == 0.
+ * out: [M][ldo] of out_dtype; ldo >= N, ldo % 4 == 0, ldo <= HBL_MAX_LDO.
  * Shapes: N >= 16, N % 16 == 0, K >= 64, K % 64 == 0, K <= HBL_MAX_GEMM_K.
  * Token counts M <= 128 take a kernel that streams the weights once (one
  * block per 16 output features, the tokens in groups of 16); larger M take

@@ -120,6 +120,17 @@ def test_gemm_k_bound(hbl, K, expect):
         assert "K =" in last(hbl)
 
 
+@pytest.mark.parametrize("ldo,expect", [((1 << 27), 0), ((1 << 27) + 4, 2)])
+def test_gemm_ldo_bound(hbl, ldo, expect):
+    # ldo <= 2^27 (HBL_MAX_LDO): the tile kernels address the rows of one
+    # store with 32-bit byte offsets; M = 0, so nothing is enqueued
+    lib = hbl.lib()
+    assert lib.hbl_ternary_gemm(A, 8, B, C, D, E, 0, 64, 256, 0, F, ldo, None) == expect
+    assert lib.hbl_ternary_gemm_mx(A, B, D, E, 0, 64, 512, 0, F, ldo, None) == expect
+    if expect:
+        assert "ldo =" in last(hbl)
+
+
 def test_forward_workspace(hbl):
     lib = hbl.lib()
     need = lib.hbl_forward_workspace_size(10, 64, 256, 4)

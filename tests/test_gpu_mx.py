@@ -125,6 +125,26 @@ def test_gemm_mx_full_tile_grid_exact(hbl):
     assert np.abs(gq.astype(int) - oracle.unpack_int4(oq, K).astype(int)).max() <= 1
 
 
+# bf16 output of the 256 x 256 tiles (at least one tile per CU): 33 x 9 =
+# 297 tiles, so some blocks run two (the second tile's first stages start
+# while the first tile's stores drain); ragged M and N; contiguous rows,
+# 16-byte aligned strided rows (pad 8) and 8-byte aligned ones (pad 4).
+# Every element against the int8 path, which has its own oracle parity.
+@pytest.mark.parametrize("pad", [0, 8, 4])
+def test_gemm_mx_bf16_wide_tiles(hbl, pad):
+    M, N, K = 33 * 256 - 179, 8 * 256 + 16, 1024
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= torch.cuda.get_device_properties(0).multi_processor_count
+    x = to_device(workloads.random_rows(51, M, K, "t3"))
+    _, packed, alpha, wq = _weights(hbl, N, K, 10)
+    cm, sm = hbl.hadamard_quant_mx(x)
+    q4, s4, r4 = hbl.hadamard_quant(x, 4)
+    ref = hbl.ternary_gemm(q4, 4, s4, r4, packed, alpha, K)
+    big = torch.full((M, N + pad), 5, dtype=torch.bfloat16, device="cuda")
+    hbl.ternary_gemm_mx(cm, sm, wq, alpha, K, out=big[:, :N])
+    assert torch.equal(big[:, :N].contiguous().view(torch.int16), ref.view(torch.int16))
+    assert torch.all(big[:, N:] == 5)
+
+
 # (M, N, K) -> slices: (1, 4096, 16384) 8, (100, 272, 4096) 4, (256, 4096,
 # 16384) 8, (300, 528, 8192) 8, (768, 4096, 4096) 2 (int16 partial sums);
 # (200, 4224, 16384) 4 (slices of 4096: fp32 partial sums)
