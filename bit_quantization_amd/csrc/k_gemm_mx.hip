@@ -52,10 +52,10 @@
 // time, so the stores come in bursts.  Each wave writes its fragments to
 // its own LDS area and stores whole 128-byte row pieces from there (16
 // bytes per lane; rows or features outside the matrix take an offset past
-// the buffer range and are dropped, so the number of stores is fixed), and
-// the next tile's first stages do not wait for those stores: their load
-// waits count them (vmcnt retires in issue order), so only the fourth
-// stage of the next tile waits for them.
+// the buffer range and are dropped, so the number of stores is fixed; the
+// stores are non-temporal), and the next tile's first stages do not wait
+// for those stores: their load waits count them (vmcnt retires in issue
+// order), so only the fourth stage of the next tile waits for them.
 //
 // Fragment layout (32x32x64, measured on the device): lane l of an operand
 // holds row l % 32 and the 32 k's 32 (l / 32) .. + 31 of the MFMA step,
@@ -201,7 +201,8 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // (half loads: unit 32 w + l of the one block, lanes l < 32)
   const uint32_t wb0 = BHALF ? 16u * (uint32_t)(32 * wave + (lane & 31))
                              : (uint32_t)((64 * wave + lane) / 256) * wblk + 16u * (uint32_t)((64 * wave + lane) % 256);
-  constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero
+  constexpr uint32_t kOut = 0x80000000u;  // beyond any buffer range: reads zero, stores dropped
+  constexpr int kNT = 2;                  // buffer store cache policy: non-temporal
 
   int dr = 0, dk = 0;  // load cursor: tile dr of this block, stage dk
   uint32_t amo = 0, ato = 16384;  // offsets of the tile's main and tail areas in a stage image
@@ -444,11 +445,14 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
                 reinterpret_cast<uint16_t*>(out) + mr * ldo + nc, (short)0, 0x7fffffff, 0x00020000);
             const bool ok = mr + rl < M && nc + 8 * u < N;
             const uint32_t off = ok ? (uint32_t)(rl * ldo + 8 * u) * 2u : kOut;
+            // non-temporal (cache policy bit 1, "nt"): a round of tiles writes
+            // about an L2's worth of outputs per XCD, which would otherwise
+            // displace the code and weight rows the next tiles read again
             if (wide) {
-              __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, rO, (int)off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, rO, (int)off, 0, kNT);
             } else {  // rows 8-byte aligned: two stores (more in flight than EPI_STORES: waits only lengthen)
-              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, rO, (int)off, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.z, v.w}, rO, (int)(off + 8u), 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, rO, (int)off, 0, kNT);
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{v.z, v.w}, rO, (int)(off + 8u), 0, kNT);
             }
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half's writes
