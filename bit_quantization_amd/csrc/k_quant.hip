@@ -453,6 +453,18 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
   // the matrix-core first pass needs the bf16 inputs themselves as operands;
   // normalised rows take the register path
   constexpr bool MFMA1 = BF16 && HAD && !NORM;
+  // bf16 rows without the rotation: lane t takes the 16-byte units t + T q
+  // (8 elements each) of its row, so that every load instruction reads
+  // consecutive bytes (and the INT8 / INT4 code stores write them).  INT8
+  // (a maximum: the order of the elements changes no bits) for every K;
+  // INT4 and MX6 codes (a sum, in the same order for both, so that the two
+  // layouts keep identical codes) for K = 4096 and 8192, where a row spans
+  // whole waves.  The four units of a group of 32 MX6 codes then lie in four
+  // consecutive lanes of one wave: the codes go through a wave-private LDS
+  // area as bytes to gather each group.  (At K = 16384 the MX6 form measured
+  // slower this way: the rows keep 64 contiguous elements per lane there.)
+  constexpr bool SPREAD = BF16 && !HAD && !NORM && OUT != 1 && (BITS == 8 || T == 64 || T == 128);
+  __shared__ __attribute__((aligned(16))) uint8_t cb[SPREAD && OUT == 2 ? (BS / 64) * 4096 : 16];
   __shared__ __attribute__((aligned(16))) float lds[RPB * K];
   __shared__ float redf[RPB * (T > 64 ? T / 64 : 1)];
   __shared__ int redi[RPB * (T > 64 ? T / 64 : 1)];
@@ -510,6 +522,14 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 #pragma unroll
         for (int st = 0; st < 4; ++st) raw[4 * cg + st] = live ? src[2 * st] : make_uint4(0, 0, 0, 0);
       }
+    } else if constexpr (SPREAD) {
+      // 16-byte unit t + T q of the row: each load instruction reads
+      // consecutive bytes
+      const int64_t m = grp * RPB + row;
+      const bool live = grp < ngroups && m < M;
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + (live ? m : 0) * ldx * ESZ);
+#pragma unroll
+      for (int q = 0; q < NL; ++q) raw[q] = live ? src[t + T * q] : make_uint4(0, 0, 0, 0);
     } else {
       const int64_t m = grp * RPB + row;
       const bool live = grp < ngroups && m < M;
@@ -702,7 +722,32 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         *reinterpret_cast<uint4*>(dst + mx6_main_off(m, g, K)) = make_uint4(r[0], r[1], r[2], r[3]);
         *reinterpret_cast<uint2*>(dst + mx6_tail_off(m, g, K)) = make_uint2(r[4], r[5]);
       };
-      if constexpr (!HAD && OUT == 2) {
+      if constexpr (SPREAD && OUT == 2) {
+        // the wave's codes as bytes to its LDS area, slice q holding the 8
+        // codes of unit t + T q of each lane in lane order; piece j (32
+        // bytes) of slice q is then group (T / 4) q + 16 (t / 64) + j, and
+        // each lane converts two pieces.  (The barrier is not needed for the
+        // data, which stays within the wave; it keeps the block's waves in
+        // step, measured 7 % faster at K = 4096.)
+        uint8_t* const C = cb + wave * 4096;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          *reinterpret_cast<uint2*>(C + 512 * q + 8 * lane) = make_uint2(quant4(v + 8 * q), quant4(v + 8 * q + 4));
+        __syncthreads();
+        if (live) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = (lane >> 4) + 4 * qq, j = lane & 15;
+            const int g = (T / 4) * q + 16 * (t >> 6) + j;
+            const uint4 a = *reinterpret_cast<const uint4*>(C + 512 * q + 32 * j);
+            const uint4 b = *reinterpret_cast<const uint4*>(C + 512 * q + 32 * j + 16);
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = (float)(int)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+            mx6_group(v, g);
+          }
+        }
+      } else if constexpr (!HAD && OUT == 2) {
         // the thread's 64 elements are contiguous: groups 2t and 2t + 1
 #pragma unroll
         for (int i = 0; i < 64; ++i) v[i] = qf(v[i]);
@@ -737,7 +782,7 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           const uint32_t w0 = quant4(v + 8 * gq), w1 = quant4(v + 8 * gq + 4);
           qs[(2 * gq) % 4] = __builtin_amdgcn_sdot4((int)w0, 0x01010101, qs[(2 * gq) % 4], false);
           qs[(2 * gq + 1) % 4] = __builtin_amdgcn_sdot4((int)w1, 0x01010101, qs[(2 * gq + 1) % 4], false);
-          const int e0 = (t << 6) | (8 * gq);
+          const int e0 = SPREAD ? 8 * (t + T * gq) : (t << 6) | (8 * gq);
           if (live) {
             if constexpr (BITS == 8) {
               *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(codes) + m * (int64_t)K + e0) = make_uint2(w0, w1);

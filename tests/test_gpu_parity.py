@@ -82,7 +82,7 @@ def test_quant_int8_rotation_token_counts(hbl, M, K):
     _quant_case(hbl, x, 8, True, f"M={M} K={K} INT8")
 
 
-@pytest.mark.parametrize("K", [64, 192, 960, 4096, 16384])
+@pytest.mark.parametrize("K", [64, 192, 960, 1024, 2048, 4096, 8192, 16384])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quant_plain(hbl, K, bits, dtype):
