@@ -42,6 +42,9 @@
 // four stage buffers, each its own LDS variable, are refilled four stages
 // ahead by direct-to-LDS buffer loads; the stage sequence runs through the
 // block's tiles, so the last stages of a tile already load the next one.
+// For bf16 outputs of 256 x 256 tiles up to K = 8192 the stage loads are
+// issued by one wave per SIMD only, so that each SIMD keeps a wave that
+// never waits to issue a load.
 // The waves meet once per stage, between its two MFMA steps: past that
 // barrier the stage's buffer may be refilled and the next stage's fragments
 // are read while the second step runs.  The barrier carries no memory fence
@@ -114,7 +117,7 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
 
 
-template <int OUT, int BM, int BN, int NWV>
+template <int OUT, int BM, int BN, int NWV, int PWV = NWV>
 __global__ void __launch_bounds__(64 * NWV, 1)
 k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, const uint32_t* __restrict__ wq,
           const float* __restrict__ alpha, int64_t M, int64_t N, int64_t K, void* __restrict__ out, int64_t ldo,
@@ -135,10 +138,15 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   // wave then loads 512 bytes with its lanes 0-31
   constexpr bool BHALF = BN * BROW / 1024 == NW / 2;
   constexpr bool THALF = BM * TROW / 1024 == NW / 2;
-  constexpr int MDMA = BM * MROW / 1024 / NW, TDMA = THALF ? 1 : BM * TROW / 1024 / NW,
-                BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
-  static_assert(MDMA * NW * 1024 == BM * MROW && (THALF || TDMA * NW * 1024 == BM * TROW) &&
-                    (BHALF || BDMA * NW * 1024 == BN * BROW),
+  // PW waves issue the stage loads: all of them, or (256 x 256 tiles, PWV
+  // = 4) one wave per SIMD, so that each SIMD keeps a wave that never waits
+  // to issue a load
+  constexpr int PW = PWV;
+  static_assert(PW == NW || (PW == 4 && NW == 8 && BM == 256 && BN == 256), "loading waves: all, or one per SIMD");
+  constexpr int MDMA = BM * MROW / 1024 / PW, TDMA = THALF ? 1 : BM * TROW / 1024 / PW,
+                BDMA = BHALF ? 1 : BN * BROW / 1024 / PW;
+  static_assert(MDMA * PW * 1024 == BM * MROW && (THALF || TDMA * PW * 1024 == BM * TROW) &&
+                    (BHALF || BDMA * PW * 1024 == BN * BROW) && (PW == NW || (!THALF && !BHALF)),
                 "staging must divide evenly");
   constexpr int DPS = MDMA + TDMA + BDMA;  // loads per wave per stage
   constexpr int MSZ = BM * MROW, TSZ = BM * TROW, BSZ = BN * BROW;
@@ -197,7 +205,7 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
   const uint32_t cl0 = 16u * (uint32_t)(64 * wave + lane);
   const uint32_t tl0 = THALF ? 16u * (uint32_t)(32 * wave + (lane & 31)) : cl0;
   const uint32_t wblk = (uint32_t)(K / BK) * 4096u;  // bytes of one 128-row weight block
-  // weight unit 64 (w + NW j) + l lies in 128-row block (64 w + l) / 256 + j NW / 4
+  // weight unit 64 (w + PW j) + l lies in 128-row block (64 w + l) / 256 + j PW / 4
   // (half loads: unit 32 w + l of the one block, lanes l < 32)
   const uint32_t wb0 = BHALF ? 16u * (uint32_t)(32 * wave + (lane & 31))
                              : (uint32_t)((64 * wave + lane) / 256) * wblk + 16u * (uint32_t)((64 * wave + lane) % 256);
@@ -235,15 +243,16 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     const uint32_t vm = live ? (uint32_t)dk * 24576u + amo + cl0 : kOut;
     const uint32_t vt = live ? (uint32_t)dk * 24576u + ato + tl0 : kOut;
     const uint32_t vb = live ? (uint32_t)dk * 4096u + wb0 : kOut;
+    if (PW == NW || wave < PW) {
 #pragma unroll
     for (int j = 0; j < MDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + NW * j), 16, vm + j * (NW * 1024u), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Md + 1024 * (wave + PW * j), 16, vm + j * (PW * 1024u), 0, 0, 0);
     if constexpr (THALF) {
       if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 512 * wave, 16, vt, 0, 0, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < TDMA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + NW * j), 16, vt + j * (NW * 1024u), 0, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Td + 1024 * (wave + PW * j), 16, vt + j * (PW * 1024u), 0, 0,
                                                  0);
     }
     if constexpr (BHALF) {
@@ -251,8 +260,9 @@ k_gemm_mx(const uint8_t* __restrict__ codes, const float* __restrict__ scales, c
     } else {
 #pragma unroll
       for (int j = 0; j < BDMA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * (NW / 4) * wblk, 0, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + PW * j), 16, vb + j * (PW / 4) * wblk, 0, 0,
                                                  0);
+    }
     }
     ++dk;
     if constexpr (SW) {
@@ -695,13 +705,23 @@ hipError_t launch_gemm_mx(const void* codes, const float* scales, const uint32_t
   // against 256 x 128 (bit-identical), unsplit: layer at M = 2048, N = K =
   // 4096 35.1 -> 32.9 us, M = 1024 28.8 -> 27.2, M = 3072 55.1 -> 53.4;
   // M = 2048, K = 16384 102 -> 99.
-#define HBL_MXT(OUT, BM, BN)                                                                                     \
-  hipLaunchKernelGGL((k_gemm_mx<OUT, BM, BN, 8>), dim3((unsigned)P), dim3(512), 0, s, c, scales, wq, alpha, M, N, K, \
-                     out, ldo, tm, tn, gm, ksplit, p16, part)
+#define HBL_MXT(OUT, BM, BN, PWV)                                                                          \
+  hipLaunchKernelGGL((k_gemm_mx<OUT, BM, BN, 8, PWV>), dim3((unsigned)P), dim3(512), 0, s, c, scales, wq, alpha, M, N, \
+                     K, out, ldo, tm, tn, gm, ksplit, p16, part)
+  // bf16 outputs of 256 x 256 tiles up to K = 8192: the stage loads from one
+  // wave per SIMD (bit-identical; us against all eight waves loading: 65536
+  // x 4096 x 4096 508 -> 496, 65536 x 16384 x 4096 2033 -> 1991; at K =
+  // 16384 slower, 1835 -> 1895)
   if (p.bm == 128) {
-    if (out_kind == 0) HBL_MXT(0, 128, 256); else if (out_kind == 1) HBL_MXT(1, 128, 256); else HBL_MXT(2, 128, 256);
+    if (out_kind == 0) HBL_MXT(0, 128, 256, 8); else if (out_kind == 1) HBL_MXT(1, 128, 256, 8); else HBL_MXT(2, 128, 256, 8);
   } else {
-    if (out_kind == 0) HBL_MXT(0, 256, 256); else if (out_kind == 1) HBL_MXT(1, 256, 256); else HBL_MXT(2, 256, 256);
+    if (out_kind == 0) {
+      if (K <= 8192) HBL_MXT(0, 256, 256, 4); else HBL_MXT(0, 256, 256, 8);
+    } else if (out_kind == 1) {
+      HBL_MXT(1, 256, 256, 8);
+    } else {
+      HBL_MXT(2, 256, 256, 8);
+    }
   }
 #undef HBL_MXT
   if (ksplit == 1) return hipGetLastError();
