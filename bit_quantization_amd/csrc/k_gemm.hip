@@ -353,8 +353,14 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   // the weights of a 256 x 128 tile's stage (4 KB) are half a load per wave
   // with 8 waves: each wave then loads 512 bytes with its lanes 0-31
   constexpr bool BHALF = BN * BROW / 1024 == NW / 2;
-  constexpr int ADMA = BM * AROW / 1024 / NW, BDMA = BHALF ? 1 : BN * BROW / 1024 / NW;
-  static_assert(ADMA * NW * 1024 == BM * AROW && (BHALF || BDMA * NW * 1024 == BN * BROW),
+  // waves issuing the stage loads: for INT8 codes on 256 x 256 tiles one per
+  // SIMD (waves 0-3, twice the loads each), so that each SIMD keeps a wave
+  // that never waits to issue a load (bit-identical; us against all eight
+  // waves loading: 65536 x 4096 x 4096 976 -> 950, 4096 x 4096 x 16384 219
+  // -> 215, 65536 x 16384 x 4096 3788 -> 3747; INT4 codes 1 % slower)
+  constexpr int PW = (BITS == 8 && BM == 256 && BN == 256 && NW == 8) ? 4 : NW;
+  constexpr int ADMA = BM * AROW / 1024 / PW, BDMA = BHALF ? 1 : BN * BROW / 1024 / PW;
+  static_assert(ADMA * PW * 1024 == BM * AROW && (BHALF || BDMA * PW * 1024 == BN * BROW) && (PW == NW || !BHALF),
                 "staging must divide evenly");
   static_assert(NBU == 1, "one weight unit per lane half");
   constexpr int DPS = ADMA + BDMA;  // loads per wave per stage
@@ -400,7 +406,7 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
   // (l % U) ^ swizzle(row); the swizzle term is the same for every j, so one
   // column offset per lane serves all loads.  Rows past the end of the
   // matrix lie beyond the buffer's range and read as zero.
-  constexpr int AJR = 64 * NW / AU, BJR = 64 * NW / BU;  // rows between loads j and j + 1
+  constexpr int AJR = 64 * PW / AU, BJR = 64 * PW / BU;  // rows between loads j and j + 1
   // (half loads: unit 32 w + l of the weight stage, lanes l < 32)
   const int ar0 = (64 * wave + lane) / AU, br0 = (BHALF ? 32 * wave + (lane & 31) : 64 * wave + lane) / BU;
   const uint32_t aoff0 = (uint32_t)ar0 * (uint32_t)arow_bytes + 16u * (uint32_t)aswz(ar0, lane % AU);
@@ -434,15 +440,17 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
     const bool live = dr < ntiles;
     const uint32_t va = live ? aoff0 + (uint32_t)dk * AROW : kOut;
     const uint32_t vb = live ? boff0 + (uint32_t)dk * BROW : kOut;
+    if (PW == NW || wave < PW) {
 #pragma unroll
     for (int j = 0; j < ADMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Ad + 1024 * (wave + NW * j), 16, va + j * astep, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, Ad + 1024 * (wave + PW * j), 16, va + j * astep, 0, 0, 0);
     if constexpr (BHALF) {
       if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 512 * wave, 16, vb, 0, 0, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < BDMA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + NW * j), 16, vb + j * bstep, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, Bd + 1024 * (wave + PW * j), 16, vb + j * bstep, 0, 0, 0);
+    }
     }
     ++dk;
     if constexpr (SW) {
