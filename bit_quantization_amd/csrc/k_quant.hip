@@ -43,6 +43,11 @@ constexpr float kSqrt7 = 2.6457513110645907f;
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+// Two fp32 values whose low 16 bits are zero (small integers) as packed bf16,
+// the first in the low half: exact, no rounding.
+__device__ __forceinline__ uint32_t pk_bf16_exact(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
 
 // Byte offsets of group g (32 codes) of token row m in the MX6 layout: the
 // codes of 256-row block B = m / 256 and stage s = g / 4 (128 codes) form one
@@ -464,6 +469,9 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
   // area as bytes to gather each group.  (At K = 16384 the MX6 form measured
   // slower this way: the rows keep 64 contiguous elements per lane there.)
   constexpr bool SPREAD = BF16 && !HAD && !NORM && OUT != 1 && (BITS == 8 || T == 64 || T == 128);
+  // MX6 codes of rotated rows of whole waves: the last exchange stays in
+  // the wave (see the output stage)
+  constexpr bool WLOC = HAD && OUT == 2 && T >= 64 && !NORM;
   __shared__ __attribute__((aligned(16))) uint8_t cb[SPREAD && OUT == 2 ? (BS / 64) * 4096 : 16];
   __shared__ __attribute__((aligned(16))) float lds[RPB * K];
   __shared__ float redf[RPB * (T > 64 ? T / 64 : 1)];
@@ -575,7 +583,10 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
             *reinterpret_cast<float4*>(Lr + swz16(e)) = make_float4(a[4 * blk], a[4 * blk + 1], a[4 * blk + 2], a[4 * blk + 3]);
           }
       }
-      __syncthreads();
+      // each wave's chunks are exactly the elements its pass-2 lanes read
+      // (the element's bits from 12 up, or its row, name the wave): with
+      // WLOC no block barrier here
+      if constexpr (WLOC) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); else __syncthreads();
     } else {
       if constexpr (BF16) {
 #pragma unroll
@@ -722,6 +733,16 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         *reinterpret_cast<uint4*>(dst + mx6_main_off(m, g, K)) = make_uint4(r[0], r[1], r[2], r[3]);
         *reinterpret_cast<uint2*>(dst + mx6_tail_off(m, g, K)) = make_uint2(r[4], r[5]);
       };
+      // the same from 32 codes in bf16 (16 words, code i in half i % 2 of
+      // word i / 2): the bf16 form of the conversion, element i at field i
+      auto mx6_group_bf16 = [&](const uint4 (&u)[4], int g) {
+        typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
+        struct W16 { uint4 a, b, c, d; };
+        const auto r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(__builtin_bit_cast(v32bf, W16{u[0], u[1], u[2], u[3]}), 1.0f);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
+        *reinterpret_cast<uint4*>(dst + mx6_main_off(m, g, K)) = make_uint4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<uint2*>(dst + mx6_tail_off(m, g, K)) = make_uint2(r[4], r[5]);
+      };
       if constexpr (SPREAD && OUT == 2) {
         // the wave's codes as bytes to its LDS area, slice q holding the 8
         // codes of unit t + T q of each lane in lane order; piece j (32
@@ -755,6 +776,45 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
           mx6_group(v, 2 * t);
           mx6_group(v + 32, 2 * t + 1);
         }
+      } else if constexpr (WLOC) {
+        // The lanes holding the 32 codes of a group share element bits 5 and
+        // up (bits 2-4 come from the lane's low bits and its register index):
+        // with T >= 64 they lie in one wave, which holds element bits 6-9
+        // in MPW values and every higher bit.  Each wave stages its 4096
+        // codes as bf16 (exact: integers in [-8, 7]) in the first 8 KB of
+        // its own 16 KB of the row's area (the rotated values there are no
+        // longer read: every wave's pass 3 read before the row reduction's
+        // barrier), at local index (bits 10 and up, bits 6-9 - MPW wr, bits
+        // 0-5), 16-byte unit q of local group lg at q ^ ((lg >> 2) & 3) so
+        // that both the 8-byte writes and the 64-byte group reads of 16
+        // lanes fall into distinct banks.  Each lane then converts two
+        // groups with the bf16 form of the packed E3M2 conversion.
+        constexpr int MPW = 1024 / T;
+        const int wr = t >> 6;
+        uint8_t* const S = reinterpret_cast<uint8_t*>(L) + 16384 * wr;
+#pragma unroll
+        for (int gi = 0; gi < 16; ++gi) {
+          const int e = last_e(gi);
+          const int li = ((((e >> 10) * MPW) + (((e >> 6) & 15) - MPW * wr)) << 6) | (e & 63);
+          const int lg = li >> 5;
+          const uint32_t lo = pk_bf16_exact(qf(v[4 * gi]), qf(v[4 * gi + 1]));
+          const uint32_t hi = pk_bf16_exact(qf(v[4 * gi + 2]), qf(v[4 * gi + 3]));
+          *reinterpret_cast<uint2*>(S + 64 * lg + 16 * (((li >> 3) & 3) ^ ((lg >> 2) & 3)) + 2 * (li & 7)) =
+              make_uint2(lo, hi);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own area: no block barrier
+        if (live) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int lg = (t & 63) + 64 * qq, hb = lg >> 1;
+            uint4 u[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) u[q] = *reinterpret_cast<const uint4*>(S + 64 * lg + 16 * (q ^ ((lg >> 2) & 3)));
+            const int e = ((hb / MPW) << 10) | ((MPW * wr + hb % MPW) << 6) | (32 * (lg & 1));
+            mx6_group_bf16(u, e >> 5);
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next row's writes
       } else if constexpr (HAD && OUT == 2) {
         // codes as fp32 to LDS in natural order, then each thread converts
         // groups t and t + T (32 consecutive codes each)
@@ -841,7 +901,11 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
         scales[mi] = s;
         if (rowsum) rowsum[mi] = qsum;
       }
-      __syncthreads();  // LDS and reduction scratch are reused by the next row group
+      // LDS and reduction scratch are reused by the next row group (with
+      // WLOC each wave reuses only its own area, after its own reads; the
+      // reduction scratch is rewritten only past the next row's pass-2
+      // barrier)
+      if constexpr (!WLOC) __syncthreads();
     }
   };
   const int64_t S = gridDim.x;
