@@ -68,6 +68,14 @@ __device__ __forceinline__ int64_t mx6_tail_off(int64_t m, int g, int K) {
   return tile * 24576 + 16384 + 16 * (2 * r + ((gi >> 1) ^ ((r >> 3) & 1))) + 8 * (gi & 1);
 }
 
+// A 16-byte load with the non-temporal hint: data read once, which should
+// not displace what the next kernel reads from the Infinity Cache.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned v4u_ __attribute__((ext_vector_type(4)));
+  const v4u_ v = __builtin_nontemporal_load(reinterpret_cast<const v4u_*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Loads 8 consecutive elements starting at p (16-byte aligned) as fp32.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* p, float* v) {
@@ -532,12 +540,18 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
       }
     } else if constexpr (SPREAD) {
       // 16-byte unit t + T q of the row: each load instruction reads
-      // consecutive bytes
+      // consecutive bytes, whole 128-byte lines, so they can carry the
+      // non-temporal hint: the rows (read once) then leave the codes this
+      // kernel writes in the Infinity Cache for the matmuls that read them
+      // next (the first such matmul of the 7B block, 65536 x 4096 x 4096:
+      // 577 -> 513 us).  The rotation paths read a line in four pieces,
+      // one per load instruction, and keep plain loads (with the hint the
+      // K = 16384 rotation ran 753 -> 1022 us).
       const int64_t m = grp * RPB + row;
       const bool live = grp < ngroups && m < M;
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + (live ? m : 0) * ldx * ESZ);
 #pragma unroll
-      for (int q = 0; q < NL; ++q) raw[q] = live ? src[t + T * q] : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < NL; ++q) raw[q] = live ? load_nt(src + t + T * q) : make_uint4(0, 0, 0, 0);
     } else {
       const int64_t m = grp * RPB + row;
       const bool live = grp < ngroups && m < M;
