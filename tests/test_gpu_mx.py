@@ -50,6 +50,32 @@ def test_quant_mx_codes(hbl, log2k, had, dtype):
     check_scales(sm.cpu().numpy(), os_, "mx scales")
 
 
+def test_quant_mx_codes_xcd_row_ranges(hbl):
+    """K = 16384 rotated rows, at least 32 per block of the persistent grid,
+    so that each XCD walks a contiguous range of rows: the MX6 codes equal
+    the INT4 layout's (whose kernel walks the rows in the plain order) bit
+    for bit on rows at the start, the middle, the ragged end and around
+    each XCD's range boundary, every scale equals, and a few rows match the
+    oracle to the code rule."""
+    K, M = 16384, 16421
+    x = workloads.random_rows(1603, M, K, "t3", as_bf16=True)
+    xd = to_device(x)
+    cm, sm = hbl.hadamard_quant_mx(xd, hadamard=True)
+    q4, s4, _ = hbl.hadamard_quant(xd, 4, hadamard=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(sm.cpu().numpy(), s4.cpu().numpy())
+    bounds = (np.arange(1, 8) * ((M + 7) // 8))[:, None] + np.arange(-3, 3)
+    rows = np.unique(np.concatenate([np.arange(0, 260), np.arange(8000, 8260), np.arange(M - 260, M),
+                                     bounds.reshape(-1)]))
+    got = mx_util.decode_mx6(cm.cpu().numpy(), K, rows)
+    q4n = q4.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, oracle.unpack_int4(q4n[rows], K).astype(np.float64))
+    few = np.array([0, 2052, 8191, M - 1])
+    oq, os_, _, xr = oracle.quantize(x[few], 4, hadamard=True, want_xr=True)
+    check_codes(oracle.unpack_int4(q4n[few], K), oracle.unpack_int4(oq, K), xr, 4, "mx K=16384 xcd ranges")
+    check_scales(sm.cpu().numpy()[few], os_, "mx K=16384 xcd ranges scales")
+
+
 # (unsplit: 128 x 256 tiles, whose rows are one half of a 256-row MX6 block;
 # M = 129 and 383 end in the second half of a block and the first half of the
 # next one, N = 16 and 272 leave part of a 256-column tile empty)
