@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import mx_util
 import oracle
 import workloads
 from parity_util import (bf16_to_f64, check_codes, check_hadamard, check_output, check_scales,
@@ -37,6 +38,28 @@ def test_hadamard_strided_rows(hbl):
     x_dev = to_device(big)[:, :K]
     y = hbl.hadamard_f32(x_dev).cpu().numpy()
     check_hadamard(y, oracle.hadamard(np.ascontiguousarray(big[:, :K])), "strided")
+
+
+@pytest.mark.parametrize("K", [1024, 4096, 16384])
+@pytest.mark.parametrize("M", [37, 600])
+@pytest.mark.parametrize("had", [False, True])
+def test_quant_strided_rows(hbl, K, M, had):
+    """Row-strided bf16 inputs (row stride K + 24 elements, 16-byte aligned
+    rows): INT8 and INT4 codes, scales and row sums, and MX6 codes and scales,
+    equal those of the same rows stored contiguously, bit for bit (the row
+    loads of every path, the line-wise non-temporal ones included, follow the
+    stride)."""
+    big = to_device(workloads.random_rows(4400 + K + M, M, K + 24, "t3", as_bf16=True))
+    xs, xc = big[:, :K], big[:, :K].contiguous()
+    assert xs.stride(0) == K + 24
+    for bits in (8, 4):
+        for u, v in zip(hbl.hadamard_quant(xs, bits, hadamard=had), hbl.hadamard_quant(xc, bits, hadamard=had)):
+            assert torch.equal(u, v), f"K={K} M={M} had={had} bits={bits}"
+    # (the MX6 buffer holds whole 256-row blocks; rows past M are not written)
+    (cs, ss), (cc, sc) = hbl.hadamard_quant_mx(xs, hadamard=had), hbl.hadamard_quant_mx(xc, hadamard=had)
+    assert torch.equal(ss, sc), f"K={K} M={M} had={had} MX6 scales"
+    assert np.array_equal(mx_util.decode_mx6(cs.cpu().numpy(), K, M), mx_util.decode_mx6(cc.cpu().numpy(), K, M)), \
+        f"K={K} M={M} had={had} MX6 codes"
 
 
 def test_hadamard_twice_is_identity(hbl):
