@@ -1015,7 +1015,7 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
     *reinterpret_cast<float4*>(Lw + 4 * unit(16 * cc + 4 * rb + g)) = make_float4(c[rb][0], c[rb][1], c[rb][2], c[rb][3]);
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // pass 2 reads the wave's own 1024 elements
   // pass 2: element bits 0-5 = lane, bits 6-9 = register index
   float v[16];
 #pragma unroll
@@ -1044,18 +1044,26 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
   const float fc = cn * f;
   constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   constexpr int kMagicBits = 0x4b400000;
-  __syncthreads();  // every thread's pass-3 reads are done: L takes the codes
-  int8_t* C8 = reinterpret_cast<int8_t*>(L);
+  // Every thread's pass-3 reads are done (the row reduction's barrier, or
+  // in-order LDS within a one-wave row).  Wave w holds the codes of elements
+  // 1024 wv + 64 P w .. + 64 P - 1 for each wv: 16 spans of 64 P bytes, 1 KB,
+  // which it stages in its own area (local byte 64 P wv + P l + p) and
+  // stores as 16-byte pieces, with no block barrier.
+  if constexpr (TR <= 64) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  int8_t* C8 = reinterpret_cast<int8_t*>(Lw);
 #pragma unroll
   for (int wv = 0; wv < NWV; ++wv)
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int bits = __float_as_int(__builtin_fmaf(v[p + P * wv], fc, kMagic));
-      C8[1024 * wv + P * tid + p] = (int8_t)(min(max(bits, kMagicBits - 128), kMagicBits + 127) - kMagicBits);
+      C8[64 * P * wv + P * lane + p] = (int8_t)(min(max(bits, kMagicBits - 128), kMagicBits + 127) - kMagicBits);
     }
-  __syncthreads();
-  const uint4 q4 = *reinterpret_cast<const uint4*>(C8 + 16 * tid);
-  *reinterpret_cast<uint4*>(codes + m * (int64_t)K + 16 * tid) = q4;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own codes
+  const uint4 q4 = *reinterpret_cast<const uint4*>(C8 + 16 * lane);
+  {
+    const int wv = (16 * lane) / (64 * P), o = (16 * lane) % (64 * P);
+    *reinterpret_cast<uint4*>(codes + m * (int64_t)K + 1024 * wv + 64 * P * wave + o) = q4;
+  }
   int qs = __builtin_amdgcn_sdot4((int)q4.x, 0x01010101, 0, false);
   qs = __builtin_amdgcn_sdot4((int)q4.y, 0x01010101, qs, false);
   qs = __builtin_amdgcn_sdot4((int)q4.z, 0x01010101, qs, false);
