@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["k_quant.hip", "k_ternarize.hip", "k_gemm.hip", "k_gemm_mx.hip", "k_kvquant.hip", "hbl_noalloc.hip",
            "hbl_api.cpp"]
-HEADERS = [os.path.join(CSRC, "hbl_internal.h"), os.path.join(ROOT, "include", "hbl.h")]
+HEADERS = [os.path.join(CSRC, "hbl_internal.h"), os.path.join(CSRC, "k_dot.h"), os.path.join(ROOT, "include", "hbl.h")]
 
 # -ffp-contract=off: no fused multiply-adds, so every product and sum is
 # rounded as written.  Packed fp32 instructions are disabled.

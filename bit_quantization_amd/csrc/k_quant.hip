@@ -31,6 +31,7 @@
 // phase A and the 4-byte strided accesses of phase B are free of bank
 // conflicts.
 #include "hbl_internal.h"
+#include "k_dot.h"
 
 namespace hbl {
 namespace {
@@ -963,25 +964,30 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 // Then the row maximum, the codes by one fma against 1.5 * 2^23 (as the
 // row-group kernel), and the codes through LDS in natural order for
 // contiguous 16-byte stores.
+// (The row's work, for a block of exactly K / 16 threads, in two parts: the
+// loads of the pass-1 operands (row_load_int8), then the rest
+// (row_quant_int8).  L holds K floats of LDS, redf and redi K / 1024
+// entries each.  codes, scales and rowsum may point to LDS.)
+// pass 1's B operand of k-step ks = 8 consecutive inputs of chunk lane % 16
 template <int LOG2K>
-__global__ void __launch_bounds__((1 << LOG2K) / 16)
-k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ codes, float* __restrict__ scales,
-                 int32_t* __restrict__ rowsum) {
-  constexpr int K = 1 << LOG2K, TR = K / 16, WB = LOG2K - 10, NWV = 1 << WB;
-  constexpr int PB = 4 - WB, P = 1 << PB;  // passengers of pass 3
-  __shared__ __attribute__((aligned(16))) float L[K];
-  __shared__ float redf[NWV];
-  __shared__ int redi[NWV];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m = blockIdx.x;
+__device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_t ldx, int64_t m, int tid,
+                                              v8bf (&bx)[2]) {
+  const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g = lane >> 4;
   const __bf16* xr = reinterpret_cast<const __bf16*>(x) + m * ldx;
-  const int cc = lane & 15, g = lane >> 4;
-
-  // pass 1: B operand of k-step ks = 8 consecutive inputs of chunk cc
-  v8bf bx[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     bx[ks] = *reinterpret_cast<const v8bf*>(xr + 1024 * wave + 64 * cc + 32 * ks + 8 * g);
+}
+
+template <int LOG2K>
+__device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __restrict__ codes,
+                                               float* __restrict__ scales, int32_t* __restrict__ rowsum, int64_t m,
+                                               int tid, float* __restrict__ L, float* __restrict__ redf,
+                                               int* __restrict__ redi) {
+  constexpr int K = 1 << LOG2K, TR = K / 16, WB = LOG2K - 10, NWV = 1 << WB;
+  constexpr int PB = 4 - WB, P = 1 << PB;  // passengers of pass 3
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cc = lane & 15, g = lane >> 4;
   // A operand (rb, ks): rows 16 rb + i of H_64 (i = l % 16), columns 32 ks +
   // kk (kk = 8 (l / 16) + e, e = 0..7).  The row and column bits split into
   // disjoint parts, so H_64[16 rb + i][32 ks + kk] = (-1)^popcount(i & kk) *
@@ -1073,6 +1079,61 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
     scales[m] = gamma / 127.0f;
     if (rowsum) rowsum[m] = qs;
   }
+}
+
+template <int LOG2K>
+__global__ void __launch_bounds__((1 << LOG2K) / 16)
+k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ codes, float* __restrict__ scales,
+                 int32_t* __restrict__ rowsum) {
+  constexpr int K = 1 << LOG2K, NWV = K / 1024;
+  __shared__ __attribute__((aligned(16))) float L[K];
+  __shared__ float redf[NWV];
+  __shared__ int redi[NWV];
+  v8bf bx[2];
+  row_load_int8<LOG2K>(x, ldx, blockIdx.x, threadIdx.x, bx);
+  row_quant_int8<LOG2K>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
+}
+
+// Decode layer of one token in one launch (H-BitLinear forward, INT8 codes,
+// bf16 input, K = 2^k, k = 10 ... 14): every block of the dot-product matmul
+// (gemv_dot_body, DecodeNB<k> output features per block) issues the loads of
+// the token row, then its weight loads, and, while the weights are in
+// flight, rotates and quantises the row itself (row_quant_int8, the same
+// arithmetic as k_fwht_quant_row, so the same codes), keeping the codes,
+// scale and row sum in its LDS.  (A wave's loads complete in issue order:
+// with the row loaded after the weights, the rotation waited for all of
+// them.)  Every
+// block repeats that work (an n log n transform of one row, small beside
+// its share of the weight stream) so that no block waits for another and
+// the layer needs no second launch.
+template <int LOG2K>
+constexpr int DecodeNB = LOG2K >= 14 ? 16 : 8;  // K = 16384: 80 KB of LDS, one block per CU, 256 blocks
+
+template <int LOG2K>
+__global__ void __launch_bounds__((1 << LOG2K) / 16)
+k_decode_token(const void* __restrict__ x, const uint32_t* __restrict__ wp, const float* __restrict__ alpha,
+               void* __restrict__ out) {
+  constexpr int K = 1 << LOG2K, NT = K / 16, TK = K / 64, NWV = K / 1024;
+  static_assert(DotGeom<1, TK, NT, DecodeNB<LOG2K>>::RED_INTS <= K, "the matmul's sums fit the row buffer");
+  __shared__ __attribute__((aligned(16))) float L[K];
+  __shared__ __attribute__((aligned(16))) int8_t cl[K];
+  __shared__ float redf[NWV];
+  __shared__ int redi[NWV];
+  __shared__ float s_tok;
+  __shared__ int32_t r_tok;
+  const int tid = threadIdx.x;
+  v8bf bx[2];
+  gemv_dot_body<8, 0, 1, TK, NT, DecodeNB<LOG2K>>(
+      cl, &s_tok, &r_tok, wp, alpha, 1, K, out, 0, blockIdx.x, tid, reinterpret_cast<int*>(L),
+      [&] {
+        row_load_int8<LOG2K>(x, 0, 0, tid, bx);
+        __builtin_amdgcn_sched_barrier(0);  // the row's loads are issued before the weights'
+      },
+      [&] {
+        __builtin_amdgcn_sched_barrier(0);
+        row_quant_int8<LOG2K>(bx, cl, &s_tok, &r_tok, 0, tid, L, redf, redi);
+        __syncthreads();  // codes, scale and row sum in LDS
+      });
 }
 
 // Plain (no rotation) quantisation for any K % 64 == 0, K <= 16384: one row
@@ -1291,6 +1352,27 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
   if (M == 0) return hipSuccess;
   return norm ? quant_by_k<true>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, gain, cu, s)
               : quant_by_k<false>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, nullptr, cu, s);
+}
+
+bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits) {
+  return bits == 8 && x_bf16 && hadamard && !norm && M == 1 && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0 &&
+         N % (K >= 16384 ? 16 : 8) == 0;
+}
+
+hipError_t launch_decode_token(const void* x, int K, const uint32_t* wp, const float* alpha, int64_t N, void* out,
+                               hipStream_t s) {
+#define HBL_DT(L)                                                                                              \
+  case L: {                                                                                                    \
+    constexpr int NB = DotGeom<1, (1 << L) / 64, (1 << L) / 16, DecodeNB<L>>::NB;                              \
+    if (N % NB != 0) return hipErrorInvalidValue;                                                              \
+    hipLaunchKernelGGL((k_decode_token<L>), dim3((unsigned)(N / NB)), dim3((1 << L) / 16), 0, s, x, wp, alpha, out); \
+    return hipGetLastError();                                                                                  \
+  }
+  switch (ilog2(K)) {
+    HBL_DT(10) HBL_DT(11) HBL_DT(12) HBL_DT(13) HBL_DT(14)
+    default: return hipErrorInvalidValue;
+  }
+#undef HBL_DT
 }
 
 hipError_t launch_hadamard_f32(const void* x, bool x_bf16, int64_t M, int K, int64_t ldx, float* y, int cu,

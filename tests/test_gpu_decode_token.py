@@ -1,0 +1,114 @@
+"""The one-token decode layer in one launch: hbl_forward with a single bf16
+token, INT8 codes and the rotation (BitNet v2 architecture write-up, §3.4
+"H-BitLinear", Eq. 9 with the INT8 quantiser of Eq. 7) runs in one kernel
+whose every block rotates and quantises the token row itself.
+
+Checked here:
+  - the layer output bit for bit against the two-launch path
+    (hbl_hadamard_quant, then hbl_ternary_gemm): the same rotation and
+    rounding give the same codes, and the integer sums are exact;
+  - the layer output against the oracle's fp64 layer value (per-row L2);
+  - K = 1024 ... 16384, N = 16 (one or two matmul blocks), 48 (ragged against
+    the block widths of 8 and 16) and 4096; a strided token row and a
+    strided output; an all-zero token (output exactly zero);
+  - 100 consecutive calls on changing inputs, each checked;
+  - a HIP graph of several calls replayed with new inputs between replays.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import bf16_to_f64, check_output, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _two_launch(hbl, x, packed, alpha):
+    q, s, rs = hbl.hadamard_quant(x, 8)
+    return hbl.ternary_gemm(q, 8, s, rs, packed, alpha, x.shape[1])
+
+
+@pytest.mark.parametrize("K", [1024, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("N", [16, 48, 4096])
+def test_decode_token_layer(hbl, K, N):
+    print(f"[one-token decode] K={K} N={N}", flush=True)
+    x_np = workloads.random_rows(K + 3 * N, 1, K, "t3")
+    w_np = workloads.gaussian_weights(9, K // 1024 + N, N, K)
+    x = to_device(x_np)
+    packed, alpha = hbl.ternarize_weights(to_device(w_np))
+    y = hbl.forward(x, packed, alpha, 8)
+    y2 = _two_launch(hbl, x, packed, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "one-launch and two-launch outputs differ"
+    o_packed, o_alpha, _ = oracle.ternarize(w_np)
+    y64 = oracle.forward(x_np, o_packed, o_alpha, 8, hadamard=True)
+    check_output(bf16_to_f64(y), y64, f"one-token decode K={K} N={N}")
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_decode_token_strided_and_zero_row(hbl, K):
+    N = 64
+    xb = torch.zeros((2, K + 256), dtype=torch.bfloat16, device="cuda")
+    xb[0, :K] = to_device(workloads.random_rows(33, 1, K, "t3"))[0]
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(10, 1, N, K)))
+    yb = torch.full((2, N + 24), -7.0, dtype=torch.bfloat16, device="cuda")
+    hbl.forward(xb[0:1, :K], packed, alpha, 8, out=yb[0:1, :N])
+    hbl.forward(xb[1:2, :K], packed, alpha, 8, out=yb[1:2, :N])  # the all-zero token
+    y2 = _two_launch(hbl, xb[0:1, :K].contiguous(), packed, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(yb[0:1, :N].view(torch.int16), y2.view(torch.int16))
+    assert torch.all(yb[:, N:] == -7.0), "wrote outside the output view"
+    assert torch.all(yb[1, :N].view(torch.int16) == 0), "an all-zero token must give exactly zero"
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_decode_token_many_calls(hbl, K):
+    N = 512
+    xs = [to_device(workloads.random_rows(80 + i, 1, K, "t3")) for i in range(3)]
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(11, 2, N, K)))
+    refs = [_two_launch(hbl, xi, packed, alpha) for xi in xs]
+    x = torch.empty_like(xs[0])
+    outs = torch.empty((100, 1, N), dtype=torch.bfloat16, device="cuda")
+    for i in range(100):
+        x.copy_(xs[i % 3])
+        hbl.forward(x, packed, alpha, 8, out=outs[i])
+    torch.cuda.synchronize()
+    for i in range(100):
+        assert torch.equal(outs[i].view(torch.int16), refs[i % 3].view(torch.int16)), f"call {i}"
+
+
+def test_decode_token_graph_replays(hbl):
+    """A graph of four calls (two matrices, two widths), replayed four times
+    with a new token row copied in eagerly before each replay."""
+    mats = [(4096, hbl.ternarize_weights(to_device(workloads.gaussian_weights(12, j, 4096, 4096)))) for j in range(2)]
+    mats += [(16384, hbl.ternarize_weights(to_device(workloads.gaussian_weights(12, 2 + j, 4096, 16384))))
+             for j in range(2)]
+    xs = {K: torch.empty((1, K), dtype=torch.bfloat16, device="cuda") for K in (4096, 16384)}
+    outs = [torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda") for _ in mats]
+    ws = [hbl.forward_workspace(1, 4096, K, 8, "cuda") for K, _ in mats]
+
+    def run():
+        for c, (K, (p, a)) in enumerate(mats):
+            hbl.forward(xs[K], p, a, 8, out=outs[c], workspace=ws[c])
+
+    for K in xs:
+        xs[K].copy_(to_device(workloads.random_rows(90 + K // 1024, 1, K, "t3")))
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for K in xs:
+            xs[K].copy_(to_device(workloads.random_rows(100 + 10 * r + K // 1024, 1, K, "t3")))
+        refs = [_two_launch(hbl, xs[K], p, a) for K, (p, a) in mats]
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c in range(len(mats)):
+            assert torch.equal(outs[c].view(torch.int16), refs[c].view(torch.int16)), f"replay {r}, call {c}"
