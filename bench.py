@@ -407,11 +407,11 @@ def run_decode(args, hbl, torch):
     t_g = time_stream(gem, n_mats)
     t_q = time_stream(lambda: hbl.hadamard_quant(x, bits), args.kernel_reps)
     g_bytes = w_bytes + M * K + 8 * M + 2 * M * N
-    if M == 1:
-        # one token: the layer is one launch (rotation, quantisation and
-        # weight streaming in k_decode_token), so the step is that kernel;
-        # algorithmic bytes: weights, the bf16 token row, the bf16 outputs
-        kern, t_k, k_bytes = "k_decode_token (one-token layer in one launch)", dt, w_bytes + 2 * K + 2 * N
+    if M <= (1 if K > 4096 else 2):
+        # one or two tokens: the layer is one launch (rotation, quantisation
+        # and weight streaming in k_decode_token), so the step is that kernel;
+        # algorithmic bytes: weights, the bf16 token rows, the bf16 outputs
+        kern, t_k, k_bytes = "k_decode_token (the layer in one launch)", dt, w_bytes + 2 * M * K + 2 * M * N
     else:
         kern, t_k, k_bytes = "k_gemv_dot / k_gemv (weight streaming)", t_g, g_bytes
     bw = k_bytes / t_k / 1e9

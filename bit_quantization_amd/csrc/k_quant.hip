@@ -971,12 +971,13 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 // pass 1's B operand of k-step ks = 8 consecutive inputs of chunk lane % 16
 template <int LOG2K>
 __device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_t ldx, int64_t m, int tid,
-                                              v8bf (&bx)[2]) {
+                                              v8bf (&bx)[2], bool live = true) {
   const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g = lane >> 4;
-  const __bf16* xr = reinterpret_cast<const __bf16*>(x) + m * ldx;
+  const __bf16* xr = reinterpret_cast<const __bf16*>(x) + (live ? m : 0) * ldx;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
-    bx[ks] = *reinterpret_cast<const v8bf*>(xr + 1024 * wave + 64 * cc + 32 * ks + 8 * g);
+    bx[ks] = live ? *reinterpret_cast<const v8bf*>(xr + 1024 * wave + 64 * cc + 32 * ks + 8 * g)
+                  : __builtin_bit_cast(v8bf, make_uint4(0u, 0u, 0u, 0u));
 }
 
 template <int LOG2K>
@@ -1094,45 +1095,49 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
   row_quant_int8<LOG2K>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
 }
 
-// Decode layer of one token in one launch (H-BitLinear forward, INT8 codes,
-// bf16 input, K = 2^k, k = 10 ... 14): every block of the dot-product matmul
-// (gemv_dot_body, DecodeNB<k> output features per block) issues the loads of
-// the token row, then its weight loads, and, while the weights are in
-// flight, rotates and quantises the row itself (row_quant_int8, the same
-// arithmetic as k_fwht_quant_row, so the same codes), keeping the codes,
-// scale and row sum in its LDS.  (A wave's loads complete in issue order:
-// with the row loaded after the weights, the rotation waited for all of
-// them.)  Every
-// block repeats that work (an n log n transform of one row, small beside
-// its share of the weight stream) so that no block waits for another and
-// the layer needs no second launch.
+// Decode layer of one or two tokens in one launch (H-BitLinear forward,
+// INT8 codes, bf16 input, K = 2^k, k = 10 ... 14, MT tokens with MT K / 16
+// <= 1024): every block of the dot-product matmul (gemv_dot_body, NB output
+// features per block) issues the loads of the token rows, then its weight
+// loads, and, while the weights are in flight, rotates and quantises the
+// rows itself, one group of K / 16 threads per row (row_quant_int8, the same
+// arithmetic as k_fwht_quant_row, so the same codes; the groups pass the
+// same barriers), keeping the codes, scales and row sums in its LDS.  Every
+// block repeats that work (an n log n transform per row, small beside its
+// share of the weight stream) so that no block waits for another and the
+// layer needs no second launch.  Rows m >= M are zero and their outputs are
+// not stored.  (A wave's loads complete in issue
+// order: the rows are loaded before the weights, whose arrival the rotation
+// does not need.)
 template <int LOG2K>
-constexpr int DecodeNB = LOG2K >= 14 ? 16 : 8;  // K = 16384: 80 KB of LDS, one block per CU, 256 blocks
+constexpr int DecodeNB = LOG2K >= 14 ? 16 : 8;  // one token at K = 16384: 80 KB of LDS, one block per CU, 256 blocks
 
-template <int LOG2K>
-__global__ void __launch_bounds__((1 << LOG2K) / 16)
-k_decode_token(const void* __restrict__ x, const uint32_t* __restrict__ wp, const float* __restrict__ alpha,
-               void* __restrict__ out) {
-  constexpr int K = 1 << LOG2K, NT = K / 16, TK = K / 64, NWV = K / 1024;
-  static_assert(DotGeom<1, TK, NT, DecodeNB<LOG2K>>::RED_INTS <= K, "the matmul's sums fit the row buffer");
-  __shared__ __attribute__((aligned(16))) float L[K];
-  __shared__ __attribute__((aligned(16))) int8_t cl[K];
-  __shared__ float redf[NWV];
-  __shared__ int redi[NWV];
-  __shared__ float s_tok;
-  __shared__ int32_t r_tok;
-  const int tid = threadIdx.x;
+template <int LOG2K, int MT>
+__global__ void __launch_bounds__(MT * (1 << LOG2K) / 16)
+k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ wp,
+               const float* __restrict__ alpha, void* __restrict__ out, int64_t ldo) {
+  constexpr int K = 1 << LOG2K, TR = K / 16, NT = MT * TR, TK = K / 64, NWV = K / 1024;
+  static_assert(NT <= 1024, "one block holds the rows");
+  static_assert(DotGeom<MT, TK, NT, DecodeNB<LOG2K>>::RED_INTS <= MT * K, "the matmul's sums fit the row buffers");
+  __shared__ __attribute__((aligned(16))) float L[MT * K];
+  __shared__ __attribute__((aligned(16))) int8_t cl[MT * K];
+  __shared__ float redf[MT * NWV];
+  __shared__ int redi[MT * NWV];
+  __shared__ float s_tok[MT];
+  __shared__ int32_t r_tok[MT];
+  const int tid = threadIdx.x, grp = tid / TR, gt = tid % TR;
   v8bf bx[2];
-  gemv_dot_body<8, 0, 1, TK, NT, DecodeNB<LOG2K>>(
-      cl, &s_tok, &r_tok, wp, alpha, 1, K, out, 0, blockIdx.x, tid, reinterpret_cast<int*>(L),
+  gemv_dot_body<8, 0, MT, TK, NT, DecodeNB<LOG2K>>(
+      cl, s_tok, r_tok, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
       [&] {
-        row_load_int8<LOG2K>(x, 0, 0, tid, bx);
-        __builtin_amdgcn_sched_barrier(0);  // the row's loads are issued before the weights'
+        row_load_int8<LOG2K>(x, ldx, grp, gt, bx, grp < M);
+        __builtin_amdgcn_sched_barrier(0);  // the rows' loads are issued before the weights'
       },
       [&] {
         __builtin_amdgcn_sched_barrier(0);
-        row_quant_int8<LOG2K>(bx, cl, &s_tok, &r_tok, 0, tid, L, redf, redi);
-        __syncthreads();  // codes, scale and row sum in LDS
+        row_quant_int8<LOG2K>(bx, cl + grp * K, s_tok + grp, r_tok + grp, 0, gt, L + grp * K, redf + grp * NWV,
+                              redi + grp * NWV);
+        __syncthreads();  // codes, scales and row sums in LDS
       });
 }
 
@@ -1354,22 +1359,40 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
               : quant_by_k<false>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, nullptr, cu, s);
 }
 
+// tokens taken in one launch: two up to K = 4096, else one.  (The rows must
+// fit one block of at most 1024 threads.  Measured against the two launches,
+// us per layer: two tokens at K = 4096 5.9 against 6.4; with 16 waves and
+// 80 KB of LDS per block, one block per CU, several rows lose: four tokens
+// at K = 4096 6.7 against 6.8, two at K = 8192 10.8 against about 8.)
+int decode_token_max_m(int64_t K) { return K > 4096 ? 1 : 2; }
+
+template <int L, int MT>
+constexpr int decode_nb() { return DotGeom<MT, (1 << L) / 64, MT * (1 << L) / 16, DecodeNB<L>>::NB; }
+
 bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits) {
-  return bits == 8 && x_bf16 && hadamard && !norm && M == 1 && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0 &&
-         N % (K >= 16384 ? 16 : 8) == 0;
+  if (!(bits == 8 && x_bf16 && hadamard && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0)) return false;
+  if (M < 1 || M > decode_token_max_m(K)) return false;
+  // features per block (decode_nb): 16 for one token at K = 16384, else 8
+  return N % (M == 1 && K >= 16384 ? 16 : 8) == 0;
 }
 
-hipError_t launch_decode_token(const void* x, int K, const uint32_t* wp, const float* alpha, int64_t N, void* out,
-                               hipStream_t s) {
-#define HBL_DT(L)                                                                                              \
-  case L: {                                                                                                    \
-    constexpr int NB = DotGeom<1, (1 << L) / 64, (1 << L) / 16, DecodeNB<L>>::NB;                              \
-    if (N % NB != 0) return hipErrorInvalidValue;                                                              \
-    hipLaunchKernelGGL((k_decode_token<L>), dim3((unsigned)(N / NB)), dim3((1 << L) / 16), 0, s, x, wp, alpha, out); \
-    return hipGetLastError();                                                                                  \
+hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, const uint32_t* wp,
+                               const float* alpha, int64_t N, void* out, int64_t ldo, hipStream_t s) {
+#define HBL_DT(L, MT)                                                                                           \
+  {                                                                                                             \
+    constexpr int NB = decode_nb<L, MT>();                                                                      \
+    if (N % NB != 0) return hipErrorInvalidValue;                                                               \
+    hipLaunchKernelGGL((k_decode_token<L, MT>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, ldx, \
+                       (int)M, wp, alpha, out, ldo);                                                            \
+    return hipGetLastError();                                                                                   \
   }
+  if (M < 1 || M > decode_token_max_m(K)) return hipErrorInvalidValue;
   switch (ilog2(K)) {
-    HBL_DT(10) HBL_DT(11) HBL_DT(12) HBL_DT(13) HBL_DT(14)
+    case 10: if (M == 1) HBL_DT(10, 1) else HBL_DT(10, 2)
+    case 11: if (M == 1) HBL_DT(11, 1) else HBL_DT(11, 2)
+    case 12: if (M == 1) HBL_DT(12, 1) else HBL_DT(12, 2)
+    case 13: HBL_DT(13, 1)
+    case 14: HBL_DT(14, 1)
     default: return hipErrorInvalidValue;
   }
 #undef HBL_DT

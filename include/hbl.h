@@ -244,11 +244,11 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
  *     0), the int32 partial sums of a split of K (at most 32 MiB); integer
  *     sums make the output the same bits with or without the split.
  * Shapes: the union of the rules of hbl_hadamard_quant and
- * hbl_ternary_gemm.  Two kernels are enqueued, except for one bf16 token
- * (M = 1) with INT8 codes and HBL_HADAMARD, K a power of two in [1024,
- * 16384] (N % 16 == 0 at K = 16384): then one kernel, in which every
- * block rotates and quantises the token itself while its weights stream
- * in; the codes stay on chip, ws is validated but not written, and y is
+ * hbl_ternary_gemm.  Two kernels are enqueued, except for one or two bf16
+ * tokens (M <= 2 up to K = 4096, M = 1 above) with INT8 codes and
+ * HBL_HADAMARD, K a power of two in [1024, 16384]: then one kernel, in which every block
+ * rotates and quantises the tokens itself while its weights stream in; the
+ * codes stay on chip, ws is validated but not written, and y is
  * bit-identical to the two-kernel result.
  * ------------------------------------------------------------------- */
 size_t hbl_forward_workspace_size(int64_t M, int64_t N, int64_t K, int bits);

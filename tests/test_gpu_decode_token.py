@@ -1,16 +1,18 @@
-"""The one-token decode layer in one launch: hbl_forward with a single bf16
-token, INT8 codes and the rotation (BitNet v2 architecture write-up, §3.4
-"H-BitLinear", Eq. 9 with the INT8 quantiser of Eq. 7) runs in one kernel
-whose every block rotates and quantises the token row itself.
+"""The few-token decode layer in one launch: hbl_forward with M bf16 tokens
+(M <= 2 up to K = 4096, else 1), INT8 codes and the
+rotation (BitNet v2 architecture write-up, §3.4 "H-BitLinear", Eq. 9 with
+the INT8 quantiser of Eq. 7) runs in one kernel whose every block rotates
+and quantises the token rows itself.
 
 Checked here:
   - the layer output bit for bit against the two-launch path
     (hbl_hadamard_quant, then hbl_ternary_gemm): the same rotation and
     rounding give the same codes, and the integer sums are exact;
   - the layer output against the oracle's fp64 layer value (per-row L2);
-  - K = 1024 ... 16384, N = 16 (one or two matmul blocks), 48 (ragged against
-    the block widths of 8 and 16) and 4096; a strided token row and a
-    strided output; an all-zero token (output exactly zero);
+  - every supported (K, M), K = 1024 ... 16384, M = 1 and 2, and N = 16 (one or
+    two matmul blocks), 48 (ragged against the block widths of 8 and 16) and
+    4096; strided token rows and outputs; an all-zero token among others
+    (its outputs exactly zero); the next M up, which takes two launches;
   - 100 consecutive calls on changing inputs, each checked;
   - a HIP graph of several calls replayed with new inputs between replays.
 """
@@ -32,11 +34,14 @@ def _two_launch(hbl, x, packed, alpha):
     return hbl.ternary_gemm(q, 8, s, rs, packed, alpha, x.shape[1])
 
 
-@pytest.mark.parametrize("K", [1024, 2048, 4096, 8192, 16384])
+KM = [(K, M) for K, mmax in ((1024, 2), (2048, 2), (4096, 2), (8192, 1), (16384, 1)) for M in range(1, mmax + 2)]
+
+
+@pytest.mark.parametrize("K,M", KM)
 @pytest.mark.parametrize("N", [16, 48, 4096])
-def test_decode_token_layer(hbl, K, N):
-    print(f"[one-token decode] K={K} N={N}", flush=True)
-    x_np = workloads.random_rows(K + 3 * N, 1, K, "t3")
+def test_decode_token_layer(hbl, K, M, N):
+    print(f"[few-token decode] K={K} M={M} N={N}", flush=True)
+    x_np = workloads.random_rows(K + 3 * N + M, M, K, "t3")
     w_np = workloads.gaussian_weights(9, K // 1024 + N, N, K)
     x = to_device(x_np)
     packed, alpha = hbl.ternarize_weights(to_device(w_np))
@@ -46,23 +51,24 @@ def test_decode_token_layer(hbl, K, N):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "one-launch and two-launch outputs differ"
     o_packed, o_alpha, _ = oracle.ternarize(w_np)
     y64 = oracle.forward(x_np, o_packed, o_alpha, 8, hadamard=True)
-    check_output(bf16_to_f64(y), y64, f"one-token decode K={K} N={N}")
+    check_output(bf16_to_f64(y), y64, f"few-token decode K={K} M={M} N={N}")
 
 
-@pytest.mark.parametrize("K", [4096, 16384])
-def test_decode_token_strided_and_zero_row(hbl, K):
+@pytest.mark.parametrize("K,M", [(4096, 1), (4096, 2), (4096, 3), (8192, 2), (16384, 1)])
+def test_decode_token_strided_and_zero_row(hbl, K, M):
     N = 64
-    xb = torch.zeros((2, K + 256), dtype=torch.bfloat16, device="cuda")
-    xb[0, :K] = to_device(workloads.random_rows(33, 1, K, "t3"))[0]
+    zero = M - 1  # the last token is all zero
+    xb = torch.zeros((M, K + 256), dtype=torch.bfloat16, device="cuda")
+    if M > 1:
+        xb[:zero, :K] = to_device(workloads.random_rows(33 + M, zero, K, "t3"))
     packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(10, 1, N, K)))
-    yb = torch.full((2, N + 24), -7.0, dtype=torch.bfloat16, device="cuda")
-    hbl.forward(xb[0:1, :K], packed, alpha, 8, out=yb[0:1, :N])
-    hbl.forward(xb[1:2, :K], packed, alpha, 8, out=yb[1:2, :N])  # the all-zero token
-    y2 = _two_launch(hbl, xb[0:1, :K].contiguous(), packed, alpha)
+    yb = torch.full((M, N + 24), -7.0, dtype=torch.bfloat16, device="cuda")
+    hbl.forward(xb[:, :K], packed, alpha, 8, out=yb[:, :N])
+    y2 = _two_launch(hbl, xb[:, :K].contiguous(), packed, alpha)
     torch.cuda.synchronize()
-    assert torch.equal(yb[0:1, :N].view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(yb[:, :N].view(torch.int16), y2.view(torch.int16))
     assert torch.all(yb[:, N:] == -7.0), "wrote outside the output view"
-    assert torch.all(yb[1, :N].view(torch.int16) == 0), "an all-zero token must give exactly zero"
+    assert torch.all(yb[zero, :N].view(torch.int16) == 0), "an all-zero token must give exactly zero"
 
 
 @pytest.mark.parametrize("K", [4096, 16384])
@@ -82,21 +88,23 @@ def test_decode_token_many_calls(hbl, K):
 
 
 def test_decode_token_graph_replays(hbl):
-    """A graph of four calls (two matrices, two widths), replayed four times
-    with a new token row copied in eagerly before each replay."""
+    """A graph of four calls (two matrices at each of two widths: two tokens
+    at K = 4096, one at K = 16384), replayed four times with new token rows
+    copied in eagerly before each replay."""
     mats = [(4096, hbl.ternarize_weights(to_device(workloads.gaussian_weights(12, j, 4096, 4096)))) for j in range(2)]
     mats += [(16384, hbl.ternarize_weights(to_device(workloads.gaussian_weights(12, 2 + j, 4096, 16384))))
              for j in range(2)]
-    xs = {K: torch.empty((1, K), dtype=torch.bfloat16, device="cuda") for K in (4096, 16384)}
-    outs = [torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda") for _ in mats]
-    ws = [hbl.forward_workspace(1, 4096, K, 8, "cuda") for K, _ in mats]
+    rows = {4096: 2, 16384: 1}
+    xs = {K: torch.empty((rows[K], K), dtype=torch.bfloat16, device="cuda") for K in rows}
+    outs = [torch.empty((rows[K], 4096), dtype=torch.bfloat16, device="cuda") for K, _ in mats]
+    ws = [hbl.forward_workspace(rows[K], 4096, K, 8, "cuda") for K, _ in mats]
 
     def run():
         for c, (K, (p, a)) in enumerate(mats):
             hbl.forward(xs[K], p, a, 8, out=outs[c], workspace=ws[c])
 
     for K in xs:
-        xs[K].copy_(to_device(workloads.random_rows(90 + K // 1024, 1, K, "t3")))
+        xs[K].copy_(to_device(workloads.random_rows(90 + K // 1024, rows[K], K, "t3")))
     run()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -105,7 +113,7 @@ def test_decode_token_graph_replays(hbl):
     torch.cuda.synchronize()
     for r in range(4):
         for K in xs:
-            xs[K].copy_(to_device(workloads.random_rows(100 + 10 * r + K // 1024, 1, K, "t3")))
+            xs[K].copy_(to_device(workloads.random_rows(100 + 10 * r + K // 1024, rows[K], K, "t3")))
         refs = [_two_launch(hbl, xs[K], p, a) for K, (p, a) in mats]
         torch.cuda.synchronize()
         g.replay()
