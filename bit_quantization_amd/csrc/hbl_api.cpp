@@ -166,7 +166,7 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, 
   if (hbl::decode_token_applies(x_dtype == HBL_DTYPE_BF16, M, N, K, (flags & HBL_HADAMARD) != 0, norm, bits)) {
     // a few tokens: rotation, quantisation and matmul in one launch (the
     // workspace is not used)
-    hipError_t e = hbl::launch_decode_token(x, ldx, M, (int)K, w_packed, alpha, N, y, ldy, s);
+    hipError_t e = hbl::launch_decode_token(x, ldx, M, (int)K, bits, w_packed, alpha, N, y, ldy, s);
     if (e != hipSuccess) return hip_fail(e, "few-token decode launch");
     return HBL_OK;
   }

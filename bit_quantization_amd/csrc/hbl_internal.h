@@ -115,12 +115,12 @@ hipError_t launch_kv_quant(const void* x, bool x_bf16, int64_t B, int64_t S, int
                            int bits, int keep_bos8, void* codes, float* scales, void* bos_codes,
                            float* bos_scales, int cu_count, hipStream_t s);
 
-// Few-token decode layer (k_quant.hip): the rotation + INT8 quantisation of
-// M bf16 token rows (M <= 2 up to K = 4096, else 1) and the
+// Few-token decode layer (k_quant.hip): the rotation + INT8 or INT4
+// quantisation of M bf16 token rows (M <= 2 up to K = 4096, else 1) and the
 // dot-product matmul with the rescale of Eq. 9 in one launch, bf16 output
 // [M][ldo]; the codes never leave the chip.
 bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits);
-hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, const uint32_t* wp,
+hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, const uint32_t* wp,
                                const float* alpha, int64_t N, void* out, int64_t ldo, hipStream_t s);
 
 // Token counts up to this take the weight-streaming kernel.

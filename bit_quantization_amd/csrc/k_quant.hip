@@ -980,7 +980,10 @@ __device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_
                   : __builtin_bit_cast(v8bf, make_uint4(0u, 0u, 0u, 0u));
 }
 
-template <int LOG2K>
+// BITS 8: INT8 absmax codes (Eq. 7), int8 [K]; BITS 4: INT4 absmean codes
+// (Eq. 8), packed as the public INT4 layout (code j = 4 h + b of a word at
+// bits 8 b + 4 h), K / 2 bytes.
+template <int LOG2K, int BITS = 8>
 __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ rowsum, int64_t m,
                                                int tid, float* __restrict__ L, float* __restrict__ redf,
@@ -1041,16 +1044,25 @@ __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __re
     }
   butterflies<16, PB, 4>(v);
 
-  // INT8 absmax (Eq. 7) of the rotated row x_r = c v
+  // INT8 absmax (Eq. 7) or INT4 absmean (Eq. 8) of the rotated row x_r = c v
   constexpr float scale = (LOG2K % 2 == 0) ? (float)(1.0 / (double)(1 << (LOG2K / 2))) : 0.0f;
   const float cn = (LOG2K % 2 == 0) ? scale : (float)(1.0 / __builtin_sqrt((double)K));
-  float st = abs_tree<16, true>(v);
-  st = row_reduce<TR, true>(st, redf, 0, tid);
-  const float gamma = st * cn;
-  const float f = 127.0f / (gamma + kEps);
+  float st = abs_tree<16, BITS == 8>(v);
+  st = row_reduce<TR, BITS == 8>(st, redf, 0, tid);
+  float f, s_out;
+  if constexpr (BITS == 8) {
+    const float gamma = st * cn;
+    f = 127.0f / (gamma + kEps);
+    s_out = gamma / 127.0f;
+  } else {
+    const float beta = (st * cn) / (float)K;
+    f = kSqrt7 / (beta + kEps);
+    s_out = beta / kSqrt7;
+  }
   const float fc = cn * f;
   constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   constexpr int kMagicBits = 0x4b400000;
+  constexpr int kLo = BITS == 8 ? -128 : -8, kHi = BITS == 8 ? 127 : 7;
   // Every thread's pass-3 reads are done (the row reduction's barrier, or
   // in-order LDS within a one-wave row).  Wave w holds the codes of elements
   // 1024 wv + 64 P w .. + 64 P - 1 for each wv: 16 spans of 64 P bytes, 1 KB,
@@ -1063,13 +1075,20 @@ __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __re
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int bits = __float_as_int(__builtin_fmaf(v[p + P * wv], fc, kMagic));
-      C8[64 * P * wv + P * lane + p] = (int8_t)(min(max(bits, kMagicBits - 128), kMagicBits + 127) - kMagicBits);
+      C8[64 * P * wv + P * lane + p] = (int8_t)(min(max(bits, kMagicBits + kLo), kMagicBits + kHi) - kMagicBits);
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own codes
   const uint4 q4 = *reinterpret_cast<const uint4*>(C8 + 16 * lane);
   {
     const int wv = (16 * lane) / (64 * P), o = (16 * lane) % (64 * P);
-    *reinterpret_cast<uint4*>(codes + m * (int64_t)K + 1024 * wv + 64 * P * wave + o) = q4;
+    const int64_t e = m * (int64_t)K + 1024 * wv + 64 * P * wave + o;  // first of the 16 codes
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint4*>(codes + e) = q4;
+    } else {
+      // codes 0-3 of each group of 8 in the low nibbles, 4-7 in the high ones
+      *reinterpret_cast<uint2*>(codes + e / 2) =
+          make_uint2((q4.x & 0x0f0f0f0fu) | ((q4.y & 0x0f0f0f0fu) << 4), (q4.z & 0x0f0f0f0fu) | ((q4.w & 0x0f0f0f0fu) << 4));
+    }
   }
   int qs = __builtin_amdgcn_sdot4((int)q4.x, 0x01010101, 0, false);
   qs = __builtin_amdgcn_sdot4((int)q4.y, 0x01010101, qs, false);
@@ -1077,7 +1096,7 @@ __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __re
   qs = __builtin_amdgcn_sdot4((int)q4.w, 0x01010101, qs, false);
   qs = row_reduce_int<TR>(qs, redi, 0, tid);
   if (tid == 0) {
-    scales[m] = gamma / 127.0f;
+    scales[m] = s_out;
     if (rowsum) rowsum[m] = qs;
   }
 }
@@ -1112,22 +1131,23 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 template <int LOG2K>
 constexpr int DecodeNB = LOG2K >= 14 ? 16 : 8;  // one token at K = 16384: 80 KB of LDS, one block per CU, 256 blocks
 
-template <int LOG2K, int MT>
+template <int LOG2K, int MT, int BITS>
 __global__ void __launch_bounds__(MT * (1 << LOG2K) / 16)
 k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ wp,
                const float* __restrict__ alpha, void* __restrict__ out, int64_t ldo) {
   constexpr int K = 1 << LOG2K, TR = K / 16, NT = MT * TR, TK = K / 64, NWV = K / 1024;
+  constexpr int CB = K * BITS / 8;  // code bytes per row
   static_assert(NT <= 1024, "one block holds the rows");
   static_assert(DotGeom<MT, TK, NT, DecodeNB<LOG2K>>::RED_INTS <= MT * K, "the matmul's sums fit the row buffers");
   __shared__ __attribute__((aligned(16))) float L[MT * K];
-  __shared__ __attribute__((aligned(16))) int8_t cl[MT * K];
+  __shared__ __attribute__((aligned(16))) int8_t cl[MT * CB];
   __shared__ float redf[MT * NWV];
   __shared__ int redi[MT * NWV];
   __shared__ float s_tok[MT];
   __shared__ int32_t r_tok[MT];
   const int tid = threadIdx.x, grp = tid / TR, gt = tid % TR;
   v8bf bx[2];
-  gemv_dot_body<8, 0, MT, TK, NT, DecodeNB<LOG2K>>(
+  gemv_dot_body<BITS, 0, MT, TK, NT, DecodeNB<LOG2K>>(
       cl, s_tok, r_tok, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
       [&] {
         row_load_int8<LOG2K>(x, ldx, grp, gt, bx, grp < M);
@@ -1135,8 +1155,8 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
       },
       [&] {
         __builtin_amdgcn_sched_barrier(0);
-        row_quant_int8<LOG2K>(bx, cl + grp * K, s_tok + grp, r_tok + grp, 0, gt, L + grp * K, redf + grp * NWV,
-                              redi + grp * NWV);
+        row_quant_int8<LOG2K, BITS>(bx, cl + grp * CB, s_tok + grp, r_tok + grp, 0, gt, L + grp * K,
+                                    redf + grp * NWV, redi + grp * NWV);
         __syncthreads();  // codes, scales and row sums in LDS
       });
 }
@@ -1370,22 +1390,28 @@ template <int L, int MT>
 constexpr int decode_nb() { return DotGeom<MT, (1 << L) / 64, MT * (1 << L) / 16, DecodeNB<L>>::NB; }
 
 bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits) {
-  if (!(bits == 8 && x_bf16 && hadamard && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0)) return false;
+  if (!((bits == 8 || bits == 4) && x_bf16 && hadamard && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0))
+    return false;
   if (M < 1 || M > decode_token_max_m(K)) return false;
   // features per block (decode_nb): 16 for one token at K = 16384, else 8
   return N % (M == 1 && K >= 16384 ? 16 : 8) == 0;
 }
 
-hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, const uint32_t* wp,
+hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, const uint32_t* wp,
                                const float* alpha, int64_t N, void* out, int64_t ldo, hipStream_t s) {
-#define HBL_DT(L, MT)                                                                                           \
-  {                                                                                                             \
-    constexpr int NB = decode_nb<L, MT>();                                                                      \
-    if (N % NB != 0) return hipErrorInvalidValue;                                                               \
-    hipLaunchKernelGGL((k_decode_token<L, MT>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, ldx, \
-                       (int)M, wp, alpha, out, ldo);                                                            \
-    return hipGetLastError();                                                                                   \
+#define HBL_DT(L, MT)                                                                                            \
+  {                                                                                                              \
+    constexpr int NB = decode_nb<L, MT>();                                                                       \
+    if (N % NB != 0) return hipErrorInvalidValue;                                                                \
+    if (bits == 8)                                                                                               \
+      hipLaunchKernelGGL((k_decode_token<L, MT, 8>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, \
+                         ldx, (int)M, wp, alpha, out, ldo);                                                      \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_decode_token<L, MT, 4>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, \
+                         ldx, (int)M, wp, alpha, out, ldo);                                                      \
+    return hipGetLastError();                                                                                    \
   }
+  if (bits != 8 && bits != 4) return hipErrorInvalidValue;
   if (M < 1 || M > decode_token_max_m(K)) return hipErrorInvalidValue;
   switch (ilog2(K)) {
     case 10: if (M == 1) HBL_DT(10, 1) else HBL_DT(10, 2)

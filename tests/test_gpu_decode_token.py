@@ -1,11 +1,11 @@
 """The few-token decode layer in one launch: hbl_forward with M bf16 tokens
-(M <= 2 up to K = 4096, else 1), INT8 codes and the
+(M <= 2 up to K = 4096, else 1), INT8 or INT4 codes and the
 rotation (BitNet v2 architecture write-up, §3.4 "H-BitLinear", Eq. 9 with
-the INT8 quantiser of Eq. 7) runs in one kernel whose every block rotates
-and quantises the token rows itself.
+the INT8 quantiser of Eq. 7 or the INT4 one of Eq. 8) runs in one kernel
+whose every block rotates and quantises the token rows itself.
 
 Checked here:
-  - the layer output bit for bit against the two-launch path
+  - INT8: the layer output bit for bit against the two-launch path
     (hbl_hadamard_quant, then hbl_ternary_gemm): the same rotation and
     rounding give the same codes, and the integer sums are exact;
   - the layer output against the oracle's fp64 layer value (per-row L2);
@@ -14,7 +14,9 @@ Checked here:
     4096; strided token rows and outputs; an all-zero token among others
     (its outputs exactly zero); the next M up, which takes two launches;
   - 100 consecutive calls on changing inputs, each checked;
-  - a HIP graph of several calls replayed with new inputs between replays.
+  - a HIP graph of several calls replayed with new inputs between replays;
+  - INT4 at every supported (K, M): against the oracle, and within 1e-3
+    per-row L2 of the two-launch path (see test_decode_token_layer_int4).
 """
 from __future__ import annotations
 
@@ -120,3 +122,28 @@ def test_decode_token_graph_replays(hbl):
         torch.cuda.synchronize()
         for c in range(len(mats)):
             assert torch.equal(outs[c].view(torch.int16), refs[c].view(torch.int16)), f"replay {r}, call {c}"
+
+
+@pytest.mark.parametrize("K,M", KM)
+@pytest.mark.parametrize("N", [16, 4096])
+def test_decode_token_layer_int4(hbl, K, M, N):
+    """INT4 absmean codes (Eq. 8): the one-launch kernel sums the row
+    statistic in another order than the many-token quantiser, so its codes
+    may differ from hbl_hadamard_quant's at rounding ties and its scale in
+    the last fp32 bit; checked against the oracle (per-row L2) and within
+    1e-3 per-row L2 of the two-launch path."""
+    print(f"[few-token decode INT4] K={K} M={M} N={N}", flush=True)
+    x_np = workloads.random_rows(2 * K + 3 * N + M, M, K, "t3")
+    w_np = workloads.gaussian_weights(13, K // 1024 + N, N, K)
+    x = to_device(x_np)
+    packed, alpha = hbl.ternarize_weights(to_device(w_np))
+    y = hbl.forward(x, packed, alpha, 4)
+    q, s, rs = hbl.hadamard_quant(x, 4)
+    y2 = hbl.ternary_gemm(q, 4, s, rs, packed, alpha, K)
+    torch.cuda.synchronize()
+    o_packed, o_alpha, _ = oracle.ternarize(w_np)
+    y64 = oracle.forward(x_np, o_packed, o_alpha, 4, hadamard=True)
+    check_output(bf16_to_f64(y), y64, f"few-token decode INT4 K={K} M={M} N={N}")
+    a, b = bf16_to_f64(y), bf16_to_f64(y2)
+    rel = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+    assert rel.max() <= 1e-3, f"one-launch and two-launch INT4 outputs differ by {rel.max():.2e}"
