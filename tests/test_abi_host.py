@@ -151,6 +151,24 @@ def test_forward_workspace(hbl):
     assert lib.hbl_forward(A, 1, 10, 256, 256, 60, 1, 4, B, C, D, 64, E, need, None) == hbl.ERR_SHAPE
 
 
+@pytest.mark.parametrize("M,K,bits", [(1, 4096, 8), (2, 4096, 8), (1, 16384, 8), (1, 16384, 4)])
+def test_forward_one_launch_shapes_still_validated(hbl, M, K, bits):
+    """One or two bf16 tokens with the rotation run as one kernel that does
+    not write the workspace; the arguments are validated all the same, and
+    an invalid call enqueues nothing (no device is needed to reach these
+    returns)."""
+    lib = hbl.lib()
+    N = 4096
+    need = lib.hbl_forward_workspace_size(M, N, K, bits)
+    assert need > 0
+    f = lib.hbl_forward
+    assert f(A, 1, M, K, K, N, 1, bits, B, C, D, N, E, need - 1, None) == hbl.ERR_WORKSPACE
+    assert f(A, 1, M, K, K, N, 1, bits, B, C, D, N, None, need, None) == hbl.ERR_WORKSPACE
+    assert f(A, 1, M, K, K, N, 1, bits, B, C, D, N - 4, E, need, None) == hbl.ERR_SHAPE  # ldy < N
+    assert f(A, 1, M, K, K, N, 1, bits, None, C, D, N, E, need, None) == hbl.ERR_NULL
+    assert f(A, 1, M, K, K, N, 1, bits, B, C, D + 2, N, E, need, None) == hbl.ERR_ALIGN
+
+
 def test_ternarize_errors(hbl):
     lib = hbl.lib()
     need = lib.hbl_ternarize_workspace_size(64, 256)
