@@ -1128,8 +1128,13 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 // not stored.  (A wave's loads complete in issue
 // order: the rows are loaded before the weights, whose arrival the rotation
 // does not need.)
+// 16 output features per block (256 blocks at N = 4096).  Measured with one
+// token, us per layer at K = 16384 / 4096 (two tokens at 4096): 8 features
+// per block - / 4.3 (5.7), 16: 8.5 / 3.7 (4.8), 32: 9.9 / 4.2 (5.2), 64:
+// 14.5 at K = 16384; blocks beyond one per CU would run in a second round
+// at K = 16384 (80 KB of LDS each)
 template <int LOG2K>
-constexpr int DecodeNB = LOG2K >= 14 ? 16 : 8;  // one token at K = 16384: 80 KB of LDS, one block per CU, 256 blocks
+constexpr int DecodeNB = 16;
 
 template <int LOG2K, int MT, int BITS>
 __global__ void __launch_bounds__(MT * (1 << LOG2K) / 16)
@@ -1393,8 +1398,7 @@ bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool had
   if (!((bits == 8 || bits == 4) && x_bf16 && hadamard && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0))
     return false;
   if (M < 1 || M > decode_token_max_m(K)) return false;
-  // features per block (decode_nb): 16 for one token at K = 16384, else 8
-  return N % (M == 1 && K >= 16384 ? 16 : 8) == 0;
+  return N % 16 == 0;  // features per block (decode_nb)
 }
 
 hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, const uint32_t* wp,

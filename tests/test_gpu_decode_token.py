@@ -9,9 +9,8 @@ Checked here:
     (hbl_hadamard_quant, then hbl_ternary_gemm): the same rotation and
     rounding give the same codes, and the integer sums are exact;
   - the layer output against the oracle's fp64 layer value (per-row L2);
-  - every supported (K, M), K = 1024 ... 16384, M = 1 and 2, and N = 16 (one or
-    two matmul blocks), 48 (ragged against the block widths of 8 and 16) and
-    4096; strided token rows and outputs; an all-zero token among others
+  - every supported (K, M), K = 1024 ... 16384, M = 1 and 2, and N = 16 (one
+    matmul block of 16 features), 48 (three) and 4096; strided token rows and outputs; an all-zero token among others
     (its outputs exactly zero); the next M up, which takes two launches;
   - 100 consecutive calls on changing inputs, each checked;
   - a HIP graph of several calls replayed with new inputs between replays;
