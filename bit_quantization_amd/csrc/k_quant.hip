@@ -982,8 +982,9 @@ __device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_
 
 // BITS 8: INT8 absmax codes (Eq. 7), int8 [K]; BITS 4: INT4 absmean codes
 // (Eq. 8), packed as the public INT4 layout (code j = 4 h + b of a word at
-// bits 8 b + 4 h), K / 2 bytes.
-template <int LOG2K, int BITS = 8>
+// bits 8 b + 4 h), K / 2 bytes, or, with MX, as MX6 operands of the FP6 x
+// FP4 matmul (mx6_main_off, mx6_tail_off; codes is then the buffer base).
+template <int LOG2K, int BITS = 8, bool MX = false>
 __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ rowsum, int64_t m,
                                                int tid, float* __restrict__ L, float* __restrict__ redf,
@@ -1082,7 +1083,33 @@ __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __re
   {
     const int wv = (16 * lane) / (64 * P), o = (16 * lane) % (64 * P);
     const int64_t e = m * (int64_t)K + 1024 * wv + 64 * P * wave + o;  // first of the 16 codes
-    if constexpr (BITS == 8) {
+    if constexpr (MX) {
+      static_assert(BITS == 4, "MX6 operands hold INT4 codes");
+      // lanes 2 i and 2 i + 1 hold the 32 codes of group (e - m K) / 32 (o
+      // is a multiple of 32 in even lanes); the even lane converts them
+      // with the gfx950 packed E3M2 conversion (scale 1: exact for integers
+      // in [-8, 7]), element 2 j of its first operand at field 2 j and
+      // element j of its second at field 2 j + 1
+      const uint32_t nb[4] = {(uint32_t)__shfl_xor((int)q4.x, 1), (uint32_t)__shfl_xor((int)q4.y, 1),
+                              (uint32_t)__shfl_xor((int)q4.z, 1), (uint32_t)__shfl_xor((int)q4.w, 1)};
+      if ((lane & 1) == 0) {
+        const uint32_t own[4] = {q4.x, q4.y, q4.z, q4.w};
+        v16f a, b;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c0 = 2 * i, c1 = 2 * i + 1;  // codes of the group
+          const uint32_t w0 = c0 < 16 ? own[c0 >> 2] : nb[(c0 - 16) >> 2];
+          const uint32_t w1 = c1 < 16 ? own[c1 >> 2] : nb[(c1 - 16) >> 2];
+          a[i] = (float)(int)(int8_t)(w0 >> (8 * (c0 & 3)));
+          b[i] = (float)(int)(int8_t)(w1 >> (8 * (c1 & 3)));
+        }
+        const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+        const int g = (int)((e - m * (int64_t)K) >> 5);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(codes);
+        *reinterpret_cast<uint4*>(dst + mx6_main_off(m, g, K)) = make_uint4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<uint2*>(dst + mx6_tail_off(m, g, K)) = make_uint2(r[4], r[5]);
+      }
+    } else if constexpr (BITS == 8) {
       *reinterpret_cast<uint4*>(codes + e) = q4;
     } else {
       // codes 0-3 of each group of 8 in the low nibbles, 4-7 in the high ones
@@ -1101,7 +1128,7 @@ __device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __re
   }
 }
 
-template <int LOG2K>
+template <int LOG2K, int BITS, bool MX>
 __global__ void __launch_bounds__((1 << LOG2K) / 16)
 k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ codes, float* __restrict__ scales,
                  int32_t* __restrict__ rowsum) {
@@ -1111,7 +1138,7 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
   __shared__ int redi[NWV];
   v8bf bx[2];
   row_load_int8<LOG2K>(x, ldx, blockIdx.x, threadIdx.x, bx);
-  row_quant_int8<LOG2K>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
+  row_quant_int8<LOG2K, BITS, MX>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
 }
 
 // Decode layer of one or two tokens in one launch (H-BitLinear forward,
@@ -1302,16 +1329,23 @@ template <int LOG2K, bool NORM>
 hipError_t dispatch_quant(const void* x, bool bf16, int64_t M, int64_t ldx, bool had, int bits,
                           void* codes, float* scales, int32_t* rowsum, const float* gain, int cu,
                           hipStream_t s) {
-  if constexpr (!NORM)  // MX6 codes are written without the normalisation layer
-    if (bits == 6) return dispatch_quant_mx<LOG2K, NORM>(x, bf16, M, ldx, had, codes, scales, rowsum, gain, cu, s);
   if constexpr (!NORM && LOG2K >= 10) {
-    // few rows of INT8 codes: one row per block of K / 16 threads
-    if (bits == 8 && bf16 && had && M <= kRowKernelMaxM<LOG2K>) {
-      hipLaunchKernelGGL((k_fwht_quant_row<LOG2K>), dim3((unsigned)M), dim3((1 << LOG2K) / 16), 0, s, x, ldx,
-                         static_cast<int8_t*>(codes), scales, rowsum);
-      return hipGetLastError();
+    // few rotated bf16 rows: one row per block of K / 16 threads, for every
+    // code layout (INT8, INT4, MX6), so that INT4 and MX6 codes of the same
+    // rows still come from the same arithmetic
+    if (bf16 && had && M <= kRowKernelMaxM<LOG2K>) {
+#define HBL_ROW(BITS, MX)                                                                                   \
+  hipLaunchKernelGGL((k_fwht_quant_row<LOG2K, BITS, MX>), dim3((unsigned)M), dim3((1 << LOG2K) / 16), 0, s, x, \
+                     ldx, static_cast<int8_t*>(codes), scales, rowsum);                                     \
+  return hipGetLastError()
+      if (bits == 8) { HBL_ROW(8, false); }
+      if (bits == 4) { HBL_ROW(4, false); }
+      if (bits == 6) { HBL_ROW(4, true); }
+#undef HBL_ROW
     }
   }
+  if constexpr (!NORM)  // MX6 codes are written without the normalisation layer
+    if (bits == 6) return dispatch_quant_mx<LOG2K, NORM>(x, bf16, M, ldx, had, codes, scales, rowsum, gain, cu, s);
 #define HBL_FQ(B16, BITS, HAD)                                                                              \
   if constexpr (LOG2K >= 10)                                                                                \
     return launch_fq64<LOG2K, B16, BITS, HAD, 0, NORM>(x, M, ldx, codes, scales, rowsum, nullptr, gain, cu, \

@@ -248,10 +248,8 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
  * tokens (M <= 2 up to K = 4096, M = 1 above) with HBL_HADAMARD, K a
  * power of two in [1024, 16384]: then one kernel, in which every block
  * rotates and quantises the tokens itself while its weights stream in; the
- * codes stay on chip and ws is validated but not written.  With INT8 codes
- * y is bit-identical to the two-kernel result; with INT4 codes the row's
- * absmean is summed in another order, so a code at a rounding tie, or the
- * last bit of the scale, may differ from hbl_hadamard_quant's.
+ * codes stay on chip and ws is validated but not written; y is
+ * bit-identical to the two-kernel result.
  * ------------------------------------------------------------------- */
 size_t hbl_forward_workspace_size(int64_t M, int64_t N, int64_t K, int bits);
 int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,

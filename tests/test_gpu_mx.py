@@ -50,6 +50,28 @@ def test_quant_mx_codes(hbl, log2k, had, dtype):
     check_scales(sm.cpu().numpy(), os_, "mx scales")
 
 
+@pytest.mark.parametrize("M,K", [(1, 1024), (3, 4096), (1024, 4096), (1025, 4096), (255, 16384), (256, 16384),
+                                 (257, 16384)])
+def test_quant_mx_codes_token_counts(hbl, M, K):
+    """Rotated bf16 rows take the one-row-per-block kernel up to 256 tokens
+    at K = 16384 and 1024 below, for the MX6 and the INT4 layouts alike:
+    on both sides of each boundary the two layouts hold the same codes and
+    scales bit for bit, and match the oracle to the code rule."""
+    x = workloads.random_rows(900 + M + K // 1024, M, K, "t3", as_bf16=True)
+    xd = to_device(x)
+    cm, sm = hbl.hadamard_quant_mx(xd, hadamard=True)
+    q4, s4, _ = hbl.hadamard_quant(xd, 4, hadamard=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(min(M, 40)), np.arange(max(0, M - 40), M)]))
+    got = mx_util.decode_mx6(cm.cpu().numpy(), K, rows)
+    q4n = q4.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, oracle.unpack_int4(q4n[rows], K).astype(np.float64))
+    assert np.array_equal(sm.cpu().numpy(), s4.cpu().numpy())
+    oq, os_, _, xr = oracle.quantize(np.ascontiguousarray(x[rows]), 4, hadamard=True, want_xr=True)
+    check_codes(got.astype(np.int8), oracle.unpack_int4(oq, K), xr, 4, f"mx M={M} K={K}")
+    check_scales(sm.cpu().numpy()[rows], os_, f"mx M={M} K={K} scales")
+
+
 def test_quant_mx_codes_xcd_row_ranges(hbl):
     """K = 16384 rotated rows, at least 32 per block of the persistent grid,
     so that each XCD walks a contiguous range of rows: the MX6 codes equal

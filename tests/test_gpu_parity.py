@@ -95,14 +95,15 @@ def test_quant_with_rotation(hbl, log2k, bits):
     _quant_case(hbl, x, bits, True, f"K={K} INT{bits}")
 
 
-# INT8 codes with the rotation take the one-row-per-block kernel up to 256
-# tokens at K = 16384 and 1024 below, the row-group kernel beyond: both
-# sides of each boundary against the oracle
+# Rotated bf16 rows take the one-row-per-block kernel up to 256 tokens at
+# K = 16384 and 1024 below (INT8, INT4 and MX6 codes alike), the row-group
+# kernel beyond: both sides of each boundary against the oracle
 @pytest.mark.parametrize("M,K", [(1, 1024), (5, 2048), (65, 4096), (1024, 4096), (1025, 4096), (256, 8192),
                                  (200, 16384), (256, 16384), (257, 16384)])
-def test_quant_int8_rotation_token_counts(hbl, M, K):
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quant_rotation_token_counts(hbl, M, K, bits):
     x = workloads.random_rows(400 + M + K // 1024, M, K, "t3", as_bf16=True)
-    _quant_case(hbl, x, 8, True, f"M={M} K={K} INT8")
+    _quant_case(hbl, x, bits, True, f"M={M} K={K} INT{bits}")
 
 
 @pytest.mark.parametrize("K", [64, 192, 960, 1024, 2048, 4096, 8192, 16384])
