@@ -848,8 +848,7 @@ k_gemv(const void* __restrict__ codes, const float* __restrict__ scales,
   }
 }
 
-// Decode with very few tokens (M <= 2, or INT4 M <= 4 at K = 16384), K a
-// power of two from 1024 to 16384: the dot-product form (k_dot.h), one
+// Decode with one or two tokens, K a power of two from 1024 to 16384: the dot-product form (k_dot.h), one
 // block of 512 threads per DotGeom::NB output features.
 template <int BITS, int OUT, int MT, int TK>
 __global__ void __launch_bounds__(512)
@@ -926,15 +925,14 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
       return hipGetLastError();
     }
   }
-  // the dot-product kernel for 1-2 tokens, and for 3-4 INT4 tokens from
-  // K = 16384; its per-token code loads grow with M, and the matrix-core
-  // GEMV is faster from 3 tokens on otherwise (measured at N = 4096, 10 or
-  // more matrices cycled, us dot against MFMA: K = 4096, M = 4 INT8 6.3 /
-  // 3.8, INT4 4.6 / 4.4; M = 2 INT4 3.7 / 4.0; K = 16384, M = 4 INT8 9.9 /
-  // 8.5 (INT8 codes staged through LDS), INT4 10.2 / 10.7)
+  // the dot-product kernel for 1-2 tokens; its per-token code loads grow
+  // with M, and the matrix-core GEMV is faster from 3 tokens on (measured
+  // at N = 4096, 32 or 128 matrices cycled, us dot against MFMA: K = 16384,
+  // M = 2 INT4 6.9 / 7.7, INT8 6.6 / 7.0; M = 3 INT4 8.6 / 7.6; M = 4 INT4
+  // 8.9 / 7.6; K = 4096, M = 2 INT4 3.5 / 3.8, INT8 3.5 / 3.6)
   // (a thread covers 64 codes of each of its rows, TK = K / 64 a power of
   // two from 16 to 256: K = 1024 ... 16384)
-  if ((M <= 2 || (BITS == 4 && M <= 4 && K >= 16384)) && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0) {
+  if (M <= 2 && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0) {
     const int64_t tk = K / 64;
 #define HBL_DOT(MT, TK)                                                                                  \
   if (N % DotGeom<MT, TK>::NB == 0) {                                                                  \
@@ -949,8 +947,7 @@ hipError_t launch_bits_out(const void* codes, const float* scales, const int32_t
   else if (tk == 32) { HBL_DOT(MT, 32) }        \
   else { HBL_DOT(MT, 16) }
     if (M == 1) { HBL_DOT_TK(1) }
-    else if (M == 2) { HBL_DOT_TK(2) }
-    else { HBL_DOT_TK(4) }
+    else { HBL_DOT_TK(2) }
 #undef HBL_DOT_TK
 #undef HBL_DOT
   }

@@ -183,8 +183,8 @@ def test_gemm_decode_widths_outside_dot_kernel(hbl, M, N, K, bits):
 
 
 # every decode dispatch branch at the 7B widths: the dot-product kernel (M <=
-# 2, and INT4 M = 3-4 at K = 16384), its interleaved INT8 code loads (K <=
-# 8192) and the matrix-core weight streaming (M = 3-4 otherwise)
+# 2), its interleaved INT8 code loads (K <= 8192) and the matrix-core weight
+# streaming (M = 3-4)
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("K", [4096, 8192, 16384])
 @pytest.mark.parametrize("bits", [8, 4])
