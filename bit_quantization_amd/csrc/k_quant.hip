@@ -1276,7 +1276,10 @@ k_quant_plain(const void* __restrict__ x, int64_t M, int K, int64_t ldx,
 // rotation, bf16 input): measured on MI355X against the row-group kernel
 // (us per call, graph replay): K = 16384 M = 1 5.37 -> 4.98, M = 256 8.10 ->
 // 7.63, M = 512 10.63 -> 10.89 (slower); K = 4096 M = 1 4.03 -> 2.90, M =
-// 1024 7.47 -> 6.81; K = 8192 M = 256 6.71 -> 4.91.
+// 1024 7.47 -> 6.81; K = 8192 M = 256 6.71 -> 4.91.  Beyond the thresholds
+// (row-group -> row kernel, INT8 / INT4 / MX6 codes): K = 4096 M = 2048
+// 7.8 / 7.2 / 8.3 -> 7.8 / 7.3 / 8.7; K = 8192 M = 1024 8.3 / 7.5 / 9.1 ->
+// 8.3 / 7.4 / 8.8; K = 16384 M = 512 8.5 / 7.9 / 9.2 -> 9.0 / 8.2 / 9.4.
 template <int LOG2K>
 constexpr int64_t kRowKernelMaxM = LOG2K >= 14 ? 256 : 1024;
 
