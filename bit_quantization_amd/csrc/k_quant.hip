@@ -965,12 +965,12 @@ k_fwht_quant64(const void* __restrict__ x, int64_t M, int64_t ldx,
 // row-group kernel), and the codes through LDS in natural order for
 // contiguous 16-byte stores.
 // (The row's work, for a block of exactly K / 16 threads, in two parts: the
-// loads of the pass-1 operands (row_load_int8), then the rest
-// (row_quant_int8).  L holds K floats of LDS, redf and redi K / 1024
+// loads of the pass-1 operands (row_load), then the rest
+// (row_quant).  L holds K floats of LDS, redf and redi K / 1024
 // entries each.  codes, scales and rowsum may point to LDS.)
 // pass 1's B operand of k-step ks = 8 consecutive inputs of chunk lane % 16
 template <int LOG2K>
-__device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_t ldx, int64_t m, int tid,
+__device__ __forceinline__ void row_load(const void* __restrict__ x, int64_t ldx, int64_t m, int tid,
                                               v8bf (&bx)[2], bool live = true) {
   const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g = lane >> 4;
   const __bf16* xr = reinterpret_cast<const __bf16*>(x) + (live ? m : 0) * ldx;
@@ -985,7 +985,7 @@ __device__ __forceinline__ void row_load_int8(const void* __restrict__ x, int64_
 // bits 8 b + 4 h), K / 2 bytes, or, with MX, as MX6 operands of the FP6 x
 // FP4 matmul (mx6_main_off, mx6_tail_off; codes is then the buffer base).
 template <int LOG2K, int BITS = 8, bool MX = false>
-__device__ __forceinline__ void row_quant_int8(const v8bf (&bx)[2], int8_t* __restrict__ codes,
+__device__ __forceinline__ void row_quant(const v8bf (&bx)[2], int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ rowsum, int64_t m,
                                                int tid, float* __restrict__ L, float* __restrict__ redf,
                                                int* __restrict__ redi) {
@@ -1137,8 +1137,8 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
   __shared__ float redf[NWV];
   __shared__ int redi[NWV];
   v8bf bx[2];
-  row_load_int8<LOG2K>(x, ldx, blockIdx.x, threadIdx.x, bx);
-  row_quant_int8<LOG2K, BITS, MX>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
+  row_load<LOG2K>(x, ldx, blockIdx.x, threadIdx.x, bx);
+  row_quant<LOG2K, BITS, MX>(bx, codes, scales, rowsum, blockIdx.x, threadIdx.x, L, redf, redi);
 }
 
 // Decode layer of one or two tokens in one launch (H-BitLinear forward,
@@ -1146,7 +1146,7 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 // <= 1024): every block of the dot-product matmul (gemv_dot_body, NB output
 // features per block) issues the loads of the token rows, then its weight
 // loads, and, while the weights are in flight, rotates and quantises the
-// rows itself, one group of K / 16 threads per row (row_quant_int8, the same
+// rows itself, one group of K / 16 threads per row (row_quant, the same
 // arithmetic as k_fwht_quant_row, so the same codes; the groups pass the
 // same barriers), keeping the codes, scales and row sums in its LDS.  Every
 // block repeats that work (an n log n transform per row, small beside its
@@ -1182,12 +1182,12 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
   gemv_dot_body<BITS, 0, MT, TK, NT, DecodeNB<LOG2K>>(
       cl, s_tok, r_tok, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
       [&] {
-        row_load_int8<LOG2K>(x, ldx, grp, gt, bx, grp < M);
+        row_load<LOG2K>(x, ldx, grp, gt, bx, grp < M);
         __builtin_amdgcn_sched_barrier(0);  // the rows' loads are issued before the weights'
       },
       [&] {
         __builtin_amdgcn_sched_barrier(0);
-        row_quant_int8<LOG2K, BITS>(bx, cl + grp * CB, s_tok + grp, r_tok + grp, 0, gt, L + grp * K,
+        row_quant<LOG2K, BITS>(bx, cl + grp * CB, s_tok + grp, r_tok + grp, 0, gt, L + grp * K,
                                     redf + grp * NWV, redi + grp * NWV);
         __syncthreads();  // codes, scales and row sums in LDS
       });
