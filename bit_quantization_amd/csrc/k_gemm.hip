@@ -685,7 +685,6 @@ k_gemm_pt(const void* __restrict__ codes, const float* __restrict__ scales,
 
 // ---------------------------------------------------------------------------
 // Decode: M <= 16 tokens, one block per 16 output features.
-constexpr int kGemvBatch = 8;  // 16-byte weight loads in flight per lane
 
 // MG groups of 16 tokens (M <= 16 MG): every block streams its 16 features'
 // weights once and applies each decoded weight fragment to all token groups,
