@@ -65,10 +65,12 @@ struct DotGeom {
 
 // One block's share: features fb * NB .. + NB - 1.  red: RED_INTS ints of
 // LDS.  before_weights() runs first, before_codes() after the weight loads
-// are issued and before the codes, scales and row sums are read (the
-// one-launch decode layer issues its token-row loads in the first and
-// computes the codes in the second; the codes may then live in LDS).
-template <int BITS, int OUT, int MT, int TK, int NTH, int NBMIN = 8, typename Pre, typename Hook>
+// are issued and before the scales and row sums are read (the one-launch
+// decode layer issues its token-row loads in the first and computes the
+// codes in the second; the codes may then live in LDS).  The codes are
+// loaded after before_codes(), or, with XFIRST, before the weight loads
+// are issued (codes in global memory, written by an earlier launch).
+template <int BITS, int OUT, int MT, int TK, int NTH, int NBMIN = 8, bool XFIRST = false, typename Pre, typename Hook>
 __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, const float* __restrict__ scales,
                                               const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
                                               const float* __restrict__ alpha, int M, int64_t K, void* __restrict__ out,
@@ -91,9 +93,45 @@ __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, co
   // K = 4096 3.5 -> 3.1 us, M = 2 4.4 -> 3.7; at K = 16384 and with INT4
   // codes, read as 8-byte pieces, 3-11 % slower); else the 64 consecutive
   // codes 64 kt .. + 63 and one 16-byte weight load per row.  Weights: rows
-  // n0 + rg + RP i; every load is issued first.
+  // n0 + rg + RP i; every weight load is issued before any is used.
   constexpr bool IL = BITS == 8 && TK <= 128;
+  // the tokens' codes for k = 64*kt .. +63, as 16 dwords of signed bytes
+  // (16-byte piece j of token m at byte m K BITS/8 + 16 j)
+  auto piece = [&](int m, int64_t j) -> uint4 {
+    return reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (int64_t)m * K * BITS / 8)[j];
+  };
+  uint32_t x[MT][16];
+  auto load_codes = [&] {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        if constexpr (BITS == 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 u = piece(m, IL ? kt + TK * q : 4 * kt + q);
+            x[m][4 * q] = u.x; x[m][4 * q + 1] = u.y; x[m][4 * q + 2] = u.z; x[m][4 * q + 3] = u.w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint4 u = piece(m, 2 * kt + q);
+            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              x[m][8 * q + 2 * j] = (ww[j] << 4) & 0xf0f0f0f0u;  // codes 0-3 of the word, as 16 q
+              x[m][8 * q + 2 * j + 1] = ww[j] & 0xf0f0f0f0u;     // codes 4-7
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[m][j] = 0;
+      }
+    }
+  };
+
   before_weights();
+  if constexpr (XFIRST) load_codes();
   uint4 w[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -105,39 +143,7 @@ __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, co
       w[i] = load_stream(row + 4 * kt);
   }
   before_codes();
-
-  // the tokens' codes for k = 64*kt .. +63, as 16 dwords of signed bytes
-  // (16-byte piece j of token m at byte m K BITS/8 + 16 j)
-  auto piece = [&](int m, int64_t j) -> uint4 {
-    return reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(codes) + (int64_t)m * K * BITS / 8)[j];
-  };
-  uint32_t x[MT][16];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m < M) {
-      if constexpr (BITS == 8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 u = piece(m, IL ? kt + TK * q : 4 * kt + q);
-          x[m][4 * q] = u.x; x[m][4 * q + 1] = u.y; x[m][4 * q + 2] = u.z; x[m][4 * q + 3] = u.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint4 u = piece(m, 2 * kt + q);
-          const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[m][8 * q + 2 * j] = (ww[j] << 4) & 0xf0f0f0f0u;  // codes 0-3 of the word, as 16 q
-            x[m][8 * q + 2 * j + 1] = ww[j] & 0xf0f0f0f0u;     // codes 4-7
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) x[m][j] = 0;
-    }
-  }
+  if constexpr (!XFIRST) load_codes();
 
   int acc[RPT][MT];
 #pragma unroll
