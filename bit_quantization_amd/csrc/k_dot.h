@@ -69,8 +69,12 @@ struct DotGeom {
 // decode layer issues its token-row loads in the first and computes the
 // codes in the second; the codes may then live in LDS).  The codes are
 // loaded after before_codes(), or, with XFIRST, before the weight loads
-// are issued (codes in global memory, written by an earlier launch).
-template <int BITS, int OUT, int MT, int TK, int NTH, int NBMIN = 8, bool XFIRST = false, typename Pre, typename Hook>
+// are issued (codes in global memory, written by an earlier launch).  With
+// SELF, rowsum is not read: each thread starts its sums at minus the sum
+// of its own codes, so that the reduction over the row's threads yields
+// sum q_x c - sum q_x = sum q_x q_w directly (the same integers).
+template <int BITS, int OUT, int MT, int TK, int NTH, int NBMIN = 8, bool XFIRST = false, bool SELF = false,
+          typename Pre, typename Hook>
 __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, const float* __restrict__ scales,
                                               const int32_t* __restrict__ rowsum, const uint32_t* __restrict__ wp,
                                               const float* __restrict__ alpha, int M, int64_t K, void* __restrict__ out,
@@ -146,10 +150,18 @@ __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, co
   if constexpr (!XFIRST) load_codes();
 
   int acc[RPT][MT];
+  int xsum[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    xsum[m] = 0;
+    if constexpr (SELF)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xsum[m] = __builtin_amdgcn_sdot4((int)x[m][j], 0x01010101, xsum[m], false);
+  }
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[i][m] = 0;
+    for (int m = 0; m < MT; ++m) acc[i][m] = -xsum[m];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
@@ -209,7 +221,7 @@ __device__ __forceinline__ void gemv_dot_body(const void* __restrict__ codes, co
       if constexpr (BITS == 4) v >>= 4;  // exact: every product carries a factor 16
       const int64_t n = n0 + row;
       const float sc = scales[m] * *alpha;
-      const int t = v - rowsum[m];
+      const int t = SELF ? v : v - rowsum[m];
       if constexpr (OUT == 2) {
         reinterpret_cast<int32_t*>(out)[(int64_t)m * ldo + n] = t;
       } else if constexpr (OUT == 1) {

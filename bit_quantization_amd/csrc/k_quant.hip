@@ -984,7 +984,9 @@ __device__ __forceinline__ void row_load(const void* __restrict__ x, int64_t ldx
 // (Eq. 8), packed as the public INT4 layout (code j = 4 h + b of a word at
 // bits 8 b + 4 h), K / 2 bytes, or, with MX, as MX6 operands of the FP6 x
 // FP4 matmul (mx6_main_off, mx6_tail_off; codes is then the buffer base).
-template <int LOG2K, int BITS = 8, bool MX = false>
+// RSUM false: no row sum (rowsum and redi unused; the one-launch decode
+// layer takes each thread's code sums into its matmul instead).
+template <int LOG2K, int BITS = 8, bool MX = false, bool RSUM = true>
 __device__ __forceinline__ void row_quant(const v8bf (&bx)[2], int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ rowsum, int64_t m,
                                                int tid, float* __restrict__ L, float* __restrict__ redf,
@@ -1117,15 +1119,15 @@ __device__ __forceinline__ void row_quant(const v8bf (&bx)[2], int8_t* __restric
           make_uint2((q4.x & 0x0f0f0f0fu) | ((q4.y & 0x0f0f0f0fu) << 4), (q4.z & 0x0f0f0f0fu) | ((q4.w & 0x0f0f0f0fu) << 4));
     }
   }
-  int qs = __builtin_amdgcn_sdot4((int)q4.x, 0x01010101, 0, false);
-  qs = __builtin_amdgcn_sdot4((int)q4.y, 0x01010101, qs, false);
-  qs = __builtin_amdgcn_sdot4((int)q4.z, 0x01010101, qs, false);
-  qs = __builtin_amdgcn_sdot4((int)q4.w, 0x01010101, qs, false);
-  qs = row_reduce_int<TR>(qs, redi, 0, tid);
-  if (tid == 0) {
-    scales[m] = s_out;
-    if (rowsum) rowsum[m] = qs;
+  if constexpr (RSUM) {
+    int qs = __builtin_amdgcn_sdot4((int)q4.x, 0x01010101, 0, false);
+    qs = __builtin_amdgcn_sdot4((int)q4.y, 0x01010101, qs, false);
+    qs = __builtin_amdgcn_sdot4((int)q4.z, 0x01010101, qs, false);
+    qs = __builtin_amdgcn_sdot4((int)q4.w, 0x01010101, qs, false);
+    qs = row_reduce_int<TR>(qs, redi, 0, tid);
+    if (tid == 0 && rowsum) rowsum[m] = qs;
   }
+  if (tid == 0) scales[m] = s_out;
 }
 
 template <int LOG2K, int BITS, bool MX>
@@ -1148,7 +1150,9 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 // loads, and, while the weights are in flight, rotates and quantises the
 // rows itself, one group of K / 16 threads per row (row_quant, the same
 // arithmetic as k_fwht_quant_row, so the same codes; the groups pass the
-// same barriers), keeping the codes, scales and row sums in its LDS.  Every
+// same barriers), keeping the codes and scales in its LDS (no row sum: each
+// matmul thread subtracts the sum of its own codes instead, which takes a
+// block reduction and its barrier off the rotation's chain).  Every
 // block repeats that work (an n log n transform per row, small beside its
 // share of the weight stream) so that no block waits for another and the
 // layer needs no second launch.  Rows m >= M are zero and their outputs are
@@ -1180,11 +1184,10 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
   __shared__ float redf[MT * NWV];
   __shared__ int redi[MT * NWV];
   __shared__ float s_tok[MT];
-  __shared__ int32_t r_tok[MT];
   const int tid = threadIdx.x, grp = tid / TR, gt = tid % TR;
   v8bf bx[2];
-  gemv_dot_body<BITS, 0, MT, TK, NT, DecodeNB<LOG2K>>(
-      cl, s_tok, r_tok, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
+  gemv_dot_body<BITS, 0, MT, TK, NT, DecodeNB<LOG2K>, false, true>(
+      cl, s_tok, nullptr, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
       [&] {
         row_load<LOG2K>(x, ldx, grp, gt, bx, grp < M);
         if constexpr (LOG2K >= 13) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the row first
@@ -1192,9 +1195,9 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
       },
       [&] {
         __builtin_amdgcn_sched_barrier(0);
-        row_quant<LOG2K, BITS>(bx, cl + grp * CB, s_tok + grp, r_tok + grp, 0, gt, L + grp * K,
-                                    redf + grp * NWV, redi + grp * NWV);
-        __syncthreads();  // codes, scales and row sums in LDS
+        row_quant<LOG2K, BITS, false, false>(bx, cl + grp * CB, s_tok + grp, nullptr, 0, gt, L + grp * K,
+                                             redf + grp * NWV, redi + grp * NWV);
+        __syncthreads();  // codes and scales in LDS
       });
 }
 
