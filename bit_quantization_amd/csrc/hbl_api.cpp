@@ -164,9 +164,10 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, 
   int32_t* rowsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scales) + round256(sizeof(float) * (size_t)M));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hbl::decode_token_applies(x_dtype == HBL_DTYPE_BF16, M, N, K, (flags & HBL_HADAMARD) != 0, norm, bits)) {
-    // a few tokens: rotation, quantisation and matmul in one launch (the
-    // workspace is not used)
-    hipError_t e = hbl::launch_decode_token(x, ldx, M, (int)K, bits, w_packed, alpha, N, y, ldy, s);
+    // a few tokens: rotation (if asked), quantisation and matmul in one
+    // launch (the workspace is not used)
+    hipError_t e = hbl::launch_decode_token(x, ldx, M, (int)K, bits, (flags & HBL_HADAMARD) != 0, w_packed, alpha,
+                                            N, y, ldy, s);
     if (e != hipSuccess) return hip_fail(e, "few-token decode launch");
     return HBL_OK;
   }

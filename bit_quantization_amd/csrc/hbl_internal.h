@@ -120,8 +120,9 @@ hipError_t launch_kv_quant(const void* x, bool x_bf16, int64_t B, int64_t S, int
 // dot-product matmul with the rescale of Eq. 9 in one launch, bf16 output
 // [M][ldo]; the codes never leave the chip.
 bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits);
-hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, const uint32_t* wp,
-                               const float* alpha, int64_t N, void* out, int64_t ldo, hipStream_t s);
+hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, bool hadamard,
+                               const uint32_t* wp, const float* alpha, int64_t N, void* out, int64_t ldo,
+                               hipStream_t s);
 
 // Token counts up to this take the weight-streaming kernel.
 constexpr int kGemvMaxM = 128;

@@ -1171,10 +1171,17 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 template <int LOG2K>
 constexpr int DecodeNB = 16;
 
-template <int LOG2K, int MT, int BITS>
+// HAD false: plain BitLinear (Eq. 9 without the rotation), INT8 codes only:
+// the row's absmax (order-free), f = 127 / (gamma + eps) and the codes by
+// one fma against 1.5 * 2^23 with an integer clip, as the many-row
+// quantiser computes them for unrotated rows, so that the layer equals its
+// two launches bit for bit.  A thread quantises the 16 elements row_load
+// gave it (two runs of 8) and stores their codes in place.
+template <int LOG2K, int MT, int BITS, bool HAD = true>
 __global__ void __launch_bounds__(MT * (1 << LOG2K) / 16)
 k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ wp,
                const float* __restrict__ alpha, void* __restrict__ out, int64_t ldo) {
+  static_assert(HAD || BITS == 8, "plain one-launch layer: INT8 codes");
   constexpr int K = 1 << LOG2K, TR = K / 16, NT = MT * TR, TK = K / 64, NWV = K / 1024;
   constexpr int CB = K * BITS / 8;  // code bytes per row
   static_assert(NT <= 1024, "one block holds the rows");
@@ -1195,8 +1202,44 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
       },
       [&] {
         __builtin_amdgcn_sched_barrier(0);
-        row_quant<LOG2K, BITS, false, false>(bx, cl + grp * CB, s_tok + grp, nullptr, 0, gt, L + grp * K,
-                                             redf + grp * NWV, redi + grp * NWV);
+        if constexpr (HAD) {
+          row_quant<LOG2K, BITS, false, false>(bx, cl + grp * CB, s_tok + grp, nullptr, 0, gt, L + grp * K,
+                                               redf + grp * NWV, redi + grp * NWV);
+        } else {
+          // row_load's runs: elements 1024 w + 64 (l % 16) + 32 ks + 8 (l / 16) + 0..7
+          const int lane = gt & 63, wave = gt >> 6;
+          float v[16];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint4 u = __builtin_bit_cast(uint4, bx[ks]);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[8 * ks + 2 * i] = __uint_as_float(w[i] << 16);
+              v[8 * ks + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+          }
+          float st = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st = fmaxf(st, fabsf(v[i]));
+          st = row_reduce<TR, true>(st, redf + grp * NWV, 0, gt);
+          const float f = 127.0f / (st + kEps);
+          constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+          constexpr int kMagicBits = 0x4b400000;
+          int8_t* c8 = cl + grp * CB + 1024 * wave + 64 * (lane & 15) + 8 * (lane >> 4);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            uint32_t wq[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int b = __float_as_int(__builtin_fmaf(v[8 * ks + j], f, kMagic));
+              const int q = min(max(b, kMagicBits - 128), kMagicBits + 127) - kMagicBits;
+              wq[j >> 2] |= (uint32_t)(q & 0xff) << (8 * (j & 3));
+            }
+            *reinterpret_cast<uint2*>(c8 + 32 * ks) = make_uint2(wq[0], wq[1]);
+          }
+          if (gt == 0) s_tok[grp] = st / 127.0f;
+        }
         __syncthreads();  // codes and scales in LDS
       });
 }
@@ -1440,27 +1483,31 @@ template <int L, int MT>
 constexpr int decode_nb() { return DotGeom<MT, (1 << L) / 64, MT * (1 << L) / 16, DecodeNB<L>>::NB; }
 
 bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool hadamard, bool norm, int bits) {
-  if (!((bits == 8 || bits == 4) && x_bf16 && hadamard && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0))
+  // rotated: INT8 or INT4 codes; plain: INT8 codes
+  if (!((bits == 8 || (bits == 4 && hadamard)) && x_bf16 && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0))
     return false;
   if (M < 1 || M > decode_token_max_m(K)) return false;
   return N % 16 == 0;  // features per block (decode_nb)
 }
 
-hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, const uint32_t* wp,
-                               const float* alpha, int64_t N, void* out, int64_t ldo, hipStream_t s) {
+hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int bits, bool hadamard,
+                               const uint32_t* wp, const float* alpha, int64_t N, void* out, int64_t ldo,
+                               hipStream_t s) {
 #define HBL_DT(L, MT)                                                                                            \
   {                                                                                                              \
     constexpr int NB = decode_nb<L, MT>();                                                                       \
     if (N % NB != 0) return hipErrorInvalidValue;                                                                \
-    if (bits == 8)                                                                                               \
-      hipLaunchKernelGGL((k_decode_token<L, MT, 8>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, \
-                         ldx, (int)M, wp, alpha, out, ldo);                                                      \
+    const dim3 grid((unsigned)(N / NB)), block(MT * (1 << L) / 16);                                              \
+    if (!hadamard)                                                                                               \
+      hipLaunchKernelGGL((k_decode_token<L, MT, 8, false>), grid, block, 0, s, x, ldx, (int)M, wp, alpha, out,   \
+                         ldo);                                                                                   \
+    else if (bits == 8)                                                                                          \
+      hipLaunchKernelGGL((k_decode_token<L, MT, 8>), grid, block, 0, s, x, ldx, (int)M, wp, alpha, out, ldo);   \
     else                                                                                                         \
-      hipLaunchKernelGGL((k_decode_token<L, MT, 4>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, s, x, \
-                         ldx, (int)M, wp, alpha, out, ldo);                                                      \
+      hipLaunchKernelGGL((k_decode_token<L, MT, 4>), grid, block, 0, s, x, ldx, (int)M, wp, alpha, out, ldo);   \
     return hipGetLastError();                                                                                    \
   }
-  if (bits != 8 && bits != 4) return hipErrorInvalidValue;
+  if (bits != 8 && (bits != 4 || !hadamard)) return hipErrorInvalidValue;
   if (M < 1 || M > decode_token_max_m(K)) return hipErrorInvalidValue;
   switch (ilog2(K)) {
     case 10: if (M == 1) HBL_DT(10, 1) else HBL_DT(10, 2)

@@ -15,7 +15,9 @@ Checked here:
   - 100 consecutive calls on changing inputs, each checked;
   - a HIP graph of several calls replayed with new inputs between replays;
   - INT4 at every supported (K, M): against the oracle, and bit for bit
-    against the two-launch path.
+    against the two-launch path;
+  - plain BitLinear (no rotation, INT8) at every supported (K, M): the same
+    two checks, strided rows, an all-zero token and repeated calls.
 """
 from __future__ import annotations
 
@@ -142,3 +144,58 @@ def test_decode_token_layer_int4(hbl, K, M, N):
     y64 = oracle.forward(x_np, o_packed, o_alpha, 4, hadamard=True)
     check_output(bf16_to_f64(y), y64, f"few-token decode INT4 K={K} M={M} N={N}")
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "one-launch and two-launch outputs differ"
+
+
+def _two_launch_plain(hbl, x, packed, alpha):
+    q, s, rs = hbl.hadamard_quant(x, 8, hadamard=False)
+    return hbl.ternary_gemm(q, 8, s, rs, packed, alpha, x.shape[1])
+
+
+@pytest.mark.parametrize("K,M", KM)
+@pytest.mark.parametrize("N", [16, 4096])
+def test_decode_plain_layer(hbl, K, M, N):
+    """Plain BitLinear (Eq. 9 without the rotation), INT8 absmax codes of
+    Eq. 7 on the raw token rows: one launch for one token (two up to K =
+    4096), bit for bit against the two-launch path (the same absmax, factor
+    and rounding) and against the oracle's fp64 layer value."""
+    print(f"[plain decode] K={K} M={M} N={N}", flush=True)
+    x_np = workloads.random_rows(7 * K + N + M, M, K, "t3")
+    w_np = workloads.gaussian_weights(13, K // 1024 + N, N, K)
+    x = to_device(x_np)
+    packed, alpha = hbl.ternarize_weights(to_device(w_np))
+    y = hbl.forward(x, packed, alpha, 8, hadamard=False)
+    y2 = _two_launch_plain(hbl, x, packed, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "one-launch and two-launch outputs differ"
+    o_packed, o_alpha, _ = oracle.ternarize(w_np)
+    y64 = oracle.forward(x_np, o_packed, o_alpha, 8, hadamard=False)
+    check_output(bf16_to_f64(y), y64, f"plain decode K={K} M={M} N={N}")
+
+
+@pytest.mark.parametrize("K,M", [(4096, 1), (4096, 2), (16384, 1)])
+def test_decode_plain_strided_zero_row_and_repeats(hbl, K, M):
+    """Strided token rows and outputs, an all-zero token (exactly zero
+    outputs), and 20 consecutive calls on changing inputs, each equal to the
+    two-launch result."""
+    N = 64
+    xb = torch.zeros((M, K + 256), dtype=torch.bfloat16, device="cuda")
+    if M > 1:
+        xb[:M - 1, :K] = to_device(workloads.random_rows(44 + M, M - 1, K, "t3"))
+    packed, alpha = hbl.ternarize_weights(to_device(workloads.gaussian_weights(14, 1, N, K)))
+    yb = torch.full((M, N + 24), -7.0, dtype=torch.bfloat16, device="cuda")
+    hbl.forward(xb[:, :K], packed, alpha, 8, hadamard=False, out=yb[:, :N])
+    y2 = _two_launch_plain(hbl, xb[:, :K].contiguous(), packed, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(yb[:, :N].view(torch.int16), y2.view(torch.int16))
+    assert torch.all(yb[:, N:] == -7.0), "wrote outside the output view"
+    assert torch.all(yb[M - 1, :N].view(torch.int16) == 0), "an all-zero token must give exactly zero"
+    xs = [to_device(workloads.random_rows(120 + i, M, K, "t3")) for i in range(3)]
+    refs = [_two_launch_plain(hbl, xi, packed, alpha) for xi in xs]
+    x = torch.empty_like(xs[0])
+    outs = torch.empty((20, M, N), dtype=torch.bfloat16, device="cuda")
+    for i in range(20):
+        x.copy_(xs[i % 3])
+        hbl.forward(x, packed, alpha, 8, hadamard=False, out=outs[i])
+    torch.cuda.synchronize()
+    for i in range(20):
+        assert torch.equal(outs[i].view(torch.int16), refs[i % 3].view(torch.int16)), f"call {i}"
