@@ -1158,11 +1158,16 @@ k_fwht_quant_row(const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ c
 // layer needs no second launch.  Rows m >= M are zero and their outputs are
 // not stored.  (A wave's loads complete in issue
 // order: the rows are loaded before the weights, whose arrival the rotation
-// does not need.)  From K = 8192 on every block first waits for its row and
-// only then issues its 64 KB of weights: issued together, the 16.8 MB of
-// weight requests queue in front of the row's and the rotation starts
-// late (one token, us per layer: 8.4 -> 7.4-7.8; at K = 8192, 5.24 ->
-// 4.95; at K = 4096 the wait costs 3.78 -> 3.87 and is not taken).
+// does not need.)  From 8192 row elements per block (two tokens at K =
+// 4096, one from K = 8192) every block first waits for its rows and only
+// then issues its weights: issued together, the weight requests (16.8 MB
+// at K = 16384) queue in front of the rows' and the quantisation starts
+// late.  Us per layer, rotated / plain: one token at K = 16384 8.4 ->
+// 7.4-7.8 / 7.2 -> 6.2, at 8192 5.24 -> 4.95 / 4.4 -> 3.9, two at 4096
+// 4.9 -> 4.6 / 4.1 -> 3.7; below, the wait costs: one token at 4096 3.78
+// -> 3.87 / 2.96 -> 3.07, two at 2048 3.50 -> 3.67, one at 1024 2.84 ->
+// 2.98 (one at 2048 gains, 3.54 -> 3.37 / 2.96 -> 2.70, and is left out
+// of the rule).
 // 16 output features per block (256 blocks at N = 4096).  Measured with one
 // token, us per layer at K = 16384 / 4096 (two tokens at 4096): 8 features
 // per block - / 4.3 (5.7), 16: 8.5 / 3.7 (4.8), 32: 9.9 / 4.2 (5.2), 64:
@@ -1197,7 +1202,7 @@ k_decode_token(const void* __restrict__ x, int64_t ldx, int M, const uint32_t* _
       cl, s_tok, nullptr, wp, alpha, M, K, out, ldo, blockIdx.x, tid, reinterpret_cast<int*>(L),
       [&] {
         row_load<LOG2K>(x, ldx, grp, gt, bx, grp < M);
-        if constexpr (LOG2K >= 13) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the row first
+        if constexpr (MT * K >= 8192) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the rows first
         __builtin_amdgcn_sched_barrier(0);  // the rows' loads are issued before the weights'
       },
       [&] {
