@@ -1482,7 +1482,13 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
 // us per layer: two tokens at K = 4096 5.9 against 6.4; with 16 waves and
 // 80 KB of LDS per block, one block per CU, several rows lose: four tokens
 // at K = 4096 6.7 against 6.8, two at K = 8192 10.8 against about 8.)
-int decode_token_max_m(int64_t K) { return K > 4096 ? 1 : 2; }
+// Tokens the one-launch layer takes: rotated, two up to K = 4096 (the
+// rows' rotation over more waves did not pay); plain INT8, whose
+// quantisation is one reduction, as many as 1024 threads hold (K / 16 each)
+int decode_token_max_m(int64_t K, bool hadamard) {
+  if (hadamard) return K > 4096 ? 1 : 2;
+  return K > 8192 ? 1 : K > 4096 ? 2 : 4;
+}
 
 template <int L, int MT>
 constexpr int decode_nb() { return DotGeom<MT, (1 << L) / 64, MT * (1 << L) / 16, DecodeNB<L>>::NB; }
@@ -1491,7 +1497,7 @@ bool decode_token_applies(bool x_bf16, int64_t M, int64_t N, int64_t K, bool had
   // rotated: INT8 or INT4 codes; plain: INT8 codes
   if (!((bits == 8 || (bits == 4 && hadamard)) && x_bf16 && !norm && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0))
     return false;
-  if (M < 1 || M > decode_token_max_m(K)) return false;
+  if (M < 1 || M > decode_token_max_m(K, hadamard)) return false;
   return N % 16 == 0;  // features per block (decode_nb)
 }
 
@@ -1512,16 +1518,33 @@ hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int
       hipLaunchKernelGGL((k_decode_token<L, MT, 4>), grid, block, 0, s, x, ldx, (int)M, wp, alpha, out, ldo);   \
     return hipGetLastError();                                                                                    \
   }
+#define HBL_DTP(L, MT)                                                                                           \
+  {                                                                                                              \
+    constexpr int NB = decode_nb<L, MT>();                                                                       \
+    if (N % NB != 0) return hipErrorInvalidValue;                                                                \
+    hipLaunchKernelGGL((k_decode_token<L, MT, 8, false>), dim3((unsigned)(N / NB)), dim3(MT * (1 << L) / 16), 0, \
+                       s, x, ldx, (int)M, wp, alpha, out, ldo);                                                  \
+    return hipGetLastError();                                                                                    \
+  }
   if (bits != 8 && (bits != 4 || !hadamard)) return hipErrorInvalidValue;
-  if (M < 1 || M > decode_token_max_m(K)) return hipErrorInvalidValue;
+  if (M < 1 || M > decode_token_max_m(K, hadamard)) return hipErrorInvalidValue;
+  if (!hadamard && M > 2) {  // plain, 3 or 4 tokens, K <= 4096
+    switch (ilog2(K)) {
+      case 10: HBL_DTP(10, 4)
+      case 11: HBL_DTP(11, 4)
+      case 12: HBL_DTP(12, 4)
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (ilog2(K)) {
     case 10: if (M == 1) HBL_DT(10, 1) else HBL_DT(10, 2)
     case 11: if (M == 1) HBL_DT(11, 1) else HBL_DT(11, 2)
     case 12: if (M == 1) HBL_DT(12, 1) else HBL_DT(12, 2)
-    case 13: HBL_DT(13, 1)
+    case 13: if (M == 1) HBL_DT(13, 1) else HBL_DTP(13, 2)
     case 14: HBL_DT(14, 1)
     default: return hipErrorInvalidValue;
   }
+#undef HBL_DTP
 #undef HBL_DT
 }
 

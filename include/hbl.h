@@ -244,12 +244,13 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
  *     0), the int32 partial sums of a split of K (at most 32 MiB); integer
  *     sums make the output the same bits with or without the split.
  * Shapes: the union of the rules of hbl_hadamard_quant and
- * hbl_ternary_gemm.  Two kernels are enqueued, except for one or two bf16
- * tokens (M <= 2 up to K = 4096, M = 1 above), K a power of two in [1024,
- * 16384], with HBL_HADAMARD (bits 8 or 4) or without it (bits 8): then one
- * kernel, in which every block rotates (if asked) and quantises the tokens
- * itself while its weights stream in; the codes stay on chip and ws is
- * validated but not written; y is bit-identical to the two-kernel result.
+ * hbl_ternary_gemm.  Two kernels are enqueued, except for a few bf16
+ * tokens, K a power of two in [1024, 16384]: with HBL_HADAMARD (bits 8 or
+ * 4) M <= 2 up to K = 4096 and M = 1 above; without it (bits 8) M <= 4 up
+ * to K = 4096, M <= 2 at 8192 and M = 1 at 16384.  Then one kernel, in
+ * which every block rotates (if asked) and quantises the tokens itself
+ * while its weights stream in; the codes stay on chip and ws is validated
+ * but not written; y is bit-identical to the two-kernel result.
  * ------------------------------------------------------------------- */
 size_t hbl_forward_workspace_size(int64_t M, int64_t N, int64_t K, int bits);
 int hbl_forward(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,

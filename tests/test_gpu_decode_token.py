@@ -16,8 +16,9 @@ Checked here:
   - a HIP graph of several calls replayed with new inputs between replays;
   - INT4 at every supported (K, M): against the oracle, and bit for bit
     against the two-launch path;
-  - plain BitLinear (no rotation, INT8) at every supported (K, M): the same
-    two checks, strided rows, an all-zero token and repeated calls.
+  - plain BitLinear (no rotation, INT8; up to four tokens at K <= 4096, two
+    at 8192) at every supported (K, M): the same two checks, strided rows,
+    an all-zero token and repeated calls.
 """
 from __future__ import annotations
 
@@ -151,13 +152,19 @@ def _two_launch_plain(hbl, x, packed, alpha):
     return hbl.ternary_gemm(q, 8, s, rs, packed, alpha, x.shape[1])
 
 
-@pytest.mark.parametrize("K,M", KM)
+# plain INT8 takes up to 4 tokens in one launch up to K = 4096, 2 at 8192
+KM_PLAIN = [(K, M) for K, mmax in ((1024, 4), (2048, 4), (4096, 4), (8192, 2), (16384, 1))
+            for M in range(1, mmax + 2)]
+
+
+@pytest.mark.parametrize("K,M", KM_PLAIN)
 @pytest.mark.parametrize("N", [16, 4096])
 def test_decode_plain_layer(hbl, K, M, N):
     """Plain BitLinear (Eq. 9 without the rotation), INT8 absmax codes of
-    Eq. 7 on the raw token rows: one launch for one token (two up to K =
-    4096), bit for bit against the two-launch path (the same absmax, factor
-    and rounding) and against the oracle's fp64 layer value."""
+    Eq. 7 on the raw token rows: one launch for up to four tokens (up to K =
+    4096; two at 8192, one at 16384), bit for bit against the two-launch
+    path (the same absmax, factor and rounding) and against the oracle's
+    fp64 layer value; the next M up takes two launches."""
     print(f"[plain decode] K={K} M={M} N={N}", flush=True)
     x_np = workloads.random_rows(7 * K + N + M, M, K, "t3")
     w_np = workloads.gaussian_weights(13, K // 1024 + N, N, K)
@@ -172,7 +179,7 @@ def test_decode_plain_layer(hbl, K, M, N):
     check_output(bf16_to_f64(y), y64, f"plain decode K={K} M={M} N={N}")
 
 
-@pytest.mark.parametrize("K,M", [(4096, 1), (4096, 2), (16384, 1)])
+@pytest.mark.parametrize("K,M", [(4096, 1), (4096, 2), (4096, 4), (8192, 2), (16384, 1)])
 def test_decode_plain_strided_zero_row_and_repeats(hbl, K, M):
     """Strided token rows and outputs, an all-zero token (exactly zero
     outputs), and 20 consecutive calls on changing inputs, each equal to the
