@@ -1482,11 +1482,14 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
 // us per layer: two tokens at K = 4096 5.9 against 6.4; with 16 waves and
 // 80 KB of LDS per block, one block per CU, several rows lose: four tokens
 // at K = 4096 6.7 against 6.8, two at K = 8192 10.8 against about 8.)
-// Tokens the one-launch layer takes: rotated, two up to K = 4096 (the
-// rows' rotation over more waves did not pay); plain INT8, whose
-// quantisation is one reduction, as many as 1024 threads hold (K / 16 each)
+// Tokens the one-launch layer takes (at most 1024 threads, K / 16 per
+// token), where it measured faster than the two launches: plain INT8,
+// whose quantisation is one reduction, every such count; rotated, not
+// three or four tokens at K = 4096 (us, two launches -> one: 6.56 -> 6.7,
+// 6.58 -> 6.9), but four at K = 1024 (5.16 -> 3.50) and 2048 (5.68 ->
+// 4.69) and two at 8192 (7.8 -> 6.9)
 int decode_token_max_m(int64_t K, bool hadamard) {
-  if (hadamard) return K > 4096 ? 1 : 2;
+  if (hadamard) return K > 8192 ? 1 : K > 2048 ? 2 : 4;
   return K > 8192 ? 1 : K > 4096 ? 2 : 4;
 }
 
@@ -1528,10 +1531,10 @@ hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int
   }
   if (bits != 8 && (bits != 4 || !hadamard)) return hipErrorInvalidValue;
   if (M < 1 || M > decode_token_max_m(K, hadamard)) return hipErrorInvalidValue;
-  if (!hadamard && M > 2) {  // plain, 3 or 4 tokens, K <= 4096
+  if (M > 2) {  // 3 or 4 tokens: K <= 2048, or plain at 4096
     switch (ilog2(K)) {
-      case 10: HBL_DTP(10, 4)
-      case 11: HBL_DTP(11, 4)
+      case 10: HBL_DT(10, 4)
+      case 11: HBL_DT(11, 4)
       case 12: HBL_DTP(12, 4)
       default: return hipErrorInvalidValue;
     }
@@ -1540,7 +1543,7 @@ hipError_t launch_decode_token(const void* x, int64_t ldx, int64_t M, int K, int
     case 10: if (M == 1) HBL_DT(10, 1) else HBL_DT(10, 2)
     case 11: if (M == 1) HBL_DT(11, 1) else HBL_DT(11, 2)
     case 12: if (M == 1) HBL_DT(12, 1) else HBL_DT(12, 2)
-    case 13: if (M == 1) HBL_DT(13, 1) else HBL_DTP(13, 2)
+    case 13: if (M == 1) HBL_DT(13, 1) else HBL_DT(13, 2)
     case 14: HBL_DT(14, 1)
     default: return hipErrorInvalidValue;
   }

@@ -246,8 +246,9 @@ int hbl_ternary_gemm(const void* codes, int bits, const float* scales,
  * Shapes: the union of the rules of hbl_hadamard_quant and
  * hbl_ternary_gemm.  Two kernels are enqueued, except for a few bf16
  * tokens, K a power of two in [1024, 16384]: with HBL_HADAMARD (bits 8 or
- * 4) M <= 2 up to K = 4096 and M = 1 above; without it (bits 8) M <= 4 up
- * to K = 4096, M <= 2 at 8192 and M = 1 at 16384.  Then one kernel, in
+ * 4) M <= 4 up to K = 2048, M <= 2 at 4096 and 8192 and M = 1 at 16384;
+ * without it (bits 8) M <= 4 up to K = 4096, M <= 2 at 8192 and M = 1 at
+ * 16384.  Then one kernel, in
  * which every block rotates (if asked) and quantises the tokens itself
  * while its weights stream in; the codes stay on chip and ws is validated
  * but not written; y is bit-identical to the two-kernel result.

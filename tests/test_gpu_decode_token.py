@@ -1,5 +1,5 @@
 """The few-token decode layer in one launch: hbl_forward with M bf16 tokens
-(M <= 2 up to K = 4096, else 1), INT8 or INT4 codes and the
+(M <= 4 up to K = 2048, 2 up to 8192, else 1), INT8 or INT4 codes and the
 rotation (BitNet v2 architecture write-up, §3.4 "H-BitLinear", Eq. 9 with
 the INT8 quantiser of Eq. 7 or the INT4 one of Eq. 8) runs in one kernel
 whose every block rotates and quantises the token rows itself.
@@ -9,7 +9,7 @@ Checked here:
     (hbl_hadamard_quant, then hbl_ternary_gemm): the same rotation and
     rounding give the same codes, and the integer sums are exact;
   - the layer output against the oracle's fp64 layer value (per-row L2);
-  - every supported (K, M), K = 1024 ... 16384, M = 1 and 2, and N = 16 (one
+  - every supported (K, M), K = 1024 ... 16384, M up to those limits, and N = 16 (one
     matmul block of 16 features), 48 (three) and 4096; strided token rows and outputs; an all-zero token among others
     (its outputs exactly zero); the next M up, which takes two launches;
   - 100 consecutive calls on changing inputs, each checked;
@@ -38,7 +38,8 @@ def _two_launch(hbl, x, packed, alpha):
     return hbl.ternary_gemm(q, 8, s, rs, packed, alpha, x.shape[1])
 
 
-KM = [(K, M) for K, mmax in ((1024, 2), (2048, 2), (4096, 2), (8192, 1), (16384, 1)) for M in range(1, mmax + 2)]
+# rotated: up to 4 tokens in one launch up to K = 2048, 2 at 4096 and 8192
+KM = [(K, M) for K, mmax in ((1024, 4), (2048, 4), (4096, 2), (8192, 2), (16384, 1)) for M in range(1, mmax + 2)]
 
 
 @pytest.mark.parametrize("K,M", KM)
