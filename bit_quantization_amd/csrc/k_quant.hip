@@ -1477,11 +1477,9 @@ hipError_t launch_hadamard_quant(const void* x, bool x_bf16, int64_t M, int K, i
               : quant_by_k<false>(x, x_bf16, M, K, ldx, hadamard, bits, codes, scales, rowsum, nullptr, cu, s);
 }
 
-// tokens taken in one launch: two up to K = 4096, else one.  (The rows must
-// fit one block of at most 1024 threads.  Measured against the two launches,
-// us per layer: two tokens at K = 4096 5.9 against 6.4; with 16 waves and
-// 80 KB of LDS per block, one block per CU, several rows lose: four tokens
-// at K = 4096 6.7 against 6.8, two at K = 8192 10.8 against about 8.)
+// (Before the rows-first wait and the code-first two-launch GEMV, two
+// rotated tokens at K = 8192 measured 10.8 us in one launch against about
+// 8 in two; with both, 6.9 against 7.8.)
 // Tokens the one-launch layer takes (at most 1024 threads, K / 16 per
 // token), where it measured faster than the two launches: plain INT8,
 // whose quantisation is one reduction, every such count; rotated, not
